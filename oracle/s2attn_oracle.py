@@ -1,0 +1,227 @@
+"""Plain float64 CPU oracle for Shifted Sparse Attention (S2-Attn), forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+``__graft_entry__.smoke`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+this module.  The GPU library never imports, links or calls it, and it shares no
+code with the GPU library: it imports NumPy and nothing else.
+
+What it computes (page "LongLoRA: Efficient Fine-tuning of Long-Context Large
+Language Models", paper-graph-ui summary, section 3.4):
+
+* "The core computational problem": attention is o = softmax(q k^T) v on each
+  head, under the causal mask of a causal language model.  The page drops the
+  softmax scale; this oracle uses 1/sqrt(d) (the scale the 7B workload states).
+* "The solution: group tokens and compute attention locally": the N tokens are
+  cut into N/G groups of G consecutive tokens and attention runs inside each
+  group only.
+* "The shifting mechanism", Steps 1-3 and Figure 3, and "Algorithmic
+  implementation" (Algorithm 1): the second chunk of heads has its tokens rolled
+  cyclically by G/2 along the sequence before grouping (a torch.roll by -G/2:
+  rolled position j holds original token (j + G/2) mod N), attention runs per
+  group in that rolled order, and the output is rolled back by +G/2.  Here the
+  "second chunk" is the last ``shift_heads`` heads (half of them by default).
+  Causality is applied in the rolled frame, exactly as a causal attention call
+  on the rolled groups would (section "Information leakage considerations"
+  keeps that wrap-around in the main method).
+* Grouped-query attention (several query heads sharing one key/value head) is
+  not on the pages; query head h reads key/value head h // (H // Hkv) and the
+  key/value gradients are summed over the query heads that share them.
+
+The backward pass is the textbook gradient of that function (the pages only say
+gradients flow through the attention during fine-tuning, section 3.2 Phase 1
+step 5):  P = exp(S - lse), dV = P^T dO, dP = dO V^T, Dvec = rowsum(dO * O),
+dS = P * (dP - Dvec), dQ = scale dS K, dK = scale dS^T Q.
+
+Evaluation order: one (batch, head, group) slice at a time; inside a group the
+query rows are taken in chunks (rows are independent in softmax), each chunk
+against the keys up to its last row (later keys are masked for every row of the
+chunk and would add exact zeros).  Nothing else is blocked or reordered.
+
+Pins (all in ``tests/test_oracle.py``): brute-force masked attention written in
+original token coordinates, a roll/regroup/causal-SDPA formulation, full causal
+attention at G = N without shift, exact invariance under reversing the roll
+direction, head-swap equivariance, closed forms (first row of each group),
+finite differences, GQA against repeated-KV MHA, and the worked index example
+of "The shifting mechanism".
+"""
+
+import numpy as np
+
+__all__ = [
+    "check_problem", "head_shift", "kv_head", "rolled_order",
+    "group_forward", "group_backward",
+    "forward", "backward",
+    "head_group_forward", "head_group_backward",
+]
+
+
+def check_problem(B, N, H, Hkv, d, G, shift_heads):
+    """Reject problems the method does not define.
+
+    Grouping views the sequence as N/G groups of G tokens (Algorithm 1's reshape
+    to [B*N/G, G, ...]) and the shift is G/2 tokens, so N must be a multiple of
+    G and G must be even.
+    """
+    for name, val in (("B", B), ("N", N), ("H", H), ("Hkv", Hkv), ("d", d), ("G", G)):
+        if val <= 0:
+            raise ValueError(f"{name} must be positive, got {val}")
+    if N % G:
+        raise ValueError(f"N={N} is not a multiple of the group size G={G}")
+    if G % 2:
+        raise ValueError(f"G={G} must be even (the shift is G/2)")
+    if not 0 <= shift_heads <= H:
+        raise ValueError(f"shift_heads={shift_heads} must lie in [0, H={H}]")
+    if H % Hkv:
+        raise ValueError(f"H={H} is not a multiple of Hkv={Hkv}")
+
+
+def head_shift(h, H, shift_heads, G):
+    """Roll amount of head h: G/2 for the last ``shift_heads`` heads, else 0.
+
+    Step 1-2 of "The shifting mechanism": the heads are split in two chunks and
+    only the second chunk is shifted by half a group.
+    """
+    return G // 2 if h >= H - shift_heads else 0
+
+
+def kv_head(h, H, Hkv):
+    """Key/value head read by query head h (consecutive query heads share one)."""
+    return h // (H // Hkv)
+
+
+def rolled_order(N, sigma):
+    """Original token index held at each rolled position.
+
+    Rolling a sequence by -sigma puts original token (j + sigma) mod N at
+    position j (the first key line of Algorithm 1 with sigma = G/2).
+    """
+    return (np.arange(N) + sigma) % N
+
+
+def group_forward(Qg, Kg, Vg, scale, chunk=1024):
+    """Causal softmax attention of one group, rows already in rolled order.
+
+    Returns (O [G, d], lse [G]) with lse the natural-log normaliser of each row.
+    """
+    G = Qg.shape[0]
+    O = np.empty((G, Vg.shape[1]), dtype=np.float64)
+    lse = np.empty(G, dtype=np.float64)
+    for r0 in range(0, G, chunk):
+        r1 = min(G, r0 + chunk)
+        S = scale * (Qg[r0:r1] @ Kg[:r1].T)
+        allowed = np.arange(r1)[None, :] <= np.arange(r0, r1)[:, None]
+        S = np.where(allowed, S, -np.inf)
+        m = S.max(axis=1, keepdims=True)
+        P = np.exp(S - m)
+        l = P.sum(axis=1, keepdims=True)
+        O[r0:r1] = (P / l) @ Vg[:r1]
+        lse[r0:r1] = (m + np.log(l))[:, 0]
+    return O, lse
+
+
+def group_backward(Qg, Kg, Vg, Og, lseg, dOg, scale, chunk=1024):
+    """Gradients of one group's causal attention given its output and lse.
+
+    Returns (dQ [G, d], dK [G, d], dV [G, d]) for the group's rows in rolled order.
+    """
+    G = Qg.shape[0]
+    Dvec = np.sum(dOg * Og, axis=1)
+    dQ = np.empty_like(Qg, dtype=np.float64)
+    dK = np.zeros_like(Kg, dtype=np.float64)
+    dV = np.zeros_like(Vg, dtype=np.float64)
+    for r0 in range(0, G, chunk):
+        r1 = min(G, r0 + chunk)
+        S = scale * (Qg[r0:r1] @ Kg[:r1].T)
+        allowed = np.arange(r1)[None, :] <= np.arange(r0, r1)[:, None]
+        P = np.where(allowed, np.exp(S - lseg[r0:r1, None]), 0.0)
+        dV[:r1] += P.T @ dOg[r0:r1]
+        dP = dOg[r0:r1] @ Vg[:r1].T
+        dS = P * (dP - Dvec[r0:r1, None])
+        dQ[r0:r1] = scale * (dS @ Kg[:r1])
+        dK[:r1] += scale * (dS.T @ Qg[r0:r1])
+    return dQ, dK, dV
+
+
+def _dims(q, k, v, G, shift_heads):
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, N, Hkv, d) or v.shape != (B, N, Hkv, d):
+        raise ValueError(f"k {k.shape} / v {v.shape} do not match q {q.shape}")
+    check_problem(B, N, H, Hkv, d, G, shift_heads)
+    return B, N, H, Hkv, d
+
+
+def head_group_forward(q, k, v, G, shift_heads, b, h, g):
+    """Forward of one (batch b, query head h, group g of h's rolled frame).
+
+    Returns (rows, O, lse): ``rows`` are the original token indices of the group
+    in rolled order; O[i] and lse[i] belong to original token rows[i].
+    """
+    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads)
+    rows = rolled_order(N, head_shift(h, H, shift_heads, G))[g * G:(g + 1) * G]
+    c = kv_head(h, H, Hkv)
+    Qg = np.asarray(q[b, rows, h], dtype=np.float64)
+    Kg = np.asarray(k[b, rows, c], dtype=np.float64)
+    Vg = np.asarray(v[b, rows, c], dtype=np.float64)
+    O, lse = group_forward(Qg, Kg, Vg, 1.0 / np.sqrt(d))
+    return rows, O, lse
+
+
+def head_group_backward(q, k, v, do, G, shift_heads, b, h, g):
+    """Backward of one (b, h, g) slice.
+
+    Returns (rows, dQ, dK_part, dV_part): dQ is complete for those rows (a query
+    only sees its own group); dK_part / dV_part are head h's contribution to the
+    gradients of key/value head kv_head(h) at the same original rows.
+    """
+    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads)
+    rows = rolled_order(N, head_shift(h, H, shift_heads, G))[g * G:(g + 1) * G]
+    c = kv_head(h, H, Hkv)
+    scale = 1.0 / np.sqrt(d)
+    Qg = np.asarray(q[b, rows, h], dtype=np.float64)
+    Kg = np.asarray(k[b, rows, c], dtype=np.float64)
+    Vg = np.asarray(v[b, rows, c], dtype=np.float64)
+    dOg = np.asarray(do[b, rows, h], dtype=np.float64)
+    O, lse = group_forward(Qg, Kg, Vg, scale)
+    dQ, dK, dV = group_backward(Qg, Kg, Vg, O, lse, dOg, scale)
+    return rows, dQ, dK, dV
+
+
+def forward(q, k, v, G, shift_heads):
+    """S2-Attn forward.
+
+    q [B, N, H, d], k and v [B, N, Hkv, d] (any float dtype; computed in float64).
+    Returns o [B, N, H, d] and lse [B, H, N] (natural log), both in original
+    token order: writing each group's rows back through ``rows`` is the roll-back
+    (Step 2, last sentence; Algorithm 1's second key line).
+    """
+    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads)
+    o = np.empty((B, N, H, d), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for g in range(N // G):
+                rows, Og, lseg = head_group_forward(q, k, v, G, shift_heads, b, h, g)
+                o[b, rows, h] = Og
+                lse[b, h, rows] = lseg
+    return o, lse
+
+
+def backward(q, k, v, do, G, shift_heads):
+    """S2-Attn backward: (dq, dk, dv) of L = sum(o * do), float64.
+
+    dk and dv sum the contributions of every query head that reads them.
+    """
+    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads)
+    dq = np.empty((B, N, H, d), dtype=np.float64)
+    dk = np.zeros((B, N, Hkv, d), dtype=np.float64)
+    dv = np.zeros((B, N, Hkv, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            c = kv_head(h, H, Hkv)
+            for g in range(N // G):
+                rows, dQg, dKg, dVg = head_group_backward(q, k, v, do, G, shift_heads, b, h, g)
+                dq[b, rows, h] = dQg
+                dk[b, rows, c] += dKg
+                dv[b, rows, c] += dVg
+    return dq, dk, dv

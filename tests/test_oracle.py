@@ -1,0 +1,76 @@
+"""The float64 oracle against independent pins (CPU only)."""
+
+import os
+
+import numpy as np
+import pytest
+
+import pins
+from oracle import s2attn_oracle as orc
+from shifted_sparse_attention_s2attn_amd import flops
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(orc)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(N=30, G=8),          # N not a multiple of G
+    dict(N=21, G=7),          # odd G
+    dict(S=5),                # more shifted heads than heads
+    dict(S=-1),
+    dict(Hkv=3),              # H not a multiple of Hkv
+    dict(G=0),
+])
+def test_oracle_rejects_undefined_problems(bad):
+    p = dict(B=1, N=32, H=4, Hkv=2, d=4, G=8, S=2)
+    p.update(bad)
+    q = np.zeros((p["B"], p["N"], p["H"], p["d"]))
+    k = np.zeros((p["B"], p["N"], p["Hkv"], p["d"]))
+    with pytest.raises(ValueError):
+        orc.forward(q, k, k, p["G"], p["S"])
+
+
+def test_table11_attention_flops():
+    """The pages' attention FLOPs (dense forward convention) are 4 N G d H L exactly."""
+    path = os.path.join(pins.GOLDEN, "table11_attention_flops.txt")
+    rows = [line.split() for line in open(path) if line.strip() and not line.startswith("#")]
+    assert len(rows) == 6
+    for N, G, tflops in rows:
+        got = flops.dense_fwd_attention_flops(int(N), int(G), d=128, H=32, L=32) / 1e12
+        assert round(got, 1) == float(tflops), (N, G, got, tflops)
+    # "training on 8192 tokens requires about 16x the self-attention computation of 2048"
+    assert flops.dense_fwd_attention_flops(8192, 8192, 128, 32, 32) == \
+        16 * flops.dense_fwd_attention_flops(2048, 2048, 128, 32, 32)
+
+
+@pytest.mark.parametrize("N,G,H,S", [(16, 8, 2, 1), (24, 8, 3, 2), (32, 32, 2, 0), (12, 4, 4, 4)])
+def test_pair_count_matches_bruteforce_mask(N, G, H, S):
+    """allowed_pairs counts exactly the entries the method lets attend."""
+    total = 0
+    for h in range(H):
+        total += int(pins.allowed_mask_original(N, G, h >= H - S).sum())
+    assert flops.allowed_pairs(1, H, N, G) == total
+
+
+def test_sampled_slices_agree_with_full_oracle():
+    """head_group_* (used for sampled parity at full size) agree with forward/backward."""
+    B, N, H, Hkv, d, G, S = 2, 32, 4, 2, 4, 8, 2
+    q, k, v, do = pins.rand_problem(B, N, H, Hkv, d, seed=5)
+    o, lse = orc.forward(q, k, v, G, S)
+    dq, dk, dv = orc.backward(q, k, v, do, G, S)
+    dk_acc = np.zeros_like(dk)
+    dv_acc = np.zeros_like(dv)
+    for b in range(B):
+        for h in range(H):
+            for g in range(N // G):
+                rows, Og, lseg = orc.head_group_forward(q, k, v, G, S, b, h, g)
+                assert np.array_equal(o[b, rows, h], Og)
+                assert np.array_equal(lse[b, h, rows], lseg)
+                rows, dQg, dKg, dVg = orc.head_group_backward(q, k, v, do, G, S, b, h, g)
+                assert np.array_equal(dq[b, rows, h], dQg)
+                dk_acc[b, rows, orc.kv_head(h, H, Hkv)] += dKg
+                dv_acc[b, rows, orc.kv_head(h, H, Hkv)] += dVg
+    np.testing.assert_allclose(dk_acc, dk, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv_acc, dv, rtol=0, atol=1e-13)

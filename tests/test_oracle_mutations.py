@@ -1,0 +1,81 @@
+"""Planted mistakes in the oracle must be caught by the pins (CPU only).
+
+Each mutation edits one expression of a copy of the oracle's source, loads the
+copy as a fresh module and runs every pin on it; at least one pin must fail.
+One edit that is *not* a mistake (reversing the roll direction, which the method
+is invariant to) must pass every pin.
+"""
+
+import importlib.util
+import os
+import types
+
+import pytest
+
+import pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "s2attn_oracle.py")
+
+# (name, original text, replacement, occurrence index to replace)
+MUTATIONS = [
+    ("shift-first-heads", "return G // 2 if h >= H - shift_heads else 0",
+     "return G // 2 if h < shift_heads else 0", 0),
+    ("shift-by-quarter", "return G // 2 if h >= H - shift_heads else 0",
+     "return G // 4 if h >= H - shift_heads else 0", 0),
+    ("strict-causal-fwd", "allowed = np.arange(r1)[None, :] <= np.arange(r0, r1)[:, None]",
+     "allowed = np.arange(r1)[None, :] < np.arange(r0, r1)[:, None]", 0),
+    ("anti-causal-bwd", "allowed = np.arange(r1)[None, :] <= np.arange(r0, r1)[:, None]",
+     "allowed = np.arange(r1)[None, :] >= np.arange(r0, r1)[:, None]", 1),
+    ("no-scale-fwd", "O, lse = group_forward(Qg, Kg, Vg, 1.0 / np.sqrt(d))",
+     "O, lse = group_forward(Qg, Kg, Vg, 1.0)", 0),
+    ("kv-head-modulo", "return h // (H // Hkv)", "return h % Hkv", 0),
+    ("drop-dvec", "dS = P * (dP - Dvec[r0:r1, None])", "dS = P * dP", 0),
+    ("dvec-wrong-operand", "Dvec = np.sum(dOg * Og, axis=1)", "Dvec = np.sum(dOg * Qg, axis=1)", 0),
+    ("dk-no-scale", "dK[:r1] += scale * (dS.T @ Qg[r0:r1])", "dK[:r1] += dS.T @ Qg[r0:r1]", 0),
+    ("dq-wrong-operand", "dQ[r0:r1] = scale * (dS @ Kg[:r1])", "dQ[r0:r1] = scale * (dS @ Vg[:r1])", 0),
+    ("dv-scaled", "dV[:r1] += P.T @ dOg[r0:r1]", "dV[:r1] += scale * (P.T @ dOg[r0:r1])", 0),
+    ("no-rollback-o", "o[b, rows, h] = Og", "o[b, g * G:(g + 1) * G, h] = Og", 0),
+    ("lse-drops-max", "lse[r0:r1] = (m + np.log(l))[:, 0]", "lse[r0:r1] = np.log(l)[:, 0]", 0),
+    ("bwd-unmasked-P", "P = np.where(allowed, np.exp(S - lseg[r0:r1, None]), 0.0)",
+     "P = np.exp(S - lseg[r0:r1, None])", 0),
+    ("gqa-overwrite-dk", "dk[b, rows, c] += dKg", "dk[b, rows, c] = dKg", 0),
+    ("transposed-scores", "S = scale * (Qg[r0:r1] @ Kg[:r1].T)\n        allowed",
+     "S = scale * (Kg[r0:r1] @ Qg[:r1].T)\n        allowed", 0),
+    ("lse-of-rolled-row", "lse[b, h, rows] = lseg", "lse[b, h, g * G:(g + 1) * G] = lseg", 0),
+]
+
+NEUTRAL = ("reverse-roll-direction", "return (np.arange(N) + sigma) % N", "return (np.arange(N) - sigma) % N", 0)
+
+
+def _mutant(name, old, new, occ):
+    src = open(SRC).read()
+    parts = src.split(old)
+    assert len(parts) > occ + 1, f"mutation {name}: pattern not found"
+    mutated = old.join(parts[:occ + 1]) + new + old.join(parts[occ + 1:])
+    assert mutated != src
+    mod = types.ModuleType(f"oracle_mutant_{name.replace('-', '_')}")
+    exec(compile(mutated, f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(mutation):
+    mod = _mutant(*mutation)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mod)
+        except (AssertionError, ValueError, IndexError) as e:
+            failed.append((pin.__name__, str(e)[:80]))
+    assert failed, f"no pin caught mutation {mutation[0]}"
+
+
+def test_direction_reversal_is_not_a_mistake():
+    """Every output is invariant; only the index map itself shows the direction."""
+    mod = _mutant(*NEUTRAL)
+    for pin in pins.ALL_PINS:
+        if pin is pins.pin_worked_example_index_map:
+            with pytest.raises(AssertionError):
+                pin(mod)
+        else:
+            pin(mod)
