@@ -1,0 +1,103 @@
+/*
+ * libs2attn — Shifted Sparse Attention (S2-Attn) forward and backward on AMD
+ * MI355X (gfx950).  C ABI: plain device pointers, sizes and a HIP stream.
+ *
+ * The operation.  Page "LongLoRA: Efficient Fine-tuning of Long-Context Large
+ * Language Models" (paper-graph-ui summary), section 3.4:
+ *   - "The core computational problem": per head, o = softmax(q k^T) v under a
+ *     causal mask.  The scale is 1/sqrt(d) (the page omits it).
+ *   - "The solution: group tokens and compute attention locally": the N tokens
+ *     form N/G groups of G consecutive tokens; attention stays inside a group.
+ *   - "The shifting mechanism" (Steps 1-3, Figure 3) and "Algorithmic
+ *     implementation" (Algorithm 1): the last `shift_heads` heads see their
+ *     tokens rolled by -G/2 along the sequence before grouping (rolled position
+ *     j holds token (j + G/2) mod N); their output is rolled back by +G/2.
+ *     Causality holds in the rolled order, so in a shifted head the last group
+ *     holds tokens N-G/2..N-1 followed by tokens 0..G/2-1.
+ *   - Grouped-query attention (not on the pages): query head h reads key/value
+ *     head h / (H / Hkv); dk and dv sum over the query heads sharing them.
+ * The roll is never materialised: it is folded into the row addresses of every
+ * tile load and store, so all tensors stay in original token order.
+ *
+ * Tensors (all device memory, contiguous, token-major, 16-byte aligned,
+ * allocated and freed by the caller; element type given by `dtype`):
+ *   q, o, dO, dq : [B, N, H,   d]
+ *   k, v, dk, dv : [B, N, Hkv, d]
+ *   lse          : [B, H, N] float32, natural-log softmax normaliser of every
+ *                  query row, in original token order (written by the
+ *                  forward, read by the backward).
+ * Outputs are fully overwritten (never accumulated into) and must not alias an
+ * input.  Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream); the library never allocates, frees or synchronises.  Errors raised
+ * while kernels run surface at the caller's next synchronisation, as for any
+ * HIP call.  The library holds no state and is reentrant.
+ *
+ * Supported: d in {64, 128}; dtype bf16 (fp32 accumulation, P and dS rounded
+ * to bf16 for the matrix cores) or fp32 (fp32 matrix cores throughout);
+ * G a multiple of 128; N a multiple of G; when a key/value head is shared by
+ * shifted and unshifted query heads (H - shift_heads not a multiple of
+ * H / Hkv), G must also be a multiple of 256.
+ */
+#ifndef S2ATTN_H
+#define S2ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    S2ATTN_BF16 = 0,   /* bfloat16 storage, fp32 accumulation */
+    S2ATTN_F32 = 1     /* float32 storage and arithmetic */
+} s2attn_dtype;
+
+typedef enum {
+    S2ATTN_OK = 0,
+    S2ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
+    S2ATTN_ERR_SHAPE = 2,        /* a size <= 0, N % G != 0, G odd, shift_heads outside [0, H], H % Hkv != 0 */
+    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype, G % 128 != 0, or the mixed-shift rule above */
+    S2ATTN_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError) */
+    S2ATTN_ERR_WORKSPACE = 5     /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
+} s2attn_status;
+
+/*
+ * Forward.  Writes o[B,N,H,d] and lse[B,H,N].
+ * Arguments are validated on the host before any HIP call; on error nothing is
+ * launched and a status code is returned.
+ */
+int s2attn_fwd(const void* q, const void* k, const void* v,
+               void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, int G, int shift_heads,
+               int dtype, void* stream);
+
+/*
+ * Bytes of device workspace s2attn_bwd needs: the fp32 row sums
+ * Dvec = rowsum(dO * o) [B,H,N] and an fp32 accumulator for dq [B,N,H,d].
+ * Returns 0 when the arguments would be rejected by s2attn_bwd.
+ */
+size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G,
+                                  int shift_heads, int dtype);
+
+/*
+ * Backward of L = sum(o * dO): writes dq, dk, dv (same dtype as q).
+ * Needs the forward's own o and lse.  `workspace` is caller-owned device
+ * memory of at least s2attn_bwd_workspace_bytes() bytes, 256-byte aligned; its
+ * contents on entry do not matter and are clobbered.  Concurrent calls must
+ * use distinct workspaces.
+ */
+int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dO,
+               void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes,
+               int B, int H, int Hkv, int N, int d, int G, int shift_heads,
+               int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* s2attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S2ATTN_H */

@@ -1,0 +1,8 @@
+"""Shifted Sparse Attention (S2-Attn) on AMD MI355X: HIP kernels behind a C ABI.
+
+The compute lives in libs2attn.so (built from csrc/ by ``build.py``); this
+package only marshals torch tensors into the C ABI declared in include/s2attn.h.
+"""
+
+from .binding import (S2Attn, S2AttnError, s2attn, s2attn_bwd, s2attn_bwd_workspace_bytes,  # noqa: F401
+                      s2attn_fwd, s2attn_status_str)

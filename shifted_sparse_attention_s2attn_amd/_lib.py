@@ -1,0 +1,48 @@
+"""ctypes view of libs2attn.so (the C ABI declared in include/s2attn.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation behind this package.
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs2attn.so")
+
+# status codes of include/s2attn.h
+S2ATTN_OK = 0
+S2ATTN_ERR_NULL = 1
+S2ATTN_ERR_SHAPE = 2
+S2ATTN_ERR_UNSUPPORTED = 3
+S2ATTN_ERR_HIP = 4
+S2ATTN_ERR_WORKSPACE = 5
+S2ATTN_BF16 = 0
+S2ATTN_F32 = 1
+
+EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes", "s2attn_status_str")
+
+_lib = None
+
+
+def load():
+    """Load the shared library once; raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m shifted_sparse_attention_s2attn_amd.build` "
+            "(there is no non-HIP implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.s2attn_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, i, i, i, vp]
+    lib.s2attn_fwd.restype = i
+    lib.s2attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.s2attn_bwd_workspace_bytes.restype = sz
+    lib.s2attn_bwd.argtypes = [vp, vp, vp, vp, fp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, vp]
+    lib.s2attn_bwd.restype = i
+    lib.s2attn_status_str.argtypes = [i]
+    lib.s2attn_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib

@@ -1,0 +1,129 @@
+"""PyTorch-facing wrappers over the C ABI of libs2attn (argument marshalling only).
+
+Tensors are token-major: q, o, dO [B, N, H, d]; k, v [B, N, Hkv, d]; lse [B, H, N]
+float32.  Every step of the computation runs in the HIP kernels of libs2attn;
+torch only provides device memory and the current stream.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+__all__ = ["S2AttnError", "s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes",
+           "s2attn_status_str", "S2Attn", "s2attn"]
+
+
+class S2AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {s2attn_status_str(status)} (status {status})")
+
+
+def s2attn_status_str(status):
+    return _lib.load().s2attn_status_str(int(status)).decode()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return _lib.S2ATTN_BF16
+    if t.dtype == torch.float32:
+        return _lib.S2ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _fptr(t):
+    return ctypes.cast(ctypes.c_void_p(t.data_ptr()), ctypes.POINTER(ctypes.c_float))
+
+
+def _check_tensors(q, k, v, extra=()):
+    for name, t in (("q", q), ("k", k), ("v", v)) + tuple(extra):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError(f"bad shapes q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream(q_device()) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def q_device():
+    return torch.cuda.current_device()
+
+
+def s2attn_fwd(q, k, v, G, shift_heads=None, out=None, lse=None, stream=None):
+    """S2-Attn forward.  Returns (o [B,N,H,d], lse [B,H,N] float32)."""
+    _check_tensors(q, k, v)
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    if shift_heads is None:
+        shift_heads = H // 2
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        st = _lib.load().s2attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse_t),
+                                    B, H, Hkv, N, d, G, shift_heads, _dtype_code(q), _stream(stream))
+    if st != _lib.S2ATTN_OK:
+        raise S2AttnError(st, "s2attn_fwd")
+    return o, lse_t
+
+
+def s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype):
+    code = _lib.S2ATTN_BF16 if dtype == torch.bfloat16 else _lib.S2ATTN_F32
+    return int(_lib.load().s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, code))
+
+
+def s2attn_bwd(q, k, v, o, lse, do, G, shift_heads=None, workspace=None, stream=None, grads=None):
+    """S2-Attn backward of sum(o * do).  Returns (dq, dk, dv)."""
+    _check_tensors(q, k, v, (("o", o), ("lse", lse), ("do", do)))
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    if shift_heads is None:
+        shift_heads = H // 2
+    need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = grads
+    with torch.cuda.device(q.device):
+        st = _lib.load().s2attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), _ptr(do),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                    B, H, Hkv, N, d, G, shift_heads, _dtype_code(q), _stream(stream))
+    if st != _lib.S2ATTN_OK:
+        raise S2AttnError(st, "s2attn_bwd")
+    return dq, dk, dv
+
+
+class S2Attn(torch.autograd.Function):
+    """autograd wrapper: forward and backward both run in libs2attn."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, G, shift_heads):
+        o, lse = s2attn_fwd(q, k, v, G, shift_heads)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.G, ctx.shift_heads = G, shift_heads
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = s2attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.G, ctx.shift_heads)
+        return dq, dk, dv, None, None
+
+
+def s2attn(q, k, v, G, shift_heads=None):
+    """Differentiable S2-Attn on [B, N, H, d] tensors (shift_heads defaults to H // 2)."""
+    return S2Attn.apply(q, k, v, G, q.shape[2] // 2 if shift_heads is None else shift_heads)

@@ -1,0 +1,59 @@
+"""Build libs2attn.so in-tree with hipcc for gfx950.
+
+    python -m shifted_sparse_attention_s2attn_amd.build
+
+Each HIP source compiles to an object in parallel, then one shared library is
+linked next to this file.  Always rebuilds.
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libs2attn.so")
+SOURCES = ["s2attn_api.hip", "s2attn_fwd.hip", "s2attn_bwd.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-munsafe-fp-atomics",                                   # hardware fp32 atomic add for the dQ accumulator
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r
+
+
+def build(verbose=False, save_temps=False):
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if save_temps:
+            cmd += ["-save-temps=obj"]
+        objs.append(obj)
+        cmds.append(cmd)
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        for r in ex.map(_run, cmds):
+            if verbose and r.stderr.strip():
+                print(r.stderr, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True, save_temps="--save-temps" in sys.argv))

@@ -1,0 +1,107 @@
+// C ABI of libs2attn: host-side validation, workspace sizing and launch.
+// Every check runs on the host before any HIP call, so a rejected call
+// launches nothing.  The library keeps no state besides one flag per backward
+// kernel instantiation recording that its LDS limit was raised.
+#include "../../include/s2attn.h"
+#include "s2attn_common.h"
+
+namespace s2a {
+template <typename T, int D>
+hipError_t launch_fwd(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
+                      hipStream_t);
+template <typename T, int D>
+hipError_t launch_bwd(const void*, const void*, const void*, const void*, const float*, const void*, void*,
+                      void*, void*, float*, float*, int, int, int, int, int, int, hipStream_t);
+}  // namespace s2a
+
+namespace {
+
+constexpr int kTileRows = 128;   // query rows per forward workgroup = key rows per backward workgroup
+
+int check_problem(int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || G <= 0) return S2ATTN_ERR_SHAPE;
+  if (N % G != 0 || G % 2 != 0) return S2ATTN_ERR_SHAPE;
+  if (shift_heads < 0 || shift_heads > H) return S2ATTN_ERR_SHAPE;
+  if (H % Hkv != 0) return S2ATTN_ERR_SHAPE;
+  if (B > 65535 || H > 65535) return S2ATTN_ERR_UNSUPPORTED;   // grid y / z limits
+  if (d != 64 && d != 128) return S2ATTN_ERR_UNSUPPORTED;
+  if (dtype != S2ATTN_BF16 && dtype != S2ATTN_F32) return S2ATTN_ERR_UNSUPPORTED;
+  if (G % kTileRows != 0) return S2ATTN_ERR_UNSUPPORTED;
+  const int r = H / Hkv;
+  // A key/value head read by both shifted and unshifted query heads is tiled in
+  // the first head's frame; the other frame is offset by G/2, which must then
+  // be a whole number of tiles.
+  if (r > 1 && (H - shift_heads) % r != 0 && (G / 2) % kTileRows != 0) return S2ATTN_ERR_UNSUPPORTED;
+  return S2ATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return S2ATTN_ERR_NULL;
+  const int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st != S2ATTN_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == S2ATTN_BF16) {
+    e = d == 64 ? s2a::launch_fwd<s2a::bf16, 64>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, s)
+                : s2a::launch_fwd<s2a::bf16, 128>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, s);
+  } else {
+    e = d == 64 ? s2a::launch_fwd<float, 64>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, s)
+                : s2a::launch_fwd<float, 128>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, s);
+  }
+  return e == hipSuccess ? S2ATTN_OK : S2ATTN_ERR_HIP;
+}
+
+size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype) {
+  if (check_problem(B, H, Hkv, N, d, G, shift_heads, dtype) != S2ATTN_OK) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return align256(rows * sizeof(float)) + align256(rows * (size_t)d * sizeof(float));
+}
+
+int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+               int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
+  const int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st != S2ATTN_OK) return st;
+  const size_t need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return S2ATTN_ERR_WORKSPACE;
+  float* dvec = static_cast<float*>(workspace);
+  float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align256((size_t)B * H * N * sizeof(float)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == S2ATTN_BF16) {
+    e = d == 64 ? s2a::launch_bwd<s2a::bf16, 64>(q, k, v, o, lse, dO, dq, dk, dv, dvec, dq_acc, B, H, Hkv, N, G,
+                                                   shift_heads, s)
+                : s2a::launch_bwd<s2a::bf16, 128>(q, k, v, o, lse, dO, dq, dk, dv, dvec, dq_acc, B, H, Hkv, N, G,
+                                                    shift_heads, s);
+  } else {
+    e = d == 64 ? s2a::launch_bwd<float, 64>(q, k, v, o, lse, dO, dq, dk, dv, dvec, dq_acc, B, H, Hkv, N, G,
+                                             shift_heads, s)
+                : s2a::launch_bwd<float, 128>(q, k, v, o, lse, dO, dq, dk, dv, dvec, dq_acc, B, H, Hkv, N, G,
+                                              shift_heads, s);
+  }
+  return e == hipSuccess ? S2ATTN_OK : S2ATTN_ERR_HIP;
+}
+
+const char* s2attn_status_str(int status) {
+  switch (status) {
+    case S2ATTN_OK: return "ok";
+    case S2ATTN_ERR_NULL: return "a required pointer is NULL";
+    case S2ATTN_ERR_SHAPE: return "invalid shape (size <= 0, N % G != 0, odd G, shift_heads outside [0,H], or H % Hkv != 0)";
+    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype, G % 128 != 0, or mixed-shift KV head with (G/2) % 128 != 0)";
+    case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
+    case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

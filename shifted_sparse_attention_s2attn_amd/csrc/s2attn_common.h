@@ -1,0 +1,102 @@
+// Device helpers shared by the S2-Attn kernels (gfx950 / CDNA4).
+//
+// Matrix-core convention used everywhere: one wave (64 lanes) computes a 32x32
+// fp32 tile C += A (32 x 16) * B (16 x 32) per step.
+//   A operand: lane l holds row (l & 31), k-slots 8*(l >> 5) .. +7
+//   B operand: lane l holds col (l & 31), k-slots 8*(l >> 5) .. +7
+//   C tile   : lane l holds col (l & 31); register r holds
+//              row 8*(r >> 2) + 4*(l >> 5) + (r & 3)
+// bf16 issues one v_mfma_f32_32x32x16_bf16; fp32 issues eight
+// v_mfma_f32_32x32x2_f32, the i-th one consuming k-slot 8*(l >> 5) + i.
+//
+// When the rows of A are loaded in the order perm32(row) (bits 2 and 3 of the
+// row index swapped), register r of C holds row
+//     16*(r >> 3) + 8*(l >> 5) + (r & 7),
+// so registers 0..7 and 8..15 of a lane are two runs of 8 consecutive rows.
+// That run is exactly the k-slot layout of the next product's B operand, which
+// lets a softmax tile feed the following matrix product straight from
+// registers, and lets epilogues store 8 consecutive elements at once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s2a {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> { using type = bf16x8; };
+template <> struct Vec8<float> { using type = f32x8; };
+// Eight consecutive elements: the per-lane share of one A or B operand.
+template <typename T> using v8 = typename Vec8<T>::type;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma32(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
+}
+
+// Eight fp32 accumulator values (registers base..base+7) as an operand of type T.
+template <typename T>
+__device__ __forceinline__ v8<T> pack8(const f32x16& x, int base);
+
+template <>
+__device__ __forceinline__ bf16x8 pack8<bf16>(const f32x16& x, int base) {
+  f32x8 f = {x[base + 0], x[base + 1], x[base + 2], x[base + 3],
+             x[base + 4], x[base + 5], x[base + 6], x[base + 7]};
+  return __builtin_convertvector(f, bf16x8);   // round to nearest even
+}
+
+template <>
+__device__ __forceinline__ f32x8 pack8<float>(const f32x16& x, int base) {
+  f32x8 f = {x[base + 0], x[base + 1], x[base + 2], x[base + 3],
+             x[base + 4], x[base + 5], x[base + 6], x[base + 7]};
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ v8<T> scale8(const f32x16& x, int base, float s) {
+  f32x16 y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[base + i] = x[base + i] * s;
+  return pack8<T>(y, base);
+}
+
+// Swap bits 2 and 3 of a row index inside a 32-row tile.
+__device__ __forceinline__ int perm32(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// LDS tiles are arrays of 8-element chunks.  The chunk column of a row is
+// XOR-ed with swz(row) so that the eight rows perm32(0..7) read by one
+// quarter-wave land on eight different chunk columns.
+template <int CPR>  // chunks per row (power of two)
+__device__ __forceinline__ int swz(int row) {
+  return ((row & 3) | ((row >> 1) & 4)) & (CPR - 1);
+}
+
+template <int CPR>
+__device__ __forceinline__ int chunk_at(int row, int chunk) {
+  return row * CPR + (chunk ^ swz<CPR>(row));
+}
+
+// Original token index of rolled position j for a head rolled by sigma
+// (0 <= j < N, 0 <= sigma < N): the roll of the method folded into addresses.
+__device__ __forceinline__ int orig_row(int j, int sigma, int N) {
+  int t = j + sigma;
+  return t >= N ? t - N : t;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace s2a

@@ -1,0 +1,225 @@
+// S2-Attn forward kernel for gfx950.
+//
+// Method: page "LongLoRA: Efficient Fine-tuning of Long-Context Large Language
+// Models", section 3.4 ("The core computational problem", "The solution: group
+// tokens and compute attention locally", "The shifting mechanism" Steps 1-3,
+// "Algorithmic implementation" / Algorithm 1).  Each (batch, head, group) is an
+// independent causal attention over G tokens; heads h >= H - shift_heads read
+// their tokens rolled by G/2, so rolled row j is original token (j + G/2) mod N,
+// and write their outputs back at the original rows (the roll-back).
+//
+// One workgroup = 4 waves = 128 consecutive query rows (rolled frame) of one
+// (batch, head).  Each wave owns 32 query rows; its Q operand stays in
+// registers.  Key/value tiles of 64 rows stream through LDS (K row-major,
+// V transposed), with the next tile's global loads issued before the current
+// tile is computed.  Per tile and wave:
+//     S^T = K Q^T        (keys on the tile rows, the wave's 32 queries on lanes)
+//     causal mask on the diagonal tiles, online softmax (one query per lane,
+//     its 32 keys split across lanes l and l ^ 32)
+//     O^T += V^T P^T     (P^T comes straight from the S^T registers)
+// Finally O = O^T / l is stored at the original rows with lse = m + ln l.
+#include "s2attn_common.h"
+
+namespace s2a {
+
+template <typename T, int D>
+struct FwdShape {
+  static constexpr int kThreads = 256;
+  static constexpr int kBR = 128;               // query rows per workgroup
+  static constexpr int kBC = 64;                // key rows per tile
+  static constexpr int kKCPR = D / 8;           // chunks per K row
+  static constexpr int kVCPR = kBC / 8;         // chunks per transposed V row
+  static constexpr int kKChunksPerThread = kBC * kKCPR / kThreads;
+  static constexpr int kVKeysPerThread = kBC * D / 8 / kThreads;
+  static constexpr int kDC = D / 16;            // k-steps over the head dim
+  static constexpr int kDT = D / 32;            // 32-wide output tiles over the head dim
+  static constexpr int kKS = kBC / 32;          // 32-key score tiles per key tile
+};
+
+template <typename T, int N_>
+struct alignas(sizeof(T) * N_) PackN { T x[N_]; };
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void s2attn_fwd_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    T* __restrict__ o, float* __restrict__ lse,
+    int N, int H, int Hkv, int G, int shift_heads, float scale) {
+  using S = FwdShape<T, D>;
+  constexpr int BR = S::kBR, BC = S::kBC, KCPR = S::kKCPR, VCPR = S::kVCPR;
+  constexpr int KPT = S::kKChunksPerThread, VKPT = S::kVKeysPerThread;
+  __shared__ v8<T> Ks[BC * KCPR];
+  __shared__ v8<T> Vt[D * VCPR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  // Heaviest query tiles (last in their group) are dispatched first.
+  const int groups = N / G, tiles_per_group = G / BR;
+  const int x = blockIdx.x;
+  const int pos = tiles_per_group - 1 - x / groups;
+  const int grp = x % groups;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int c = h / (H / Hkv);
+  const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
+
+  const int j0 = grp * G + pos * BR;            // first query row (rolled)
+  const int kv_begin = grp * G;                 // first key row of the group (rolled)
+  const int ntiles = (j0 + BR - kv_begin) / BC;
+
+  const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
+  const T* qb = q + (size_t)b * N * qstride + (size_t)h * D;
+  const T* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
+  const T* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
+
+  // ---- Q operand (B of S^T = K Q^T): query (l32), 8 head-dim values per k-step
+  const int jw = j0 + wave * 32;                // wave's first query (rolled)
+  const int jq = jw + l32;                      // this lane's query (rolled)
+  const int tq = orig_row(jq, sigma, N);
+  v8<T> qf[S::kDC];
+#pragma unroll
+  for (int cc = 0; cc < S::kDC; ++cc)
+    qf[cc] = *reinterpret_cast<const v8<T>*>(qb + (size_t)tq * qstride + cc * 16 + hf * 8);
+
+  // ---- key / value tile staging: global -> registers -> LDS
+  v8<T> kreg[KPT];
+  v8<T> vreg[VKPT];
+  const int v_dc = tid % (D / 8);               // head-dim chunk this thread transposes
+  const int v_kg = tid / (D / 8);               // key group (VKPT keys)
+
+  auto load_tile = [&](int kt0) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int ci = tid + i * 256;
+      const int row = ci / KCPR, cc = ci % KCPR;
+      const int t = orig_row(kt0 + row, sigma, N);
+      kreg[i] = *reinterpret_cast<const v8<T>*>(kb + (size_t)t * kvstride + cc * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VKPT; ++i) {
+      const int t = orig_row(kt0 + v_kg * VKPT + i, sigma, N);
+      vreg[i] = *reinterpret_cast<const v8<T>*>(vb + (size_t)t * kvstride + v_dc * 8);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int ci = tid + i * 256;
+      const int row = ci / KCPR, cc = ci % KCPR;
+      Ks[chunk_at<KCPR>(row, cc)] = kreg[i];
+    }
+    // V transposed: row = head-dim index, VKPT consecutive keys per write
+    const int kcol = v_kg * VKPT;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = v_dc * 8 + e;
+      PackN<T, VKPT> pk;
+#pragma unroll
+      for (int i = 0; i < VKPT; ++i) pk.x[i] = vreg[i][e];
+      T* rowp = reinterpret_cast<T*>(&Vt[chunk_at<VCPR>(d, kcol / 8)]);
+      *reinterpret_cast<PackN<T, VKPT>*>(rowp + (kcol % 8)) = pk;
+    }
+  };
+
+  f32x16 oacc[S::kDT];
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = scale * kLog2e;
+
+  load_tile(kv_begin);
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt0 = kv_begin + it * BC;
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(kt0 + BC);
+
+    if (kt0 > jw + 31) continue;                // tile entirely after this wave's queries
+    const bool need_mask = kt0 + BC - 1 > jw;
+
+    // S^T = K Q^T
+    f32x16 s[S::kKS];
+#pragma unroll
+    for (int ks = 0; ks < S::kKS; ++ks) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[ks][r] = 0.f;
+      const int row = ks * 32 + perm32(l32);
+#pragma unroll
+      for (int cc = 0; cc < S::kDC; ++cc) mma32(s[ks], Ks[chunk_at<KCPR>(row, cc * 2 + hf)], qf[cc]);
+    }
+
+    // causal mask + online softmax (raw scores; the scale is folded into exp2)
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < S::kKS; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (need_mask) {
+          const int key = kt0 + ks * 32 + (r >> 3) * 16 + hf * 8 + (r & 7);
+          if (key > jq) s[ks][r] = -INFINITY;
+        }
+        mloc = fmaxf(mloc, s[ks][r]);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);     // finite: the group's first key is in the first tile
+    const float alpha = fast_exp2((m_run - m_new) * c2);
+    const float nm = -m_new * c2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < S::kKS; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[ks][r], c2, nm));
+        s[ks][r] = p;
+        lsum += p;
+      }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+    // O^T += V^T P^T : 16 keys per k-step, P^T from the S^T registers
+#pragma unroll
+    for (int kc = 0; kc < BC / 16; ++kc) {
+      const v8<T> pf = pack8<T>(s[kc >> 1], (kc & 1) * 8);
+#pragma unroll
+      for (int dt = 0; dt < S::kDT; ++dt) {
+        const int row = dt * 32 + perm32(l32);
+        mma32(oacc[dt], Vt[chunk_at<VCPR>(row, kc * 2 + hf)], pf);
+      }
+    }
+  }
+
+  // ---- epilogue: normalise, store O and lse at the original row
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.f / l_tot;
+  T* orow = o + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<v8<T>*>(orow + dt * 32 + u * 16 + hf * 8) = scale8<T>(oacc[dt], u * 8, inv);
+  if (hf == 0) lse[((size_t)b * H + h) * N + tq] = m_run * scale + logf(l_tot);
+}
+
+template <typename T, int D>
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Hkv, int N, int G, int shift_heads, hipStream_t stream) {
+  dim3 grid(N / FwdShape<T, D>::kBR, H, B);
+  const float scale = 1.0f / sqrtf((float)D);
+  hipLaunchKernelGGL((s2attn_fwd_kernel<T, D>), grid, dim3(256), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, scale);
+  return hipGetLastError();
+}
+
+template hipError_t launch_fwd<bf16, 64>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, hipStream_t);
+template hipError_t launch_fwd<bf16, 128>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, hipStream_t);
+template hipError_t launch_fwd<float, 64>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, hipStream_t);
+template hipError_t launch_fwd<float, 128>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, hipStream_t);
+
+}  // namespace s2a

@@ -60,15 +60,21 @@ def small_workload(name="custom", B=1, H=4, Hkv=4, d=64, N=512, G=128, shift_hea
     return Workload(name, B, H, Hkv, d, N, G, shift_heads, dtype, qk_quarter_scale)
 
 
-def make_inputs(w, seed=0):
-    """Return dict(q, k, v, do) as CPU tensors of the workload dtype."""
-    g = torch.Generator(device="cpu").manual_seed(seed)
+def make_inputs(w, seed=0, device="cpu"):
+    """Return dict(q, k, v, do) of the workload dtype on ``device``.
+
+    The generator lives on ``device`` (torch's CPU generator, or the GPU's
+    Philox generator for the large workloads), so values depend on the device;
+    a run that checks against the oracle copies the very tensors it used.
+    """
+    g = torch.Generator(device=device).manual_seed(seed)
     qs = (w.B, w.N, w.H, w.d)
     kvs = (w.B, w.N, w.Hkv, w.d)
-    q = torch.randn(qs, dtype=torch.float32, generator=g)
-    k = torch.randn(kvs, dtype=torch.float32, generator=g)
-    v = torch.randn(kvs, dtype=torch.float32, generator=g)
-    do = torch.randn(qs, dtype=torch.float32, generator=g)
+    kw = dict(dtype=torch.float32, generator=g, device=device)
+    q = torch.randn(qs, **kw)
+    k = torch.randn(kvs, **kw)
+    v = torch.randn(kvs, **kw)
+    do = torch.randn(qs, **kw)
     if w.qk_quarter_scale:
         f = float(w.d) ** -0.25
         q.mul_(f)

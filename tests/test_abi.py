@@ -1,0 +1,111 @@
+"""The C ABI library: it loads, exports what the header declares, and its host-side
+validation returns the documented status codes before any HIP call (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from shifted_sparse_attention_s2attn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "s2attn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s2attn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_abi():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.s2attn_status_str(code)
+    assert lib.s2attn_status_str(99) == b"unknown status"
+
+
+DUMMY = ctypes.c_void_p(0x1000)   # never dereferenced: validation rejects before any HIP call
+FDUMMY = ctypes.cast(DUMMY, ctypes.POINTER(ctypes.c_float))
+GOOD = dict(B=1, H=4, Hkv=4, N=512, d=64, G=128, S=2, dtype=0)
+
+
+def fwd_status(lib, ptrs=True, **kw):
+    p = dict(GOOD)
+    p.update(kw)
+    ptr = DUMMY if ptrs else None
+    return lib.s2attn_fwd(ptr, ptr, ptr, ptr, FDUMMY if ptrs else None,
+                          p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"], p["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=500), _lib.S2ATTN_ERR_SHAPE),          # N % G != 0
+    (dict(G=129, N=129 * 4), _lib.S2ATTN_ERR_SHAPE),  # odd G
+    (dict(S=5), _lib.S2ATTN_ERR_SHAPE),
+    (dict(S=-1), _lib.S2ATTN_ERR_SHAPE),
+    (dict(Hkv=3), _lib.S2ATTN_ERR_SHAPE),
+    (dict(B=0), _lib.S2ATTN_ERR_SHAPE),
+    (dict(d=96), _lib.S2ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.S2ATTN_ERR_UNSUPPORTED),
+    (dict(G=64, N=512), _lib.S2ATTN_ERR_UNSUPPORTED),   # G not a multiple of 128
+    (dict(H=6, Hkv=2, S=2, G=128, N=512), _lib.S2ATTN_ERR_UNSUPPORTED),  # mixed-shift KV head, G/2 % 128 != 0
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd_status(lib, **kw) == code
+
+
+def test_fwd_null_pointer(lib):
+    assert fwd_status(lib, ptrs=False) == _lib.S2ATTN_ERR_NULL
+
+
+def test_mixed_shift_allowed_when_half_group_is_tile_aligned(lib):
+    assert lib.s2attn_bwd_workspace_bytes(1, 6, 2, 1024, 64, 256, 2, 0) > 0
+    assert lib.s2attn_bwd_workspace_bytes(1, 6, 2, 1024, 64, 128, 2, 0) == 0
+
+
+def test_workspace_size(lib):
+    B, H, Hkv, N, d, G, S = 1, 32, 32, 32768, 128, 8192, 16
+    n = lib.s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, S, 0)
+    assert n == B * H * N * 4 + B * N * H * d * 4
+    assert lib.s2attn_bwd_workspace_bytes(B, H, Hkv, N, 96, G, S, 0) == 0
+
+
+def test_bwd_workspace_checks(lib):
+    p = GOOD
+    need = lib.s2attn_bwd_workspace_bytes(p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"], 0)
+    args = [DUMMY] * 4 + [FDUMMY] + [DUMMY] * 4
+    dims = [p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"], 0, None]
+    assert lib.s2attn_bwd(*args, DUMMY, need - 1, *dims) == _lib.S2ATTN_ERR_WORKSPACE
+    assert lib.s2attn_bwd(*args, None, need, *dims) == _lib.S2ATTN_ERR_WORKSPACE
+    assert lib.s2attn_bwd(*args, ctypes.c_void_p(0x1010), need, *dims) == _lib.S2ATTN_ERR_WORKSPACE
+    bad = list(args)
+    bad[6] = None
+    assert lib.s2attn_bwd(*bad, DUMMY, need, *dims) == _lib.S2ATTN_ERR_NULL
+    dims_bad = list(dims)
+    dims_bad[3] = 500
+    assert lib.s2attn_bwd(*args, DUMMY, need, *dims_bad) == _lib.S2ATTN_ERR_SHAPE
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The package never imports the oracle and has no non-HIP compute path."""
+    pkg = os.path.join(ROOT, "shifted_sparse_attention_s2attn_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg, name)).read()
+            assert not re.search(r"^\s*(from|import)\s+oracle|s2attn_oracle", src, flags=re.M), name
+            assert "scaled_dot_product_attention" not in src, name

@@ -1,0 +1,210 @@
+"""HIP path (through the C ABI) against the float64 oracle, element by element.
+
+Small problems are checked on every output element.  The five named workloads
+run at full size in the library's only launch configuration; their outputs are
+checked on sampled (key/value head, group) slices that the oracle computes one
+by one, plus properties that hold everywhere (finite values, the closed form of
+the first row of every group).
+
+Bars: bf16 inputs with fp32 accumulation: max |O - O*| <= 2e-2 and
+||x - x*||_2 / ||x*||_2 <= 3e-2 for each of dQ, dK, dV; fp32 inputs: both
+metrics <= 1e-4.  lse is compared as a diagnostic (1e-3 bf16, 1e-4 fp32).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import s2attn_oracle as orc
+from shifted_sparse_attention_s2attn_amd import S2AttnError, s2attn, s2attn_bwd, s2attn_fwd
+from shifted_sparse_attention_s2attn_amd.inputs import WORKLOADS, make_inputs, small_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": dict(o=2e-2, grad=3e-2, lse=1e-3), "f32": dict(o=1e-4, grad=1e-4, lse=1e-4)}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_gpu(inp):
+    return {k: v.cuda() for k, v in inp.items()}
+
+
+def run_gpu(w, t):
+    o, lse = s2attn_fwd(t["q"], t["k"], t["v"], w.G, w.shift_heads)
+    dq, dk, dv = s2attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], w.G, w.shift_heads)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def f64(x):
+    return x.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def check_full(w, inp, out):
+    tol = TOL[w.dtype]
+    o, lse, dq, dk, dv = (f64(x) for x in out)
+    q, k, v, do = (f64(inp[n]) for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = orc.forward(q, k, v, w.G, w.shift_heads)
+    dq_ref, dk_ref, dv_ref = orc.backward(q, k, v, do, w.G, w.shift_heads)
+    err_o = float(np.max(np.abs(o - o_ref)))
+    err_lse = float(np.max(np.abs(lse - lse_ref)))
+    errs = {n: rel_l2(a, b) for n, a, b in (("dq", dq, dq_ref), ("dk", dk, dk_ref), ("dv", dv, dv_ref))}
+    say(f"  max|dO|={err_o:.3e} max|dlse|={err_lse:.3e} relL2 {errs}")
+    assert err_o <= tol["o"]
+    assert err_lse <= tol["lse"]
+    for n, e in errs.items():
+        assert e <= tol["grad"], (n, e)
+
+
+SMALL = [
+    small_workload("bf16-d128-mha", B=2, H=4, Hkv=4, d=128, N=1024, G=256, shift_heads=2),
+    small_workload("bf16-d64-gqa2", B=1, H=4, Hkv=2, d=64, N=1024, G=512, shift_heads=2),
+    small_workload("bf16-gqa3-mixed-shift", B=1, H=6, Hkv=2, d=128, N=1024, G=256, shift_heads=2),
+    small_workload("bf16-gqa8", B=1, H=16, Hkv=2, d=128, N=1024, G=256, shift_heads=8),
+    small_workload("bf16-only-unshifted", B=1, H=2, Hkv=2, d=128, N=768, G=256, shift_heads=0),
+    small_workload("bf16-only-shifted", B=1, H=2, Hkv=2, d=64, N=768, G=256, shift_heads=2),
+    small_workload("bf16-full-causal", B=1, H=2, Hkv=1, d=128, N=1024, G=1024, shift_heads=0),
+    small_workload("bf16-single-group-shifted", B=2, H=2, Hkv=2, d=128, N=128, G=128, shift_heads=1),
+    small_workload("bf16-qk-scaled", B=1, H=4, Hkv=4, d=128, N=512, G=128, shift_heads=2, qk_quarter_scale=True),
+    small_workload("f32-d128", B=1, H=2, Hkv=2, d=128, N=512, G=256, shift_heads=1, dtype="f32"),
+    small_workload("f32-gqa2", B=2, H=4, Hkv=2, d=64, N=256, G=128, shift_heads=2, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_parity(w):
+    say(f"case {w}")
+    inp = make_inputs(w, seed=1)
+    out = run_gpu(w, to_gpu(inp))
+    check_full(w, inp, out)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_tiny_f32_workload(seed):
+    """B=1, H=4 (2 shifted), d=64, N=512, G=128, fp32; seeds 0-9."""
+    w = WORKLOADS["tiny-f32"]
+    say(f"case {w.name} seed {seed}")
+    inp = make_inputs(w, seed=seed)
+    out = run_gpu(w, to_gpu(inp))
+    check_full(w, inp, out)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled slices + global properties
+# ---------------------------------------------------------------------------
+
+SAMPLES = {   # (key/value head, group index in the frame of that KV head's first query head)
+    "llama2-7b-8k": [(0, 1), (31, 3)],
+    "llama2-7b-32k": [(0, 0), (31, 3)],
+    "llama2-7b-100k": [(5, 2), (31, 3)],
+    "llama2-70b-gqa-32k": [(0, 2), (7, 3)],
+}
+
+
+def check_sampled(w, t, out, c, g0, b=0):
+    tol = TOL[w.dtype]
+    o, lse, dq, dk, dv = out
+    r = w.H // w.Hkv
+    S_sub = max(0, min(r, (c + 1) * r - (w.H - w.shift_heads)))
+    hs = slice(c * r, (c + 1) * r)
+    q = f64(t["q"][:, :, hs])
+    k = f64(t["k"][:, :, c:c + 1])
+    v = f64(t["v"][:, :, c:c + 1])
+    do = f64(t["do"][:, :, hs])
+    N, G = w.N, w.G
+    R = orc.rolled_order(N, orc.head_shift(0, r, S_sub, G))[g0 * G:(g0 + 1) * G]
+    dk_acc = np.zeros((N, w.d))
+    dv_acc = np.zeros((N, w.d))
+    o_err, lse_err = 0.0, 0.0
+    dq_num, dq_den = 0.0, 0.0
+    for hh in range(r):
+        h = c * r + hh
+        sig = orc.head_shift(hh, r, S_sub, G)
+        for g in sorted(set(((R - sig) % N) // G)):
+            rows, Og, lseg = orc.head_group_forward(q, k, v, G, S_sub, b, hh, g)
+            ridx = torch.as_tensor(rows, device=o.device)
+            o_err = max(o_err, float(np.max(np.abs(f64(o[b, ridx, h]) - Og))))
+            lse_err = max(lse_err, float(np.max(np.abs(f64(lse[b, h, ridx]) - lseg))))
+            rows, dQg, dKg, dVg = orc.head_group_backward(q, k, v, do, G, S_sub, b, hh, g)
+            dq_num += float(np.sum((f64(dq[b, ridx, h]) - dQg) ** 2))
+            dq_den += float(np.sum(dQg ** 2))
+            dk_acc[rows] += dKg
+            dv_acc[rows] += dVg
+    Ridx = torch.as_tensor(R, device=o.device)
+    e_dk = rel_l2(f64(dk[b, Ridx, c]), dk_acc[R])
+    e_dv = rel_l2(f64(dv[b, Ridx, c]), dv_acc[R])
+    e_dq = (dq_num / dq_den) ** 0.5
+    say(f"  kv head {c} group {g0}: max|dO|={o_err:.3e} max|dlse|={lse_err:.3e} "
+        f"relL2 dq={e_dq:.3e} dk={e_dk:.3e} dv={e_dv:.3e}")
+    assert o_err <= tol["o"]
+    assert lse_err <= tol["lse"]
+    assert e_dq <= tol["grad"] and e_dk <= tol["grad"] and e_dv <= tol["grad"]
+
+
+def check_global(w, t, out):
+    o, lse, dq, dk, dv = out
+    for name, x in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(x).all()), f"non-finite values in {name}"
+    # first row of every group attends to itself only: O = V exactly, lse = scale q.k
+    r = w.H // w.Hkv
+    for h in range(w.H):
+        sig = w.G // 2 if h >= w.H - w.shift_heads else 0
+        first = (torch.arange(0, w.N, w.G, device=o.device) + sig) % w.N
+        c = h // r
+        assert torch.equal(o[:, first, h], t["v"][:, first, c]), f"first-row O head {h}"
+        ref = (t["q"][:, first, h].float() * t["k"][:, first, c].float()).sum(-1) / w.d ** 0.5
+        assert float((lse[:, h, first] - ref).abs().max()) <= 1e-3, f"first-row lse head {h}"
+
+
+@pytest.mark.parametrize("name", list(SAMPLES))
+def test_full_size_workload(name):
+    w = WORKLOADS[name]
+    say(f"case {w} (generating inputs on the GPU)")
+    t = make_inputs(w, seed=0, device="cuda")
+    out = run_gpu(w, t)
+    say("  kernels done; global checks")
+    check_global(w, t, out)
+    for c, g0 in SAMPLES[name]:
+        check_sampled(w, t, out, c, g0)
+
+
+# ---------------------------------------------------------------------------
+# determinism, autograd wrapper, error path
+# ---------------------------------------------------------------------------
+
+def test_repeatability():
+    """Forward, dK and dV are bitwise repeatable; dQ differs only by fp32 atomic order."""
+    w = small_workload("rep", B=1, H=8, Hkv=2, d=128, N=2048, G=512, shift_heads=4)
+    say(f"case {w}")
+    t = to_gpu(make_inputs(w, seed=3))
+    a = run_gpu(w, t)
+    b = run_gpu(w, t)
+    for i in (0, 1, 3, 4):
+        assert torch.equal(a[i], b[i])
+    assert float((a[2].float() - b[2].float()).abs().max()) <= 1e-2
+
+
+def test_autograd_wrapper():
+    w = small_workload("autograd", B=1, H=4, Hkv=4, d=64, N=512, G=256, shift_heads=2)
+    say(f"case {w}")
+    t = to_gpu(make_inputs(w, seed=4))
+    q, k, v = (t[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    o = s2attn(q, k, v, w.G, w.shift_heads)
+    (o.float() * t["do"].float()).sum().backward()
+    ref = run_gpu(w, t)
+    assert torch.equal(o, ref[0])
+    assert torch.equal(k.grad, ref[3]) and torch.equal(v.grad, ref[4])
+    assert float((q.grad.float() - ref[2].float()).abs().max()) <= 1e-2
+
+
+def test_rejected_shape_raises():
+    q = torch.zeros((1, 500, 2, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(S2AttnError):
+        s2attn_fwd(q, q, q, 128, 1)
