@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the S2-Attn hot path on one MI355X: forward + backward per step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward (s2attn_fwd) and one backward (its three stages) over one
+batch of seeded synthetic inputs already resident in HBM.  W untimed steps,
+then K steps between two device synchronisations; the wall time of those K
+steps gives ``value`` (effective TFLOP/s: group-local causal pairs only, 4d
+FLOP per pair forward, 10d backward).  HIP events recorded on the launch
+stream around every kernel launch give each kernel's average duration; the
+longest one is the roofline kernel.  Afterwards the float64 CPU oracle is
+timed on a bounded sample of the same workload (rank 0, one GPU only).
+
+Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "shifted_sparse_attention_s2attn_amd", "csrc")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if current.
+
+    The summary lists FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the kernel,
+    the same counters for a plain copy kernel of known size, and the hash of the
+    kernel sources they were taken with.  Returns None when absent or stale.
+    """
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != kernel_source_hash():
+        return None
+    fetch_scale = float(vals["copy_bytes_read"]) / (float(vals["copy_fetch_kib"]) * 1024)
+    write_scale = float(vals["copy_bytes_written"]) / (float(vals["copy_write_kib"]) * 1024)
+    return (float(vals["kernel_fetch_kib"]) * 1024 * fetch_scale +
+            float(vals["kernel_write_kib"]) * 1024 * write_scale)
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, t, seconds):
+    """Time the float64 oracle (fwd + bwd) on whole (batch, head, group) slices of the inputs."""
+    import numpy as np
+    from oracle import s2attn_oracle as orc
+    r = w.H // w.Hkv
+    done, flop, el = 0, 0, 0.0
+    for h in range(w.H):
+        c = h // r
+        q = t["q"][:, :, h:h + 1].float().cpu().numpy().astype(np.float64)
+        k = t["k"][:, :, c:c + 1].float().cpu().numpy().astype(np.float64)
+        v = t["v"][:, :, c:c + 1].float().cpu().numpy().astype(np.float64)
+        do = t["do"][:, :, h:h + 1].float().cpu().numpy().astype(np.float64)
+        S1 = 1 if h >= w.H - w.shift_heads else 0
+        for g in range(w.N // w.G):
+            t0 = time.perf_counter()
+            orc.head_group_forward(q, k, v, w.G, S1, 0, 0, g)
+            orc.head_group_backward(q, k, v, do, w.G, S1, 0, 0, g)
+            el += time.perf_counter() - t0
+            done += 1
+            flop += 14 * w.d * w.G * (w.G + 1) // 2
+            if el >= seconds:
+                break
+        if el >= seconds:
+            break
+    return {
+        "value": flop / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{done} (batch, head, group) slices of {w.G} query rows, forward + backward, "
+                  f"float64 NumPy, {el:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2-7b-32k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "attention units (batch, head, group) are independent, so several GPUs would each "
+              "run this same kernel on their own share of heads or batch.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from shifted_sparse_attention_s2attn_amd import (s2attn_bwd_finish, s2attn_bwd_main, s2attn_bwd_prep,
+                                                     s2attn_bwd_workspace_bytes, s2attn_fwd)
+    from shifted_sparse_attention_s2attn_amd import flops as F
+    from shifted_sparse_attention_s2attn_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = make_inputs(w, seed=0, device="cuda")
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(s2attn_bwd_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.G, w.shift_heads, q.dtype),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["s2attn_fwd_kernel", "s2attn_bwd_pre", "s2attn_bwd_main", "s2attn_bwd_cvt"]
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        s2attn_fwd(q, k, v, w.G, w.shift_heads, out=o, lse=lse)
+        if ev:
+            ev[1].record(stream)
+        s2attn_bwd_prep(q, k, o, do, ws, w.G, w.shift_heads)
+        if ev:
+            ev[2].record(stream)
+        s2attn_bwd_main(q, k, v, lse, do, dk, dv, ws, w.G, w.shift_heads)
+        if ev:
+            ev[3].record(stream)
+        s2attn_bwd_finish(q, k, dq, ws, w.G, w.shift_heads)
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el * 1e3 / args.steps
+
+    kern_ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
+    fwd_f = F.fwd_flops(w.B, w.H, w.N, w.G, w.d)
+    bwd_f = F.bwd_flops(w.B, w.H, w.N, w.G, w.d)
+    peak = F.MI355X_BF16_PEAK_TFLOPS if w.dtype == "bf16" else F.MI355X_F32_PEAK_TFLOPS
+    elt = 2 if w.dtype == "bf16" else 4
+    kern_flops = {"s2attn_fwd_kernel": fwd_f, "s2attn_bwd_main": bwd_f}
+    dominant = max(kern_ms, key=kern_ms.get)
+    kernels = {}
+    for n, ms in kern_ms.items():
+        kernels[n] = {"ms": round(ms, 4)}
+        if n in kern_flops:
+            kernels[n]["tflops"] = round(kern_flops[n] / ms / 1e9, 1)
+            kernels[n]["frac_of_peak"] = round(kern_flops[n] / ms / 1e9 / peak, 4)
+    fwd_ms = kern_ms["s2attn_fwd_kernel"]
+    bwd_ms = kern_ms["s2attn_bwd_pre"] + kern_ms["s2attn_bwd_main"] + kern_ms["s2attn_bwd_cvt"]
+    if dominant in kern_flops:
+        achieved = kern_flops[dominant] / kern_ms[dominant] / 1e9
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        nbytes = {"s2attn_bwd_pre": 2 * elt * w.B * w.N * w.H * w.d + 4 * w.B * w.H * w.N
+                  + 4 * w.B * w.N * w.H * w.d,
+                  "s2attn_bwd_cvt": (4 + elt) * w.B * w.N * w.H * w.d}[dominant]
+        achieved = nbytes / kern_ms[dominant] / 1e6
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": F.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / F.MI355X_HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dominant
+    roof["traffic"] = read_traffic(dominant, w.name)
+
+    result = {
+        "metric": "S2-Attn fwd+bwd effective TFLOP/s (group-local causal pairs), % of bf16 MFMA peak",
+        "value": round((fwd_f + bwd_f) / (ms_step / 1e3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "d": w.d, "N": w.N, "G": w.G,
+                   "shift_heads": w.shift_heads, "parallelism": "none"},
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_f / fwd_ms / 1e9, 1),
+                "frac_of_peak": round(fwd_f / fwd_ms / 1e9 / peak, 4)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_f / bwd_ms / 1e9, 1),
+                "frac_of_peak": round(bwd_f / bwd_ms / 1e9 / peak, 4)},
+        "frac_of_peak": round((fwd_f + bwd_f) / (ms_step / 1e3) / 1e12 / peak, 4),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -93,6 +93,31 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
                int B, int H, int Hkv, int N, int d, int G, int shift_heads,
                int dtype, void* stream);
 
+/*
+ * The backward as its three stages, in this order on one stream; s2attn_bwd
+ * is exactly these three calls.  Same arguments, checks and workspace as
+ * s2attn_bwd; the workspace must not be touched between the stages.
+ *   prep  : Dvec[b,h,t] = sum_c dO[b,t,h,c] * o[b,t,h,c] (fp32) into the
+ *           workspace, and clears the fp32 dq accumulator.
+ *   main  : dk and dv (written), dq accumulated into the workspace.  The
+ *           backward of "The shifting mechanism" / Algorithm 1 (page section
+ *           3.4): P = exp(scale q k^T - lse) causal within each group of the
+ *           rolled frame, dv = P^T dO, dS = P * (dO v^T - Dvec),
+ *           dk = scale dS^T q, dq += scale dS k.
+ *   finish: dq = accumulator rounded to the tensor type.
+ * Useful to callers that schedule the stages themselves (and to time them).
+ */
+int s2attn_bwd_prep(const void* o, const void* dO, void* workspace, size_t workspace_bytes,
+                    int B, int H, int Hkv, int N, int d, int G, int shift_heads,
+                    int dtype, void* stream);
+int s2attn_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                    void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                    int B, int H, int Hkv, int N, int d, int G, int shift_heads,
+                    int dtype, void* stream);
+int s2attn_bwd_finish(void* dq, void* workspace, size_t workspace_bytes,
+                      int B, int H, int Hkv, int N, int d, int G, int shift_heads,
+                      int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* s2attn_status_str(int status);
 

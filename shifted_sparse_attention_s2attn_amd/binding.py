@@ -12,6 +12,7 @@ import torch
 from . import _lib
 
 __all__ = ["S2AttnError", "s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes",
+           "s2attn_bwd_prep", "s2attn_bwd_main", "s2attn_bwd_finish",
            "s2attn_status_str", "S2Attn", "s2attn"]
 
 
@@ -54,12 +55,8 @@ def _check_tensors(q, k, v, extra=()):
 
 
 def _stream(stream):
-    s = torch.cuda.current_stream(q_device()) if stream is None else stream
+    s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
-
-
-def q_device():
-    return torch.cuda.current_device()
 
 
 def s2attn_fwd(q, k, v, G, shift_heads=None, out=None, lse=None, stream=None):
@@ -105,6 +102,44 @@ def s2attn_bwd(q, k, v, o, lse, do, G, shift_heads=None, workspace=None, stream=
     if st != _lib.S2ATTN_OK:
         raise S2AttnError(st, "s2attn_bwd")
     return dq, dk, dv
+
+
+def _dims(q, k, shift_heads):
+    B, N, H, d = q.shape
+    return B, H, k.shape[2], N, d, (H // 2 if shift_heads is None else shift_heads)
+
+
+def _check(st, where):
+    if st != _lib.S2ATTN_OK:
+        raise S2AttnError(st, where)
+
+
+def s2attn_bwd_prep(q, k, o, do, workspace, G, shift_heads=None, stream=None):
+    """Stage 1 of the backward: Dvec = rowsum(dO * o) and the dq accumulator cleared."""
+    B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
+    with torch.cuda.device(q.device):
+        _check(_lib.load().s2attn_bwd_prep(_ptr(o), _ptr(do), _ptr(workspace), workspace.numel(),
+                                           B, H, Hkv, N, d, G, S, _dtype_code(q), _stream(stream)),
+               "s2attn_bwd_prep")
+
+
+def s2attn_bwd_main(q, k, v, lse, do, dk, dv, workspace, G, shift_heads=None, stream=None):
+    """Stage 2 of the backward: dk, dv written; dq accumulated in the workspace."""
+    B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
+    with torch.cuda.device(q.device):
+        _check(_lib.load().s2attn_bwd_main(_ptr(q), _ptr(k), _ptr(v), _fptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
+                                           _ptr(workspace), workspace.numel(),
+                                           B, H, Hkv, N, d, G, S, _dtype_code(q), _stream(stream)),
+               "s2attn_bwd_main")
+
+
+def s2attn_bwd_finish(q, k, dq, workspace, G, shift_heads=None, stream=None):
+    """Stage 3 of the backward: dq from the fp32 accumulator."""
+    B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
+    with torch.cuda.device(q.device):
+        _check(_lib.load().s2attn_bwd_finish(_ptr(dq), _ptr(workspace), workspace.numel(),
+                                             B, H, Hkv, N, d, G, S, _dtype_code(q), _stream(stream)),
+               "s2attn_bwd_finish")
 
 
 class S2Attn(torch.autograd.Function):

@@ -10,8 +10,12 @@ template <typename T, int D>
 hipError_t launch_fwd(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
                       hipStream_t);
 template <typename T, int D>
-hipError_t launch_bwd(const void*, const void*, const void*, const void*, const float*, const void*, void*,
-                      void*, void*, float*, float*, int, int, int, int, int, int, hipStream_t);
+hipError_t launch_bwd_prep(const void*, const void*, float*, float*, int, int, int, hipStream_t);
+template <typename T, int D>
+hipError_t launch_bwd_main(const void*, const void*, const void*, const float*, const void*, void*, void*,
+                           const float*, float*, int, int, int, int, int, int, hipStream_t);
+template <typename T, int D>
+hipError_t launch_bwd_finish(void*, const float*, int, int, int, hipStream_t);
 }  // namespace s2a
 
 namespace {
@@ -64,32 +68,107 @@ size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G, in
   return align256(rows * sizeof(float)) + align256(rows * (size_t)d * sizeof(float));
 }
 
+}  // extern "C"
+
+namespace {
+
+struct Workspace {
+  float* dvec;
+  float* dq_acc;
+};
+
+int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d, int G,
+                    int shift_heads, int dtype, Workspace* ws) {
+  const size_t need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return S2ATTN_ERR_WORKSPACE;
+  ws->dvec = static_cast<float*>(workspace);
+  ws->dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)B * H * N * sizeof(float)));
+  return S2ATTN_OK;
+}
+
+// Dispatch a launcher template over (dtype, d).
+template <template <typename, int> class L, typename... A>
+hipError_t dispatch(int dtype, int d, A... a) {
+  if (dtype == S2ATTN_BF16) return d == 64 ? L<s2a::bf16, 64>::run(a...) : L<s2a::bf16, 128>::run(a...);
+  return d == 64 ? L<float, 64>::run(a...) : L<float, 128>::run(a...);
+}
+
+template <typename T, int D>
+struct Prep {
+  static hipError_t run(const void* o, const void* dO, Workspace ws, int B, int H, int N, hipStream_t s) {
+    return s2a::launch_bwd_prep<T, D>(o, dO, ws.dvec, ws.dq_acc, B, H, N, s);
+  }
+};
+template <typename T, int D>
+struct Main {
+  static hipError_t run(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dk,
+                        void* dv, Workspace ws, int B, int H, int Hkv, int N, int G, int S, hipStream_t s) {
+    return s2a::launch_bwd_main<T, D>(q, k, v, lse, dO, dk, dv, ws.dvec, ws.dq_acc, B, H, Hkv, N, G, S, s);
+  }
+};
+template <typename T, int D>
+struct Finish {
+  static hipError_t run(void* dq, Workspace ws, int B, int H, int N, hipStream_t s) {
+    return s2a::launch_bwd_finish<T, D>(dq, ws.dq_acc, B, H, N, s);
+  }
+};
+
+int status_of(hipError_t e) { return e == hipSuccess ? S2ATTN_OK : S2ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int s2attn_bwd_prep(const void* o, const void* dO, void* workspace, size_t workspace_bytes,
+                    int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  if (!o || !dO) return S2ATTN_ERR_NULL;
+  int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st != S2ATTN_OK) return st;
+  Workspace ws;
+  st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
+  if (st != S2ATTN_OK) return st;
+  return status_of(dispatch<Prep>(dtype, d, o, dO, ws, B, H, N, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int s2attn_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                    void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                    int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  if (!q || !k || !v || !lse || !dO || !dk || !dv) return S2ATTN_ERR_NULL;
+  int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st != S2ATTN_OK) return st;
+  Workspace ws;
+  st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
+  if (st != S2ATTN_OK) return st;
+  return status_of(dispatch<Main>(dtype, d, q, k, v, lse, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads,
+                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+int s2attn_bwd_finish(void* dq, void* workspace, size_t workspace_bytes,
+                      int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  if (!dq) return S2ATTN_ERR_NULL;
+  int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st != S2ATTN_OK) return st;
+  Workspace ws;
+  st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
+  if (st != S2ATTN_OK) return st;
+  return status_of(dispatch<Finish>(dtype, d, dq, ws, B, H, N, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
                void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
-  const int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (st != S2ATTN_OK) return st;
-  const size_t need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype);
-  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
-    return S2ATTN_ERR_WORKSPACE;
-  float* dvec = static_cast<float*>(workspace);
-  float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           align256((size_t)B * H * N * sizeof(float)));
+  Workspace ws;
+  st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
+  if (st != S2ATTN_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (dtype == S2ATTN_BF16) {
-    e = d == 64 ? s2a::launch_bwd<s2a::bf16, 64>(q, k, v, o, lse, dO, dq, dk, dv, dvec, dq_acc, B, H, Hkv, N, G,
-                                                   shift_heads, s)
-                : s2a::launch_bwd<s2a::bf16, 128>(q, k, v, o, lse, dO, dq, dk, dv, dvec, dq_acc, B, H, Hkv, N, G,
-                                                    shift_heads, s);
-  } else {
-    e = d == 64 ? s2a::launch_bwd<float, 64>(q, k, v, o, lse, dO, dq, dk, dv, dvec, dq_acc, B, H, Hkv, N, G,
-                                             shift_heads, s)
-                : s2a::launch_bwd<float, 128>(q, k, v, o, lse, dO, dq, dk, dv, dvec, dq_acc, B, H, Hkv, N, G,
-                                              shift_heads, s);
-  }
-  return e == hipSuccess ? S2ATTN_OK : S2ATTN_ERR_HIP;
+  hipError_t e = dispatch<Prep>(dtype, d, o, dO, ws, B, H, N, s);
+  if (e == hipSuccess) e = dispatch<Main>(dtype, d, q, k, v, lse, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads, s);
+  if (e == hipSuccess) e = dispatch<Finish>(dtype, d, dq, ws, B, H, N, s);
+  return status_of(e);
 }
 
 const char* s2attn_status_str(int status) {

@@ -317,43 +317,49 @@ __global__ __launch_bounds__(256) void s2attn_bwd_main(
 }
 
 template <typename T, int D>
-size_t bwd_lds_bytes() { return BwdShape<T, D>::kLdsBytes; }
-
-template <typename T, int D>
-hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                      const void* dO, void* dq, void* dk, void* dv, float* dvec, float* dq_acc,
-                      int B, int H, int Hkv, int N, int G, int shift_heads, hipStream_t stream) {
-  using S = BwdShape<T, D>;
-  const float scale = 1.0f / sqrtf((float)D);
+hipError_t launch_bwd_prep(const void* o, const void* dO, float* dvec, float* dq_acc,
+                           int B, int H, int N, hipStream_t stream) {
   const long long rows = (long long)B * N * H;
   constexpr int rpb = 256 / (D / 8);
   hipLaunchKernelGGL((s2attn_bwd_pre<T, D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream,
                      (const T*)o, (const T*)dO, dvec, dq_acc, N, H, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                           void* dk, void* dv, const float* dvec, float* dq_acc,
+                           int B, int H, int Hkv, int N, int G, int shift_heads, hipStream_t stream) {
+  using S = BwdShape<T, D>;
+  const float scale = 1.0f / sqrtf((float)D);
   static bool attr_set = false;   // raising the LDS limit is idempotent; a race only repeats it
   if (!attr_set) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&s2attn_bwd_main<T, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&s2attn_bwd_main<T, D>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   hipLaunchKernelGGL((s2attn_bwd_main<T, D>), dim3(N / S::kBKV, Hkv, B), dim3(256), S::kLdsBytes, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse, (const float*)dvec,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse, dvec,
                      dq_acc, (T*)dk, (T*)dv, N, H, Hkv, G, shift_heads, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long long n8 = rows * D / 8;
-  hipLaunchKernelGGL((s2attn_bwd_cvt<T>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                     (const float*)dq_acc, (T*)dq, n8);
   return hipGetLastError();
 }
 
-#define S2A_INST_BWD(T, D)                                                                          \
-  template hipError_t launch_bwd<T, D>(const void*, const void*, const void*, const void*,         \
-                                       const float*, const void*, void*, void*, void*, float*,     \
-                                       float*, int, int, int, int, int, int, hipStream_t);          \
-  template size_t bwd_lds_bytes<T, D>();
+template <typename T, int D>
+hipError_t launch_bwd_finish(void* dq, const float* dq_acc, int B, int H, int N, hipStream_t stream) {
+  const long long n8 = (long long)B * N * H * D / 8;
+  hipLaunchKernelGGL((s2attn_bwd_cvt<T>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                     dq_acc, (T*)dq, n8);
+  return hipGetLastError();
+}
+
+#define S2A_INST_BWD(T, D)                                                                               \
+  template hipError_t launch_bwd_prep<T, D>(const void*, const void*, float*, float*, int, int, int,    \
+                                            hipStream_t);                                              \
+  template hipError_t launch_bwd_main<T, D>(const void*, const void*, const void*, const float*,        \
+                                            const void*, void*, void*, const float*, float*, int, int,  \
+                                            int, int, int, int, hipStream_t);                           \
+  template hipError_t launch_bwd_finish<T, D>(void*, const float*, int, int, int, hipStream_t);
 S2A_INST_BWD(bf16, 64)
 S2A_INST_BWD(bf16, 128)
 S2A_INST_BWD(float, 64)
