@@ -207,11 +207,251 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
   if (hf == 0) lse[((size_t)b * H + h) * N + tq] = m_run * scale + logf(l_tot);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 forward for groups holding a whole number of 256-row query tiles.
+//
+// 8 waves (two per SIMD, so one wave's matrix-core work overlaps another's
+// softmax) share each 64-row key/value tile; each wave owns 32 query rows.
+// Key and value tiles go from HBM straight into LDS (global_load_lds, no
+// register staging), double-buffered with one barrier per tile; a 64-row tile
+// never straddles the roll's wrap point, so its base row is one scalar.
+// V stays row-major in LDS: the V^T operand is read with ds_read_b64_tr_b16,
+// whose 16-lane groups return 4 consecutive keys of one head-dim column.
+// The running max is only raised when a tile exceeds it by more than 2^8 (in
+// exp2 units), so the accumulator is rarely rescaled; P stays <= 256.
+// Row sums are taken on the bf16 P actually fed to the matrix cores.
+// ---------------------------------------------------------------------------
+template <int D>
+struct FwdB16Shape {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 512;
+  static constexpr int kBR = 256;
+  static constexpr int kBC = 64;
+  static constexpr int kCPR = D / 8;                      // 16-byte chunks per tile row
+  static constexpr int kTileChunks = kBC * kCPR;
+  static constexpr int kLoads = kTileChunks / kThreads;   // chunks per thread per tensor
+  static constexpr int kDC = D / 16;
+  static constexpr int kDT = D / 32;
+};
+
+// XOR swizzles of the 16-byte chunk column.  K: the 16 rows perm32(0..15) read
+// together by an A-operand load get distinct columns.  V: the 4 rows read by
+// one 16-lane transpose read (4 consecutive keys) get disjoint column pairs.
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row) {
+  return CPR == 16 ? ((row & 3) | ((row >> 1) & 4) | ((row << 1) & 8)) : ((row & 3) | ((row >> 1) & 4));
+}
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row) {
+  return CPR == 16 ? ((4 * (row & 3)) ^ (2 * ((row >> 1) & 1))) : (2 * (row & 3));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes from global memory straight into LDS: lane i of the wave fills
+// bytes [16 i, 16 i + 16) after the wave-uniform LDS base.
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+__device__ __forceinline__ float dot2_bf16_acc(bf16 a, bf16 b, float acc) {
+  const bf16x2_t pr = {a, b};
+  const bf16x2_t ones = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+}
+
+__device__ __forceinline__ bf16x8 tr_read8(const bf16* p0, const bf16* p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p1));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    bf16* __restrict__ o, float* __restrict__ lse,
+    int N, int H, int Hkv, int G, int shift_heads, float scale) {
+  using S = FwdB16Shape<D>;
+  constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTileChunks;
+  __shared__ bf16x8 smem[2 * 2 * TC];             // [stage][K, V][chunk]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int groups = N / G, tiles_per_group = G / BR;
+  const int x = blockIdx.x;
+  const int pos = tiles_per_group - 1 - x / groups;   // heaviest query tiles first
+  const int grp = x % groups;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int c = h / (H / Hkv);
+  const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
+  const int j0 = grp * G + pos * BR;
+  const int kv_begin = grp * G;
+  const int ntiles = (j0 + BR - kv_begin) / BC;
+
+  const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
+  const bf16* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
+  const bf16* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
+
+  // Q operand in registers
+  const int jw = j0 + wave * 32;
+  const int jq = jw + l32;
+  const int tq = orig_row(jq, sigma, N);
+  bf16x8 qf[S::kDC];
+  {
+    const bf16* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+#pragma unroll
+    for (int cc = 0; cc < S::kDC; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(qrow + cc * 16 + hf * 8);
+  }
+
+  // per-lane global offsets (elements) of the chunks this lane moves into LDS
+  int koff[S::kLoads], voff[S::kLoads];
+#pragma unroll
+  for (int i = 0; i < S::kLoads; ++i) {
+    const int p = (wave + S::kWaves * i) * 64 + lane;
+    const int row = p / CPR, pc = p % CPR;
+    koff[i] = row * (int)kvstride + (pc ^ swz_k<CPR>(row)) * 8;
+    voff[i] = row * (int)kvstride + (pc ^ swz_v<CPR>(row)) * 8;
+  }
+  auto issue_tile = [&](int kt0, int stage) {
+    const size_t t0 = (size_t)orig_row(kt0, sigma, N) * kvstride;   // whole tile is contiguous
+    bf16x8* ks = smem + (2 * stage) * TC;
+    bf16x8* vs = ks + TC;
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) {
+      const int cbase = (wave + S::kWaves * i) * 64;
+      load_lds16(kb + t0 + koff[i], ks + cbase);
+      load_lds16(vb + t0 + voff[i], vs + cbase);
+    }
+  };
+
+  // per-lane LDS element offsets of the K A-operand and V^T transpose reads
+  const int krow0 = perm32(l32);
+  const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
+
+  f32x16 oacc[S::kDT];
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = scale * kLog2e;
+
+  issue_tile(kv_begin, 0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt0 = kv_begin + it * BC;
+    wait_vmem_all();                             // this lane's tile loads have landed
+    __syncthreads();                             // ... and everyone's; the other stage is free
+    if (it + 1 < ntiles) issue_tile(kt0 + BC, (it + 1) & 1);
+    if (kt0 > jw + 31) continue;                 // tile entirely after this wave's queries
+
+    const bf16* Ks = reinterpret_cast<const bf16*>(smem + (2 * (it & 1)) * TC);
+    const bf16* Vs = Ks + TC * 8;
+
+    // S^T = K Q^T
+    f32x16 s[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[ks][r] = 0.f;
+      const int row = ks * 32 + krow0;
+      const int sw = swz_k<CPR>(row);
+#pragma unroll
+      for (int cc = 0; cc < S::kDC; ++cc) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (row * CPR + ((2 * cc + hf) ^ sw)) * 8);
+        mma32(s[ks], a, qf[cc]);
+      }
+    }
+
+    // causal mask on the diagonal tile, running max with lazy rescale
+    if (kt0 + BC - 1 > jw) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + ks * 32 + (r >> 3) * 16 + hf * 8 + (r & 7);
+          if (key > jq) s[ks][r] = -INFINITY;
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[ks][r]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    if (wave_any((mloc - m_run) * c2 > 8.f)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = fast_exp2((m_run - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = -m_run * c2;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      f32x8 pv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(s[kc >> 1][(kc & 1) * 8 + i], c2, nm));
+      pf[kc] = __builtin_convertvector(pv, bf16x8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_run = dot2_bf16_acc(pf[kc][2 * i], pf[kc][2 * i + 1], l_run);
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int dt = 0; dt < S::kDT; ++dt) {
+        const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
+        const int r0 = kc * 16 + hf * 8 + ts;
+        const int r1 = r0 + 4;
+        const bf16* p0 = Vs + (r0 * CPR + ((dbase >> 3) ^ swz_v<CPR>(r0))) * 8 + (dbase & 7);
+        const bf16* p1 = Vs + (r1 * CPR + ((dbase >> 3) ^ swz_v<CPR>(r1))) * 8 + (dbase & 7);
+        mma32(oacc[dt], tr_read8(p0, p1), pf[kc]);
+      }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.f / l_tot;
+  bf16* orow = o + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<bf16x8*>(orow + dt * 32 + u * 16 + hf * 8) = scale8<bf16>(oacc[dt], u * 8, inv);
+  if (hf == 0) lse[((size_t)b * H + h) * N + tq] = m_run * scale + logf(l_tot);
+}
+
+template <int D>
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Hkv, int N, int G, int shift_heads, float scale, hipStream_t stream) {
+  dim3 grid(N / FwdB16Shape<D>::kBR, H, B);
+  hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D>), grid, dim3(FwdB16Shape<D>::kThreads), 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads, scale);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int Hkv, int N, int G, int shift_heads, hipStream_t stream) {
-  dim3 grid(N / FwdShape<T, D>::kBR, H, B);
   const float scale = 1.0f / sqrtf((float)D);
+  if constexpr (sizeof(T) == 2) {
+    if (G % FwdB16Shape<D>::kBR == 0)
+      return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, scale, stream);
+  }
+  dim3 grid(N / FwdShape<T, D>::kBR, H, B);
   hipLaunchKernelGGL((s2attn_fwd_kernel<T, D>), grid, dim3(256), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, scale);
   return hipGetLastError();

@@ -8,7 +8,10 @@ the first row of every group).
 
 Bars: bf16 inputs with fp32 accumulation: max |O - O*| <= 2e-2 and
 ||x - x*||_2 / ||x*||_2 <= 3e-2 for each of dQ, dK, dV; fp32 inputs: both
-metrics <= 1e-4.  lse is compared as a diagnostic (1e-3 bf16, 1e-4 fp32).
+metrics <= 1e-4.  lse is compared as a diagnostic: fp32 1e-4; bf16 2.5e-3,
+because the bf16 kernels normalise by the sum of the bf16-rounded P they feed to
+the matrix cores, and |sum bf16(p) - sum p| <= 2^-9 sum p bounds the lse
+deviation by ln(1 + 2^-9) ~ 1.95e-3 (largest on rows with few keys).
 """
 
 import numpy as np
@@ -21,7 +24,7 @@ from shifted_sparse_attention_s2attn_amd.inputs import WORKLOADS, make_inputs, s
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": dict(o=2e-2, grad=3e-2, lse=1e-3), "f32": dict(o=1e-4, grad=1e-4, lse=1e-4)}
+TOL = {"bf16": dict(o=2e-2, grad=3e-2, lse=2.5e-3), "f32": dict(o=1e-4, grad=1e-4, lse=1e-4)}
 
 
 def say(*a):
