@@ -145,7 +145,7 @@ def main():
         s2attn_fwd(q, k, v, w.G, w.shift_heads, out=o, lse=lse)
         if ev:
             ev[1].record(stream)
-        s2attn_bwd_prep(q, k, o, do, ws, w.G, w.shift_heads)
+        s2attn_bwd_prep(q, k, o, lse, do, ws, w.G, w.shift_heads)
         if ev:
             ev[2].record(stream)
         s2attn_bwd_main(q, k, v, lse, do, dk, dv, ws, w.G, w.shift_heads)

@@ -73,7 +73,8 @@ int s2attn_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace s2attn_bwd needs: the fp32 row sums
- * Dvec = rowsum(dO * o) [B,H,N] and an fp32 accumulator for dq [B,N,H,d].
+ * Dvec = rowsum(dO * o) [B,H,N], lse * log2(e) [B,H,N] and an fp32
+ * accumulator for dq [B,N,H,d].
  * Returns 0 when the arguments would be rejected by s2attn_bwd.
  */
 size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G,
@@ -97,17 +98,17 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * The backward as its three stages, in this order on one stream; s2attn_bwd
  * is exactly these three calls.  Same arguments, checks and workspace as
  * s2attn_bwd; the workspace must not be touched between the stages.
- *   prep  : Dvec[b,h,t] = sum_c dO[b,t,h,c] * o[b,t,h,c] (fp32) into the
- *           workspace, and clears the fp32 dq accumulator.
+ *   prep  : Dvec[b,h,t] = sum_c dO[b,t,h,c] * o[b,t,h,c] and lse * log2(e)
+ *           (fp32) into the workspace, and clears the fp32 dq accumulator.
  *   main  : dk and dv (written), dq accumulated into the workspace.  The
  *           backward of "The shifting mechanism" / Algorithm 1 (page section
  *           3.4): P = exp(scale q k^T - lse) causal within each group of the
  *           rolled frame, dv = P^T dO, dS = P * (dO v^T - Dvec),
- *           dk = scale dS^T q, dq += scale dS k.
- *   finish: dq = accumulator rounded to the tensor type.
+ *           dk = scale dS^T q, dq_acc += dS k.
+ *   finish: dq = scale * dq_acc rounded to the tensor type.
  * Useful to callers that schedule the stages themselves (and to time them).
  */
-int s2attn_bwd_prep(const void* o, const void* dO, void* workspace, size_t workspace_bytes,
+int s2attn_bwd_prep(const void* o, const float* lse, const void* dO, void* workspace, size_t workspace_bytes,
                     int B, int H, int Hkv, int N, int d, int G, int shift_heads,
                     int dtype, void* stream);
 int s2attn_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dO,

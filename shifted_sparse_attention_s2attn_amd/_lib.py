@@ -43,7 +43,7 @@ def load():
     lib.s2attn_bwd_workspace_bytes.restype = sz
     lib.s2attn_bwd.argtypes = [vp, vp, vp, vp, fp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, vp]
     lib.s2attn_bwd.restype = i
-    lib.s2attn_bwd_prep.argtypes = [vp, vp, vp, sz, i, i, i, i, i, i, i, i, vp]
+    lib.s2attn_bwd_prep.argtypes = [vp, fp, vp, vp, sz, i, i, i, i, i, i, i, i, vp]
     lib.s2attn_bwd_prep.restype = i
     lib.s2attn_bwd_main.argtypes = [vp, vp, vp, fp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, vp]
     lib.s2attn_bwd_main.restype = i

@@ -114,11 +114,11 @@ def _check(st, where):
         raise S2AttnError(st, where)
 
 
-def s2attn_bwd_prep(q, k, o, do, workspace, G, shift_heads=None, stream=None):
-    """Stage 1 of the backward: Dvec = rowsum(dO * o) and the dq accumulator cleared."""
+def s2attn_bwd_prep(q, k, o, lse, do, workspace, G, shift_heads=None, stream=None):
+    """Stage 1 of the backward: Dvec = rowsum(dO * o), lse * log2(e), dq accumulator cleared."""
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
-        _check(_lib.load().s2attn_bwd_prep(_ptr(o), _ptr(do), _ptr(workspace), workspace.numel(),
+        _check(_lib.load().s2attn_bwd_prep(_ptr(o), _fptr(lse), _ptr(do), _ptr(workspace), workspace.numel(),
                                            B, H, Hkv, N, d, G, S, _dtype_code(q), _stream(stream)),
                "s2attn_bwd_prep")
 

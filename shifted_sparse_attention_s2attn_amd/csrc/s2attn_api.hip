@@ -2,7 +2,7 @@
 // Every check runs on the host before any HIP call, so a rejected call
 // launches nothing.  The library keeps no state besides one flag per backward
 // kernel instantiation recording that its LDS limit was raised.
-#include "../../include/s2attn.h"
+#include "s2attn.h"
 #include "s2attn_common.h"
 
 namespace s2a {
@@ -10,10 +10,11 @@ template <typename T, int D>
 hipError_t launch_fwd(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
                       hipStream_t);
 template <typename T, int D>
-hipError_t launch_bwd_prep(const void*, const void*, float*, float*, int, int, int, hipStream_t);
+hipError_t launch_bwd_prep(const void*, const void*, const float*, float*, float*, float*, int, int, int,
+                           hipStream_t);
 template <typename T, int D>
-hipError_t launch_bwd_main(const void*, const void*, const void*, const float*, const void*, void*, void*,
-                           const float*, float*, int, int, int, int, int, int, hipStream_t);
+hipError_t launch_bwd_main(const void*, const void*, const void*, const float*, const float*, const void*,
+                           void*, void*, const float*, float*, int, int, int, int, int, int, hipStream_t);
 template <typename T, int D>
 hipError_t launch_bwd_finish(void*, const float*, int, int, int, hipStream_t);
 }  // namespace s2a
@@ -65,15 +66,17 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype) {
   if (check_problem(B, H, Hkv, N, d, G, shift_heads, dtype) != S2ATTN_OK) return 0;
   const size_t rows = (size_t)B * H * N;
-  return align256(rows * sizeof(float)) + align256(rows * (size_t)d * sizeof(float));
+  return 2 * align256(rows * sizeof(float)) + align256(rows * (size_t)d * sizeof(float));
 }
 
 }  // extern "C"
 
 namespace {
 
+// Workspace: Dvec [B,H,N] | lse*log2(e) [B,H,N] | dq accumulator [B,N,H,d], fp32.
 struct Workspace {
   float* dvec;
+  float* lse2;
   float* dq_acc;
 };
 
@@ -82,8 +85,10 @@ int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int H
   const size_t need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return S2ATTN_ERR_WORKSPACE;
+  const size_t vec = align256((size_t)B * H * N * sizeof(float));
   ws->dvec = static_cast<float*>(workspace);
-  ws->dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)B * H * N * sizeof(float)));
+  ws->lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + vec);
+  ws->dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * vec);
   return S2ATTN_OK;
 }
 
@@ -96,15 +101,17 @@ hipError_t dispatch(int dtype, int d, A... a) {
 
 template <typename T, int D>
 struct Prep {
-  static hipError_t run(const void* o, const void* dO, Workspace ws, int B, int H, int N, hipStream_t s) {
-    return s2a::launch_bwd_prep<T, D>(o, dO, ws.dvec, ws.dq_acc, B, H, N, s);
+  static hipError_t run(const void* o, const void* dO, const float* lse, Workspace ws, int B, int H, int N,
+                        hipStream_t s) {
+    return s2a::launch_bwd_prep<T, D>(o, dO, lse, ws.dvec, ws.lse2, ws.dq_acc, B, H, N, s);
   }
 };
 template <typename T, int D>
 struct Main {
   static hipError_t run(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dk,
                         void* dv, Workspace ws, int B, int H, int Hkv, int N, int G, int S, hipStream_t s) {
-    return s2a::launch_bwd_main<T, D>(q, k, v, lse, dO, dk, dv, ws.dvec, ws.dq_acc, B, H, Hkv, N, G, S, s);
+    return s2a::launch_bwd_main<T, D>(q, k, v, lse, ws.lse2, dO, dk, dv, ws.dvec, ws.dq_acc, B, H, Hkv, N, G, S,
+                                      s);
   }
 };
 template <typename T, int D>
@@ -120,15 +127,15 @@ int status_of(hipError_t e) { return e == hipSuccess ? S2ATTN_OK : S2ATTN_ERR_HI
 
 extern "C" {
 
-int s2attn_bwd_prep(const void* o, const void* dO, void* workspace, size_t workspace_bytes,
+int s2attn_bwd_prep(const void* o, const float* lse, const void* dO, void* workspace, size_t workspace_bytes,
                     int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
-  if (!o || !dO) return S2ATTN_ERR_NULL;
+  if (!o || !lse || !dO) return S2ATTN_ERR_NULL;
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (st != S2ATTN_OK) return st;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
-  return status_of(dispatch<Prep>(dtype, d, o, dO, ws, B, H, N, reinterpret_cast<hipStream_t>(stream)));
+  return status_of(dispatch<Prep>(dtype, d, o, dO, lse, ws, B, H, N, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int s2attn_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dO,
@@ -165,7 +172,7 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = dispatch<Prep>(dtype, d, o, dO, ws, B, H, N, s);
+  hipError_t e = dispatch<Prep>(dtype, d, o, dO, lse, ws, B, H, N, s);
   if (e == hipSuccess) e = dispatch<Main>(dtype, d, q, k, v, lse, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads, s);
   if (e == hipSuccess) e = dispatch<Finish>(dtype, d, dq, ws, B, H, N, s);
   return status_of(e);

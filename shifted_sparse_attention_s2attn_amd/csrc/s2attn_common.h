@@ -100,4 +100,52 @@ __device__ __forceinline__ int orig_row(int j, int sigma, int N) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Global memory straight into LDS (no registers): lane i of the wave fills
+// bytes [n i, n i + n) after the wave-uniform LDS base, n = 16 or 4.
+// (amdgcn builtins sit in helpers like these, not in kernel bodies, so that
+// the host pass still emits every kernel's launch stub.)
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// Raw buffer resource over [base, base + nbytes) and an fp32 atomic add into it
+// at byte offset voff (per lane) + soff (wave-uniform, kept in a scalar
+// register).  Offsets past nbytes are dropped by the hardware range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
+}
+__device__ __forceinline__ void buffer_atomic_add(float x, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(x, r, voff, soff, 0);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+__device__ __forceinline__ float dot2_bf16_acc(bf16 a, bf16 b, float acc) {
+  const bf16x2_t pr = {a, b};
+  const bf16x2_t ones = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// lane i receives element (i & 3) of the 8-byte pieces addressed by lanes
+// 4s + (i >> 2), s = 0..3, in that order.  If lane 4s + m addresses row r0 + s
+// at column c(m), lane i therefore gets rows r0..r0+3 of column c(i >> 2) + (i & 3):
+// four consecutive k-values of one operand row, from a tile stored k-major.
+// tr_read8 joins two such reads (rows r0..r0+3 and r0+4..r0+7).
+__device__ __forceinline__ bf16x8 tr_read8(const bf16* p0, const bf16* p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p1));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+
 }  // namespace s2a

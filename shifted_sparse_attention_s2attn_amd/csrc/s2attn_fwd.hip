@@ -246,32 +246,6 @@ __device__ __forceinline__ int swz_v(int row) {
   return CPR == 16 ? ((4 * (row & 3)) ^ (2 * ((row >> 1) & 1))) : (2 * (row & 3));
 }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// 16 bytes from global memory straight into LDS: lane i of the wave fills
-// bytes [16 i, 16 i + 16) after the wave-uniform LDS base.
-__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-
-__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
-
-__device__ __forceinline__ float dot2_bf16_acc(bf16 a, bf16 b, float acc) {
-  const bf16x2_t pr = {a, b};
-  const bf16x2_t ones = {(bf16)1.0f, (bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
-}
-
-__device__ __forceinline__ bf16x8 tr_read8(const bf16* p0, const bf16* p1) {
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p1));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  const i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, c);
-}
-
 template <int D>
 __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
