@@ -121,7 +121,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from shifted_sparse_attention_s2attn_amd import (s2attn_bwd_finish, s2attn_bwd_main, s2attn_bwd_prep,
+    from shifted_sparse_attention_s2attn_amd import (s2attn_bwd_dkdv, s2attn_bwd_dq, s2attn_bwd_prep,
                                                      s2attn_bwd_workspace_bytes, s2attn_fwd)
     from shifted_sparse_attention_s2attn_amd import flops as F
     from shifted_sparse_attention_s2attn_amd.inputs import WORKLOADS, make_inputs
@@ -137,7 +137,7 @@ def main():
     ws = torch.empty(s2attn_bwd_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.G, w.shift_heads, q.dtype),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    names = ["s2attn_fwd_kernel", "s2attn_bwd_pre", "s2attn_bwd_main", "s2attn_bwd_cvt"]
+    names = ["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
 
     def step(ev=None):
         if ev:
@@ -148,10 +148,10 @@ def main():
         s2attn_bwd_prep(q, k, o, lse, do, ws, w.G, w.shift_heads)
         if ev:
             ev[2].record(stream)
-        s2attn_bwd_main(q, k, v, lse, do, dk, dv, ws, w.G, w.shift_heads)
+        s2attn_bwd_dkdv(q, k, v, do, dk, dv, ws, w.G, w.shift_heads)
         if ev:
             ev[3].record(stream)
-        s2attn_bwd_finish(q, k, dq, ws, w.G, w.shift_heads)
+        s2attn_bwd_dq(q, k, v, do, dq, ws, w.G, w.shift_heads)
         if ev:
             ev[4].record(stream)
 
@@ -171,7 +171,11 @@ def main():
     bwd_f = F.bwd_flops(w.B, w.H, w.N, w.G, w.d)
     peak = F.MI355X_BF16_PEAK_TFLOPS if w.dtype == "bf16" else F.MI355X_F32_PEAK_TFLOPS
     elt = 2 if w.dtype == "bf16" else 4
-    kern_flops = {"s2attn_fwd_kernel": fwd_f, "s2attn_bwd_main": bwd_f}
+    # algorithmic FLOP per launch: the backward's five contractions are S, dP, dV, dK
+    # (the dK/dV kernel, 8d per pair) and dQ (the dQ kernel, 2d per pair; that kernel
+    # also recomputes S and dP, which are not counted again)
+    pairs = F.allowed_pairs(w.B, w.H, w.N, w.G)
+    kern_flops = {"fwd": fwd_f, "bwd_dkdv": 8 * w.d * pairs, "bwd_dq": 2 * w.d * pairs}
     dominant = max(kern_ms, key=kern_ms.get)
     kernels = {}
     for n, ms in kern_ms.items():
@@ -179,16 +183,15 @@ def main():
         if n in kern_flops:
             kernels[n]["tflops"] = round(kern_flops[n] / ms / 1e9, 1)
             kernels[n]["frac_of_peak"] = round(kern_flops[n] / ms / 1e9 / peak, 4)
-    fwd_ms = kern_ms["s2attn_fwd_kernel"]
-    bwd_ms = kern_ms["s2attn_bwd_pre"] + kern_ms["s2attn_bwd_main"] + kern_ms["s2attn_bwd_cvt"]
+    kernels["bwd_dq"]["executed_tflops"] = round(6 * w.d * pairs / kern_ms["bwd_dq"] / 1e9, 1)
+    fwd_ms = kern_ms["fwd"]
+    bwd_ms = kern_ms["bwd_prep"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
     if dominant in kern_flops:
         achieved = kern_flops[dominant] / kern_ms[dominant] / 1e9
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
     else:
-        nbytes = {"s2attn_bwd_pre": 2 * elt * w.B * w.N * w.H * w.d + 4 * w.B * w.H * w.N
-                  + 4 * w.B * w.N * w.H * w.d,
-                  "s2attn_bwd_cvt": (4 + elt) * w.B * w.N * w.H * w.d}[dominant]
+        nbytes = 2 * elt * w.B * w.N * w.H * w.d + 12 * w.B * w.H * w.N   # bwd_prep
         achieved = nbytes / kern_ms[dominant] / 1e6
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": F.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / F.MI355X_HBM_PEAK_GBS, 4)}

@@ -73,8 +73,7 @@ int s2attn_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace s2attn_bwd needs: the fp32 row sums
- * Dvec = rowsum(dO * o) [B,H,N], lse * log2(e) [B,H,N] and an fp32
- * accumulator for dq [B,N,H,d].
+ * Dvec = rowsum(dO * o) [B,H,N] and lse * log2(e) [B,H,N].
  * Returns 0 when the arguments would be rejected by s2attn_bwd.
  */
 size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G,
@@ -85,7 +84,7 @@ size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G,
  * Needs the forward's own o and lse.  `workspace` is caller-owned device
  * memory of at least s2attn_bwd_workspace_bytes() bytes, 256-byte aligned; its
  * contents on entry do not matter and are clobbered.  Concurrent calls must
- * use distinct workspaces.
+ * use distinct workspaces.  No atomics: results are bitwise repeatable.
  */
 int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
                const float* lse, const void* dO,
@@ -95,29 +94,29 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
                int dtype, void* stream);
 
 /*
- * The backward as its three stages, in this order on one stream; s2attn_bwd
- * is exactly these three calls.  Same arguments, checks and workspace as
- * s2attn_bwd; the workspace must not be touched between the stages.
- *   prep  : Dvec[b,h,t] = sum_c dO[b,t,h,c] * o[b,t,h,c] and lse * log2(e)
- *           (fp32) into the workspace, and clears the fp32 dq accumulator.
- *   main  : dk and dv (written), dq accumulated into the workspace.  The
- *           backward of "The shifting mechanism" / Algorithm 1 (page section
- *           3.4): P = exp(scale q k^T - lse) causal within each group of the
- *           rolled frame, dv = P^T dO, dS = P * (dO v^T - Dvec),
- *           dk = scale dS^T q, dq_acc += dS k.
- *   finish: dq = scale * dq_acc rounded to the tensor type.
- * Useful to callers that schedule the stages themselves (and to time them).
+ * The backward as its three stages; s2attn_bwd is exactly prep, dkdv, dq in
+ * this order on one stream.  Same checks and workspace as s2attn_bwd; dkdv
+ * and dq both read what prep wrote and may run in either order after it.
+ * The gradients are those of the causal softmax attention of "The shifting
+ * mechanism" / Algorithm 1 (page section 3.4) in every group of every head's
+ * rolled frame: P = exp(scale q k^T - lse), dS = P * (dO v^T - Dvec),
+ *   prep : Dvec[b,h,t] = sum_c dO[b,t,h,c] * o[b,t,h,c] and lse * log2(e)
+ *          (fp32) into the workspace;
+ *   dkdv : dv = P^T dO and dk = scale dS^T q, summed over the query heads
+ *          that share a key/value head;
+ *   dq   : dq = scale dS k (recomputes P and dS per query tile).
  */
 int s2attn_bwd_prep(const void* o, const float* lse, const void* dO, void* workspace, size_t workspace_bytes,
                     int B, int H, int Hkv, int N, int d, int G, int shift_heads,
                     int dtype, void* stream);
-int s2attn_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
                     void* dk, void* dv, void* workspace, size_t workspace_bytes,
                     int B, int H, int Hkv, int N, int d, int G, int shift_heads,
                     int dtype, void* stream);
-int s2attn_bwd_finish(void* dq, void* workspace, size_t workspace_bytes,
-                      int B, int H, int Hkv, int N, int d, int G, int shift_heads,
-                      int dtype, void* stream);
+int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                  void* dq, void* workspace, size_t workspace_bytes,
+                  int B, int H, int Hkv, int N, int d, int G, int shift_heads,
+                  int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* s2attn_status_str(int status);

@@ -19,8 +19,8 @@ S2ATTN_ERR_WORKSPACE = 5
 S2ATTN_BF16 = 0
 S2ATTN_F32 = 1
 
-EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes", "s2attn_bwd_prep", "s2attn_bwd_main",
-           "s2attn_bwd_finish", "s2attn_status_str")
+EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes", "s2attn_bwd_prep", "s2attn_bwd_dkdv",
+           "s2attn_bwd_dq", "s2attn_status_str")
 
 _lib = None
 
@@ -45,10 +45,10 @@ def load():
     lib.s2attn_bwd.restype = i
     lib.s2attn_bwd_prep.argtypes = [vp, fp, vp, vp, sz, i, i, i, i, i, i, i, i, vp]
     lib.s2attn_bwd_prep.restype = i
-    lib.s2attn_bwd_main.argtypes = [vp, vp, vp, fp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, vp]
-    lib.s2attn_bwd_main.restype = i
-    lib.s2attn_bwd_finish.argtypes = [vp, vp, sz, i, i, i, i, i, i, i, i, vp]
-    lib.s2attn_bwd_finish.restype = i
+    lib.s2attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, vp]
+    lib.s2attn_bwd_dkdv.restype = i
+    lib.s2attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, vp]
+    lib.s2attn_bwd_dq.restype = i
     lib.s2attn_status_str.argtypes = [i]
     lib.s2attn_status_str.restype = ctypes.c_char_p
     _lib = lib

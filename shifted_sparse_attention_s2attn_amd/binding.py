@@ -12,7 +12,7 @@ import torch
 from . import _lib
 
 __all__ = ["S2AttnError", "s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes",
-           "s2attn_bwd_prep", "s2attn_bwd_main", "s2attn_bwd_finish",
+           "s2attn_bwd_prep", "s2attn_bwd_dkdv", "s2attn_bwd_dq",
            "s2attn_status_str", "S2Attn", "s2attn"]
 
 
@@ -115,7 +115,7 @@ def _check(st, where):
 
 
 def s2attn_bwd_prep(q, k, o, lse, do, workspace, G, shift_heads=None, stream=None):
-    """Stage 1 of the backward: Dvec = rowsum(dO * o), lse * log2(e), dq accumulator cleared."""
+    """Stage 1 of the backward: Dvec = rowsum(dO * o) and lse * log2(e) into the workspace."""
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
         _check(_lib.load().s2attn_bwd_prep(_ptr(o), _fptr(lse), _ptr(do), _ptr(workspace), workspace.numel(),
@@ -123,23 +123,24 @@ def s2attn_bwd_prep(q, k, o, lse, do, workspace, G, shift_heads=None, stream=Non
                "s2attn_bwd_prep")
 
 
-def s2attn_bwd_main(q, k, v, lse, do, dk, dv, workspace, G, shift_heads=None, stream=None):
-    """Stage 2 of the backward: dk, dv written; dq accumulated in the workspace."""
+def s2attn_bwd_dkdv(q, k, v, do, dk, dv, workspace, G, shift_heads=None, stream=None):
+    """Stage 2 of the backward: dk, dv (needs prep's workspace)."""
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
-        _check(_lib.load().s2attn_bwd_main(_ptr(q), _ptr(k), _ptr(v), _fptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
+        _check(_lib.load().s2attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
                                            _ptr(workspace), workspace.numel(),
                                            B, H, Hkv, N, d, G, S, _dtype_code(q), _stream(stream)),
-               "s2attn_bwd_main")
+               "s2attn_bwd_dkdv")
 
 
-def s2attn_bwd_finish(q, k, dq, workspace, G, shift_heads=None, stream=None):
-    """Stage 3 of the backward: dq from the fp32 accumulator."""
+def s2attn_bwd_dq(q, k, v, do, dq, workspace, G, shift_heads=None, stream=None):
+    """Stage 3 of the backward: dq (needs prep's workspace)."""
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
-        _check(_lib.load().s2attn_bwd_finish(_ptr(dq), _ptr(workspace), workspace.numel(),
-                                             B, H, Hkv, N, d, G, S, _dtype_code(q), _stream(stream)),
-               "s2attn_bwd_finish")
+        _check(_lib.load().s2attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
+                                         _ptr(workspace), workspace.numel(),
+                                         B, H, Hkv, N, d, G, S, _dtype_code(q), _stream(stream)),
+               "s2attn_bwd_dq")
 
 
 class S2Attn(torch.autograd.Function):

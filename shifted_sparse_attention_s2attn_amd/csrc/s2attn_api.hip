@@ -1,7 +1,7 @@
 // C ABI of libs2attn: host-side validation, workspace sizing and launch.
 // Every check runs on the host before any HIP call, so a rejected call
-// launches nothing.  The library keeps no state besides one flag per backward
-// kernel instantiation recording that its LDS limit was raised.
+// launches nothing.  The library keeps no state besides one flag per kernel
+// instantiation recording that its LDS limit was raised.
 #include "s2attn.h"
 #include "s2attn_common.h"
 
@@ -10,13 +10,13 @@ template <typename T, int D>
 hipError_t launch_fwd(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
                       hipStream_t);
 template <typename T, int D>
-hipError_t launch_bwd_prep(const void*, const void*, const float*, float*, float*, float*, int, int, int,
-                           hipStream_t);
+hipError_t launch_bwd_prep(const void*, const void*, const float*, float*, float*, int, int, int, hipStream_t);
 template <typename T, int D>
-hipError_t launch_bwd_main(const void*, const void*, const void*, const float*, const float*, const void*,
-                           void*, void*, const float*, float*, int, int, int, int, int, int, hipStream_t);
+hipError_t launch_bwd_dkdv(const void*, const void*, const void*, const void*, const float*, const float*, void*,
+                           void*, int, int, int, int, int, int, hipStream_t);
 template <typename T, int D>
-hipError_t launch_bwd_finish(void*, const float*, int, int, int, hipStream_t);
+hipError_t launch_bwd_dq(const void*, const void*, const void*, const void*, const float*, const float*, void*,
+                         int, int, int, int, int, int, hipStream_t);
 }  // namespace s2a
 
 namespace {
@@ -65,19 +65,17 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype) {
   if (check_problem(B, H, Hkv, N, d, G, shift_heads, dtype) != S2ATTN_OK) return 0;
-  const size_t rows = (size_t)B * H * N;
-  return 2 * align256(rows * sizeof(float)) + align256(rows * (size_t)d * sizeof(float));
+  return 2 * align256((size_t)B * H * N * sizeof(float));
 }
 
 }  // extern "C"
 
 namespace {
 
-// Workspace: Dvec [B,H,N] | lse*log2(e) [B,H,N] | dq accumulator [B,N,H,d], fp32.
+// Workspace: Dvec [B,H,N] | lse*log2(e) [B,H,N], fp32.
 struct Workspace {
   float* dvec;
   float* lse2;
-  float* dq_acc;
 };
 
 int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d, int G,
@@ -85,10 +83,8 @@ int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int H
   const size_t need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return S2ATTN_ERR_WORKSPACE;
-  const size_t vec = align256((size_t)B * H * N * sizeof(float));
   ws->dvec = static_cast<float*>(workspace);
-  ws->lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + vec);
-  ws->dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * vec);
+  ws->lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)B * H * N * sizeof(float)));
   return S2ATTN_OK;
 }
 
@@ -103,21 +99,21 @@ template <typename T, int D>
 struct Prep {
   static hipError_t run(const void* o, const void* dO, const float* lse, Workspace ws, int B, int H, int N,
                         hipStream_t s) {
-    return s2a::launch_bwd_prep<T, D>(o, dO, lse, ws.dvec, ws.lse2, ws.dq_acc, B, H, N, s);
+    return s2a::launch_bwd_prep<T, D>(o, dO, lse, ws.dvec, ws.lse2, B, H, N, s);
   }
 };
 template <typename T, int D>
-struct Main {
-  static hipError_t run(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dk,
-                        void* dv, Workspace ws, int B, int H, int Hkv, int N, int G, int S, hipStream_t s) {
-    return s2a::launch_bwd_main<T, D>(q, k, v, lse, ws.lse2, dO, dk, dv, ws.dvec, ws.dq_acc, B, H, Hkv, N, G, S,
-                                      s);
+struct Dkdv {
+  static hipError_t run(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
+                        Workspace ws, int B, int H, int Hkv, int N, int G, int S, hipStream_t s) {
+    return s2a::launch_bwd_dkdv<T, D>(q, k, v, dO, ws.lse2, ws.dvec, dk, dv, B, H, Hkv, N, G, S, s);
   }
 };
 template <typename T, int D>
-struct Finish {
-  static hipError_t run(void* dq, Workspace ws, int B, int H, int N, hipStream_t s) {
-    return s2a::launch_bwd_finish<T, D>(dq, ws.dq_acc, B, H, N, s);
+struct Dq {
+  static hipError_t run(const void* q, const void* k, const void* v, const void* dO, void* dq, Workspace ws,
+                        int B, int H, int Hkv, int N, int G, int S, hipStream_t s) {
+    return s2a::launch_bwd_dq<T, D>(q, k, v, dO, ws.lse2, ws.dvec, dq, B, H, Hkv, N, G, S, s);
   }
 };
 
@@ -138,28 +134,30 @@ int s2attn_bwd_prep(const void* o, const float* lse, const void* dO, void* works
   return status_of(dispatch<Prep>(dtype, d, o, dO, lse, ws, B, H, N, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int s2attn_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dO,
-                    void* dk, void* dv, void* workspace, size_t workspace_bytes,
+int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes,
                     int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
-  if (!q || !k || !v || !lse || !dO || !dk || !dv) return S2ATTN_ERR_NULL;
+  if (!q || !k || !v || !dO || !dk || !dv) return S2ATTN_ERR_NULL;
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (st != S2ATTN_OK) return st;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
-  return status_of(dispatch<Main>(dtype, d, q, k, v, lse, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads,
+  return status_of(dispatch<Dkdv>(dtype, d, q, k, v, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads,
                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
-int s2attn_bwd_finish(void* dq, void* workspace, size_t workspace_bytes,
-                      int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
-  if (!dq) return S2ATTN_ERR_NULL;
+int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  if (!q || !k || !v || !dO || !dq) return S2ATTN_ERR_NULL;
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (st != S2ATTN_OK) return st;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
-  return status_of(dispatch<Finish>(dtype, d, dq, ws, B, H, N, reinterpret_cast<hipStream_t>(stream)));
+  return status_of(dispatch<Dq>(dtype, d, q, k, v, dO, dq, ws, B, H, Hkv, N, G, shift_heads,
+                                reinterpret_cast<hipStream_t>(stream)));
 }
 
 int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
@@ -173,13 +171,12 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
   if (st != S2ATTN_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = dispatch<Prep>(dtype, d, o, dO, lse, ws, B, H, N, s);
-  if (e == hipSuccess) e = dispatch<Main>(dtype, d, q, k, v, lse, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads, s);
-  if (e == hipSuccess) e = dispatch<Finish>(dtype, d, dq, ws, B, H, N, s);
+  if (e == hipSuccess) e = dispatch<Dkdv>(dtype, d, q, k, v, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads, s);
+  if (e == hipSuccess) e = dispatch<Dq>(dtype, d, q, k, v, dO, dq, ws, B, H, Hkv, N, G, shift_heads, s);
   return status_of(e);
 }
 
-const char* s2attn_status_str(int status) {
-  switch (status) {
+const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_OK: return "ok";
     case S2ATTN_ERR_NULL: return "a required pointer is NULL";
     case S2ATTN_ERR_SHAPE: return "invalid shape (size <= 0, N % G != 0, odd G, shift_heads outside [0,H], or H % Hkv != 0)";

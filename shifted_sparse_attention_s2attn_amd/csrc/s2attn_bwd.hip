@@ -11,37 +11,34 @@
 //     dQ = scale * dS K,   dK = scale * dS^T Q
 // with dK, dV summed over the query heads that share a key/value head.
 //
-// Three kernels on one stream:
-//   1. s2attn_bwd_pre   : Dvec[b,h,t] = sum_d dO*O (fp32) and lse*log2(e), and
-//                         zeroes the fp32 dQ accumulator rows.
-//   2. s2attn_bwd_main  : one workgroup per 128 key rows of one (batch, KV
-//                         head).  Its K and V stay in registers (each wave owns
-//                         32 keys).  It walks every query head sharing the KV
-//                         head and, in that head's rolled frame, every 64-row
-//                         query tile of the group from the diagonal to the
-//                         group end.  Per tile: S and dP (keys on lanes), P and
-//                         dS, dV^T += dO^T P and dK^T += Q^T dS in registers,
-//                         dS through LDS, then dS K added atomically into
-//                         the fp32 accumulator at the original rows.
-//                         (fp32 tensors; the bf16 kernel below is the same
-//                         algorithm laid out for the bf16 matrix cores.)
-//   3. s2attn_bwd_cvt   : dq = scale * accumulator, rounded to the output type.
+// Three stages on one stream, no atomics:
+//   prep : Dvec[b,h,t] = sum_d dO*O and lse*log2(e), fp32, into the workspace.
+//   dkdv : one workgroup per 128 key rows of one (batch, KV head); it walks
+//          every query head sharing the KV head and, in that head's rolled
+//          frame, every query tile of the group from the diagonal to the group
+//          end, accumulating dK and dV in registers (keys on lanes).
+//   dq   : one workgroup per query tile of one (batch, head); it walks the key
+//          tiles of the group up to the diagonal, recomputing S and dP (queries
+//          on lanes), so dS feeds dQ^T = K^T dS^T straight from registers.
 // dS is kept without the softmax scale; dK and dQ take it at their stores.
+// Each stage has a generic kernel (any element type, register-staged LDS
+// tiles; used for fp32) and a bf16 kernel laid out for the bf16 matrix cores
+// (direct-to-LDS tile loads, transposing LDS reads).
 #include "s2attn_common.h"
 
 namespace s2a {
 
-// ---------------------------------------------------------------------------
-// 1. Dvec and accumulator clear
-// ---------------------------------------------------------------------------
+// ===========================================================================
+// prep
+// ===========================================================================
 template <typename T, int D>
 __global__ __launch_bounds__(256) void s2attn_bwd_pre(
     const T* __restrict__ o, const T* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ dvec,
-    float* __restrict__ lse2, float* __restrict__ dq_acc, int N, int H, long long rows) {
+    float* __restrict__ lse2, int N, int H, long long rows) {
   constexpr int TPR = D / 8;                    // threads per (b, t, h) row
   const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
-  if (row >= rows) return;                      // rows is a multiple of 256 / TPR: whole groups exit
+  if (row >= rows) return;                      // whole TPR-lane groups exit together
   const v8<T> a = *reinterpret_cast<const v8<T>*>(o + row * D + part * 8);
   const v8<T> g = *reinterpret_cast<const v8<T>*>(dO + row * D + part * 8);
   float s = 0.f;
@@ -49,9 +46,6 @@ __global__ __launch_bounds__(256) void s2attn_bwd_pre(
   for (int i = 0; i < 8; ++i) s = fmaf((float)a[i], (float)g[i], s);
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  *reinterpret_cast<f32x4*>(dq_acc + row * D + part * 8) = z;
-  *reinterpret_cast<f32x4*>(dq_acc + row * D + part * 8 + 4) = z;
   if (part == 0) {
     const long long h = row % H;
     const long long bt = row / H;
@@ -60,49 +54,6 @@ __global__ __launch_bounds__(256) void s2attn_bwd_pre(
     lse2[(b * H + h) * N + t] = lse[(b * H + h) * N + t] * kLog2e;
   }
 }
-
-// ---------------------------------------------------------------------------
-// 3. accumulator -> dq
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void s2attn_bwd_cvt(const float* __restrict__ acc, T* __restrict__ dq,
-                                                      long long n8, float scale) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(acc + i * 8);
-  const f32x4 b2 = *reinterpret_cast<const f32x4*>(acc + i * 8 + 4);
-  f32x16 x;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) { x[j] = a[j] * scale; x[4 + j] = b2[j] * scale; }
-  *reinterpret_cast<v8<T>*>(dq + i * 8) = pack8<T>(x, 0);
-}
-
-// ---------------------------------------------------------------------------
-// 2. main kernel
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-struct BwdShape {
-  static constexpr int kThreads = 256;
-  static constexpr int kBKV = 128;                          // key rows per workgroup (32 per wave)
-  static constexpr int kBQ = sizeof(T) == 2 ? 64 : 32;      // query rows per step
-  static constexpr int kNQS = kBQ / 32;
-  static constexpr int kDC = D / 16;
-  static constexpr int kDT = D / 32;
-  static constexpr int kQCPR = D / 8;                       // chunks per row of Qs / dOs
-  static constexpr int kTCPR = kBQ / 8;                     // chunks per row of Qt / dOt
-  static constexpr int kKCPR = kBKV / 8;                    // chunks per row of Kt / dSs
-  static constexpr int kQRowsPerThread = kBQ * D / 8 / kThreads;   // transposed staging
-  static constexpr int kKRowsPerThread = kBKV * D / 8 / kThreads;
-  // LDS layout (in 8-element chunks)
-  static constexpr int kQs = 0;
-  static constexpr int kdOs = kQs + kBQ * kQCPR;
-  static constexpr int kQt = kdOs + kBQ * kQCPR;
-  static constexpr int kdOt = kQt + D * kTCPR;
-  static constexpr int kKt = kdOt + D * kTCPR;
-  static constexpr int kdSs = kKt + D * kKCPR;
-  static constexpr int kChunks = kdSs + kBQ * kKCPR;
-  static constexpr size_t kLdsBytes = kChunks * 8 * sizeof(T) + 2 * kBQ * sizeof(float);
-};
 
 template <typename T, int N_>
 struct alignas(sizeof(T) * N_) PackB { T x[N_]; };
@@ -122,24 +73,42 @@ __device__ __forceinline__ void store_transposed(v8<T>* tile, const v8<T>* regs,
   }
 }
 
+// ===========================================================================
+// dkdv, generic
+// ===========================================================================
 template <typename T, int D>
-__global__ __launch_bounds__(256) void s2attn_bwd_main(
+struct DkdvShape {
+  static constexpr int kThreads = 256;
+  static constexpr int kBKV = 128;                          // key rows per workgroup (32 per wave)
+  static constexpr int kBQ = sizeof(T) == 2 ? 64 : 32;      // query rows per step
+  static constexpr int kNQS = kBQ / 32;
+  static constexpr int kDC = D / 16;
+  static constexpr int kDT = D / 32;
+  static constexpr int kQCPR = D / 8;                       // chunks per row of Qs / dOs
+  static constexpr int kTCPR = kBQ / 8;                     // chunks per row of Qt / dOt
+  static constexpr int kQRowsPerThread = kBQ * D / 8 / kThreads;
+  static constexpr int kQs = 0;
+  static constexpr int kdOs = kQs + kBQ * kQCPR;
+  static constexpr int kQt = kdOs + kBQ * kQCPR;
+  static constexpr int kdOt = kQt + D * kTCPR;
+  static constexpr int kChunks = kdOt + D * kTCPR;
+  static constexpr size_t kLdsBytes = kChunks * 8 * sizeof(T) + 2 * kBQ * sizeof(float);
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ dvec,
-    float* __restrict__ dq_acc, T* __restrict__ dk, T* __restrict__ dv,
-    int N, int H, int Hkv, int G, int shift_heads, float scale) {
-  using S = BwdShape<T, D>;
+    const T* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
+    T* __restrict__ dk, T* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, float scale) {
+  using S = DkdvShape<T, D>;
   constexpr int BKV = S::kBKV, BQ = S::kBQ, NQS = S::kNQS;
-  constexpr int QCPR = S::kQCPR, TCPR = S::kTCPR, KCPR = S::kKCPR;
-  constexpr int QRPT = S::kQRowsPerThread, KRPT = S::kKRowsPerThread;
+  constexpr int QCPR = S::kQCPR, TCPR = S::kTCPR, QRPT = S::kQRowsPerThread;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   v8<T>* smem = reinterpret_cast<v8<T>*>(smem_raw);
   v8<T>* Qs = smem + S::kQs;
   v8<T>* dOs = smem + S::kdOs;
   v8<T>* Qt = smem + S::kQt;
   v8<T>* dOt = smem + S::kdOt;
-  v8<T>* Kt = smem + S::kKt;
-  v8<T>* dSs = smem + S::kdSs;
   float* lse_s = reinterpret_cast<float*>(smem + S::kChunks);   // lse * log2(e)
   float* dvec_s = lse_s + BQ;
 
@@ -161,7 +130,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_main(
   const T* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
   const T* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
 
-  // ---- this wave's 32 keys as B operands (key on lanes, head dim in k-slots)
+  // this wave's 32 keys as B operands (key on lanes, head dim in k-slots)
   const int key_local = wave * 32 + l32;
   const int tk = orig_row(j0 + key_local, sig0, N);
   v8<T> kf[S::kDC], vf[S::kDC];
@@ -169,17 +138,6 @@ __global__ __launch_bounds__(256) void s2attn_bwd_main(
   for (int cc = 0; cc < S::kDC; ++cc) {
     kf[cc] = *reinterpret_cast<const v8<T>*>(kb + (size_t)tk * kvstride + cc * 16 + hf * 8);
     vf[cc] = *reinterpret_cast<const v8<T>*>(vb + (size_t)tk * kvstride + cc * 16 + hf * 8);
-  }
-  // ---- K transposed into LDS (B operand of dQ = dS K)
-  {
-    const int dc = tid % (D / 8), kg = tid / (D / 8);
-    v8<T> kr[KRPT];
-#pragma unroll
-    for (int i = 0; i < KRPT; ++i) {
-      const int t = orig_row(j0 + kg * KRPT + i, sig0, N);
-      kr[i] = *reinterpret_cast<const v8<T>*>(kb + (size_t)t * kvstride + dc * 8);
-    }
-    store_transposed<T, KRPT, KCPR>(Kt, kr, dc, kg * KRPT);
   }
 
   f32x16 dkacc[S::kDT], dvacc[S::kDT];
@@ -201,10 +159,9 @@ __global__ __launch_bounds__(256) void s2attn_bwd_main(
     const int qt_begin = jk0 / BQ, qt_end = (gstart + G) / BQ;
     const T* qb = q + (size_t)b * N * qstride + (size_t)h * D;
     const T* dob = dO + (size_t)b * N * qstride + (size_t)h * D;
-    const float* lse_h = lse + ((size_t)b * H + h) * N;
+    const float* lse_h = lse2 + ((size_t)b * H + h) * N;
     const float* dvec_h = dvec + ((size_t)b * H + h) * N;
-    float* dqacc_h = dq_acc + (size_t)b * N * qstride + (size_t)h * D;
-    const int jkey = jk0 + key_local;           // this lane's key, rolled frame of h
+    const int jkey = jk0 + key_local;
 
     v8<T> qr[QRPT], dr[QRPT];
     float lse_r = 0.f, dvec_r = 0.f;
@@ -217,7 +174,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_main(
       }
       if (tid < BQ) {
         const int t = orig_row(jq0 + tid, sig, N);
-        lse_r = lse_h[t] * kLog2e;
+        lse_r = lse_h[t];
         dvec_r = dvec_h[t];
       }
     };
@@ -225,7 +182,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_main(
     load_q(qt_begin * BQ);
     for (int qt = qt_begin; qt < qt_end; ++qt) {
       const int jq0 = qt * BQ;
-      // stage Q, dO (row-major and transposed), lse, Dvec
+      __syncthreads();                          // previous tile's LDS reads are done
 #pragma unroll
       for (int i = 0; i < QRPT; ++i) {
         const int row = q_qg * QRPT + i;
@@ -275,40 +232,10 @@ __global__ __launch_bounds__(256) void s2attn_bwd_main(
           mma32(dkacc[dt], Qt[chunk_at<TCPR>(row, kc * 2 + hf)], sf);
         }
       }
-      // dS -> LDS as [query][key]
-#pragma unroll
-      for (int qs = 0; qs < NQS; ++qs)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = qs * 32 + (i >> 3) * 16 + hf * 8 + (i & 7);
-          T* rowp = reinterpret_cast<T*>(&dSs[chunk_at<KCPR>(qi, key_local >> 3)]);
-          rowp[key_local & 7] = (T)pacc[qs][i];
-        }
-      __syncthreads();
-
-      // dQ = dS K for this query tile, added into the fp32 accumulator
-      constexpr int n_out = NQS * S::kDT;
-      for (int ot = wave; ot < n_out; ot += 4) {
-        const int qs = ot / S::kDT, dt = ot % S::kDT;
-        f32x16 acc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-        const int rowq = qs * 32 + perm32(l32);
-        const int rowd = dt * 32 + l32;
-#pragma unroll
-        for (int kc = 0; kc < BKV / 16; ++kc)
-          mma32(acc, dSs[chunk_at<KCPR>(rowq, kc * 2 + hf)], Kt[chunk_at<KCPR>(rowd, kc * 2 + hf)]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = qs * 32 + (i >> 3) * 16 + hf * 8 + (i & 7);
-          const int t = orig_row(jq0 + qi, sig, N);
-          atomicAdd(dqacc_h + (size_t)t * qstride + rowd, acc[i]);
-        }
-      }
     }
+    __syncthreads();                            // next head restages the tiles
   }
 
-  // ---- dK, dV at the original key rows
   T* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
   T* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
 #pragma unroll
@@ -320,62 +247,198 @@ __global__ __launch_bounds__(256) void s2attn_bwd_main(
     }
 }
 
+// ===========================================================================
+// dq, generic
+// ===========================================================================
+template <typename T, int D>
+struct DqShape {
+  static constexpr int kThreads = 256;
+  static constexpr int kBR = 128;               // query rows per workgroup (32 per wave)
+  static constexpr int kBC = 64;                // key rows per tile
+  static constexpr int kKCPR = D / 8;
+  static constexpr int kTCPR = kBC / 8;
+  static constexpr int kKRowsPerThread = kBC * D / 8 / kThreads;
+  static constexpr int kDC = D / 16;
+  static constexpr int kDT = D / 32;
+  static constexpr int kKs = 0;
+  static constexpr int kVs = kKs + kBC * kKCPR;
+  static constexpr int kKt = kVs + kBC * kKCPR;
+  static constexpr int kChunks = kKt + D * kTCPR;
+  static constexpr size_t kLdsBytes = kChunks * 8 * sizeof(T);
+};
 
-// ---------------------------------------------------------------------------
-// 2'. bf16 main kernel.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void s2attn_bwd_dq(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
+    const float* __restrict__ lse2, const float* __restrict__ dvec, T* __restrict__ dq,
+    int N, int H, int Hkv, int G, int shift_heads, float scale) {
+  using S = DqShape<T, D>;
+  constexpr int BR = S::kBR, BC = S::kBC, KCPR = S::kKCPR, TCPR = S::kTCPR, KRPT = S::kKRowsPerThread;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  v8<T>* smem = reinterpret_cast<v8<T>*>(smem_raw);
+  v8<T>* Ks = smem + S::kKs;
+  v8<T>* Vs = smem + S::kVs;
+  v8<T>* Kt = smem + S::kKt;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int groups = N / G, tiles_per_group = G / BR;
+  const int x = blockIdx.x;
+  const int pos = tiles_per_group - 1 - x / groups;   // heaviest query tiles first
+  const int grp = x % groups;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int c = h / (H / Hkv);
+  const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
+  const int j0 = grp * G + pos * BR;
+  const int kv_begin = grp * G;
+  const int ntiles = (j0 + BR - kv_begin) / BC;
+
+  const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
+  const T* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
+  const T* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
+
+  // Q and dO operands (B of S^T = K Q^T and dP^T = V dO^T): query on lanes
+  const int jw = j0 + wave * 32;
+  const int jq = jw + l32;
+  const int tq = orig_row(jq, sigma, N);
+  v8<T> qf[S::kDC], dof[S::kDC];
+  {
+    const T* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+    const T* dorow = dO + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+#pragma unroll
+    for (int cc = 0; cc < S::kDC; ++cc) {
+      qf[cc] = *reinterpret_cast<const v8<T>*>(qrow + cc * 16 + hf * 8);
+      dof[cc] = *reinterpret_cast<const v8<T>*>(dorow + cc * 16 + hf * 8);
+    }
+  }
+  const float lse_q = lse2[((size_t)b * H + h) * N + tq];
+  const float dvec_q = dvec[((size_t)b * H + h) * N + tq];
+
+  const int k_dc = tid % (D / 8), k_kg = tid / (D / 8);
+  v8<T> kr[KRPT], vr[KRPT];
+  auto load_tile = [&](int kt0) {
+#pragma unroll
+    for (int i = 0; i < KRPT; ++i) {
+      const int t = orig_row(kt0 + k_kg * KRPT + i, sigma, N);
+      kr[i] = *reinterpret_cast<const v8<T>*>(kb + (size_t)t * kvstride + k_dc * 8);
+      vr[i] = *reinterpret_cast<const v8<T>*>(vb + (size_t)t * kvstride + k_dc * 8);
+    }
+  };
+
+  f32x16 dqacc[S::kDT];
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[dt][i] = 0.f;
+  const float c2 = scale * kLog2e;
+
+  load_tile(kv_begin);
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt0 = kv_begin + it * BC;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KRPT; ++i) {
+      const int row = k_kg * KRPT + i;
+      Ks[chunk_at<KCPR>(row, k_dc)] = kr[i];
+      Vs[chunk_at<KCPR>(row, k_dc)] = vr[i];
+    }
+    store_transposed<T, KRPT, TCPR>(Kt, kr, k_dc, k_kg * KRPT);
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(kt0 + BC);
+    if (kt0 > jw + 31) continue;                // tile entirely after this wave's queries
+
+    // S^T = K Q^T, dP^T = V dO^T : keys on tile rows, queries on lanes
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { s[ks][i] = 0.f; dp[ks][i] = 0.f; }
+      const int row = ks * 32 + perm32(l32);
+#pragma unroll
+      for (int cc = 0; cc < S::kDC; ++cc) {
+        mma32(s[ks], Ks[chunk_at<KCPR>(row, cc * 2 + hf)], qf[cc]);
+        mma32(dp[ks], Vs[chunk_at<KCPR>(row, cc * 2 + hf)], dof[cc]);
+      }
+    }
+    const bool need_mask = kt0 + BC - 1 > jw;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(s[ks][i], c2, -lse_q));
+        if (need_mask && kt0 + ks * 32 + (i >> 3) * 16 + hf * 8 + (i & 7) > jq) p = 0.f;
+        dp[ks][i] = p * (dp[ks][i] - dvec_q);
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kc = 0; kc < BC / 16; ++kc) {
+      const v8<T> sf = pack8<T>(dp[kc >> 1], (kc & 1) * 8);
+#pragma unroll
+      for (int dt = 0; dt < S::kDT; ++dt) {
+        const int row = dt * 32 + perm32(l32);
+        mma32(dqacc[dt], Kt[chunk_at<TCPR>(row, kc * 2 + hf)], sf);
+      }
+    }
+  }
+
+  T* dqrow = dq + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<v8<T>*>(dqrow + dt * 32 + u * 16 + hf * 8) = scale8<T>(dqacc[dt], u * 8, scale);
+}
+
+// ===========================================================================
+// bf16 kernels
 //
-// Same work split as above (one workgroup per 128 key rows of one (batch, KV
-// head), 4 waves x 32 keys, K and V of the wave's keys in registers, 64-row
-// query steps over every query head sharing the KV head), laid out for bf16:
-//   * Q, dO, lse*log2(e) and Dvec tiles go from HBM straight into LDS
-//     (global_load_lds), double-buffered, row-major; a 64-row query tile never
-//     straddles the roll's wrap point, so each tile is one scalar base row.
-//   * Transposed operands (dO^T, Q^T for dV, dK; dS and K for dQ) are read with
-//     ds_read_b64_tr_b16 from the row-major tiles: nothing is transposed on
-//     store.  dS is written as [key][query] with 16-byte stores.
-//   * dS is double-buffered so the dQ product of step j-1 runs inside step j:
-//     one barrier per step.
-// LDS swizzle: 16-byte chunk column c of row r is stored at c ^ swz(r), which
-// keeps both the row-major A-operand reads (16 rows perm32(0..15), one column)
-// and the transposing reads (4 consecutive rows, 4 consecutive columns) free of
-// bank conflicts.
-// ---------------------------------------------------------------------------
+// LDS tiles are row-major and filled straight from HBM (global_load_lds);
+// a 64-row query or key tile never straddles the roll's wrap point (G/2 is a
+// multiple of 64), so each tile is one scalar base row.  Transposed operands
+// come from ds_read_b64_tr_b16.  16-byte chunk column c of row r is stored at
+// c ^ swz2(r), which keeps both the row-major operand reads (16 rows
+// perm32(0..15), one column) and the transposing reads (4 consecutive rows,
+// 4 consecutive columns) free of bank conflicts.
+// ===========================================================================
 template <int CPR>
 __device__ __forceinline__ int swz2(int row) {
   if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
   else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
+// ---------------------------------------------------------------------------
+// dkdv, bf16: 4 waves x 32 keys, 64-row query steps, Q / dO / lse / Dvec tiles
+// double-buffered (one barrier per step).  K of the wave's keys is read from
+// the LDS key tile, V is held in registers.
+// ---------------------------------------------------------------------------
 template <int D>
-struct BwdB16Shape {
+struct DkdvB16Shape {
   static constexpr int kThreads = 256;
   static constexpr int kBKV = 128;
   static constexpr int kBQ = 64;
-  static constexpr int kCPR = D / 8;                    // chunks per Q / dO / K row
-  static constexpr int kSCPR = kBQ / 8;                 // chunks per dS row
-  static constexpr int kQTile = kBQ * kCPR;             // chunks
+  static constexpr int kCPR = D / 8;
+  static constexpr int kQTile = kBQ * kCPR;
   static constexpr int kKTile = kBKV * kCPR;
-  static constexpr int kSTile = kBKV * kSCPR;
   static constexpr int kK = 0;
   static constexpr int kQ = kK + kKTile;                // [2 stages]
   static constexpr int kdO = kQ + 2 * kQTile;           // [2 stages]
-  static constexpr int kdS = kdO + 2 * kQTile;          // [2 buffers]
-  static constexpr int kChunks = kdS + 2 * kSTile;
+  static constexpr int kChunks = kdO + 2 * kQTile;
   static constexpr size_t kLdsBytes = (size_t)kChunks * 16 + 2 * 2 * kBQ * sizeof(float);
   static constexpr int kDC = D / 16;
   static constexpr int kDT = D / 32;
-  static constexpr int kQLoads = kQTile / kThreads;     // chunks per thread per Q (or dO) tile
+  static constexpr int kQLoads = kQTile / kThreads;
   static constexpr int kKLoads = kKTile / kThreads;
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
+__global__ __launch_bounds__(256) void s2attn_bwd_dkdv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
-    float* __restrict__ dq_acc, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    int N, int H, int Hkv, int G, int shift_heads, float scale) {
-  using S = BwdB16Shape<D>;
-  constexpr int BKV = S::kBKV, BQ = S::kBQ, CPR = S::kCPR, SCPR = S::kSCPR;
+    bf16* __restrict__ dk, bf16* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, float scale) {
+  using S = DkdvB16Shape<D>;
+  constexpr int BKV = S::kBKV, BQ = S::kBQ, CPR = S::kCPR;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   bf16x8* smem = reinterpret_cast<bf16x8*>(smem_raw);
   float* fsm = reinterpret_cast<float*>(smem + S::kChunks);   // [stage][lse2 | dvec][BQ]
@@ -398,7 +461,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
   const bf16* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
   const bf16* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
 
-  // ---- K tile into LDS (row-major, rows may cross the wrap point: per-row addresses)
+  // K tile into LDS (its 128 rows may cross the wrap point: per-row addresses)
   {
     bf16x8* Ks = smem + S::kK;
 #pragma unroll
@@ -410,7 +473,6 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
       load_lds16(kb + (size_t)t * kvstride + (pc ^ swz2<CPR>(row)) * 8, Ks + cb);
     }
   }
-  // ---- this wave's 32 keys: V as B operands in registers (K is read from the LDS tile)
   const int key_local = wave * 32 + l32;
   const int tk = orig_row(j0 + key_local, sig0, N);
   bf16x8 vf[S::kDC];
@@ -418,7 +480,6 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
   for (int cc = 0; cc < S::kDC; ++cc)
     vf[cc] = *reinterpret_cast<const bf16x8*>(vb + (size_t)tk * kvstride + cc * 16 + hf * 8);
 
-  // per-lane element offsets of the Q / dO tile chunks this lane moves
   int qoff[S::kQLoads];
 #pragma unroll
   for (int i = 0; i < S::kQLoads; ++i) {
@@ -427,7 +488,6 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
     qoff[i] = row * (int)qstride + (pc ^ swz2<CPR>(row)) * 8;
   }
 
-  // ---- step cursor over (query head, query tile)
   auto head_frame = [&](int hh, int& sig, int& jk0, int& qt_b, int& qt_e) {
     const int h = h0 + hh;
     sig = (h >= H - shift_heads) ? G / 2 : 0;
@@ -439,7 +499,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
   };
   auto issue_step = [&](int hh, int qt, int sig, int stage) {
     const int h = h0 + hh;
-    const int t0 = orig_row(qt * BQ, sig, N);         // whole tile contiguous
+    const int t0 = orig_row(qt * BQ, sig, N);
     const bf16* qg = q + ((size_t)b * N + t0) * qstride + (size_t)h * D;
     const bf16* dog = dO + ((size_t)b * N + t0) * qstride + (size_t)h * D;
     bf16x8* Qs = smem + S::kQ + stage * S::kQTile;
@@ -462,54 +522,12 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
     for (int i = 0; i < 16; ++i) { dkacc[dt][i] = 0.f; dvacc[dt][i] = 0.f; }
   const float c2 = scale * kLog2e;
 
-  // dQ of one finished step: 32x32 (query, head-dim) tiles; with d = 128 a wave
-  // owns head-dim block dt = wave for both 32-query halves (sharing its K reads),
-  // with d = 64 one tile (qs, dt) per wave.
-  constexpr int NT = S::kDT / 2;
-  const int dq_dt = S::kDT == 4 ? wave : (wave & 1);
-  const int dq_qs0 = S::kDT == 4 ? 0 : (wave >> 1);
-  const int rowbytes = (int)(qstride * sizeof(float));
-  auto dq_step = [&](int buf, int h, int t0) {
-    const bf16* dSs = reinterpret_cast<const bf16*>(smem + S::kdS + buf * S::kSTile);
-    const bf16* Ks = reinterpret_cast<const bf16*>(smem + S::kK);
-    f32x16 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
-    const int dcol = dq_dt * 32 + ((g16 & 1) << 4) + 4 * tm;     // B: K columns = head dim
-#pragma unroll
-    for (int kc = 0; kc < BKV / 16; ++kc) {
-      const int r0 = kc * 16 + hf * 8 + ts, r1 = r0 + 4;
-      const bf16x8 bk = tr_read8(Ks + (r0 * CPR + ((dcol >> 3) ^ swz2<CPR>(r0))) * 8 + (dcol & 7),
-                                 Ks + (r1 * CPR + ((dcol >> 3) ^ swz2<CPR>(r1))) * 8 + (dcol & 7));
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int qcol = (dq_qs0 + t) * 32 + ((g16 & 1) << 4) + 4 * tm;   // A: dS rows = queries
-        const bf16x8 a = tr_read8(dSs + (r0 * SCPR + ((qcol >> 3) ^ swz2<SCPR>(r0))) * 8 + (qcol & 7),
-                                  dSs + (r1 * SCPR + ((qcol >> 3) ^ swz2<SCPR>(r1))) * 8 + (qcol & 7));
-        mma32(acc[t], a, bk);
-      }
-    }
-    // lane holds head-dim column dt*32 + l32 of query rows qs*32 + 8*(i>>2) + 4*hf + (i&3)
-    float* tile = dq_acc + ((size_t)b * N + t0) * qstride + (size_t)h * D;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, BQ * rowbytes);
-    const int voff = (hf * 4 * (int)qstride + dq_dt * 32 + l32) * (int)sizeof(float);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        buffer_atomic_add(acc[t][i], rs, voff, ((dq_qs0 + t) * 32 + (i >> 2) * 8 + (i & 3)) * rowbytes);
-  };
-
   int hh = 0, sig, jk0, qt_b, qt_e;
   head_frame(0, sig, jk0, qt_b, qt_e);
   int qt = qt_b;
   issue_step(hh, qt, sig, 0);
-  int prev_h = -1, prev_t0 = 0, last_stage = 0;
   for (int step = 0;; ++step) {
     const int stage = step & 1;
-    // next step's cursor
     int nhh = hh, nqt = qt + 1, nsig = sig, njk0 = jk0, nqt_b = qt_b, nqt_e = qt_e;
     if (nqt == qt_e) {
       ++nhh;
@@ -521,10 +539,9 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
     const bool has_next = nhh < r;
 
     wait_vmem_all();
-    __syncthreads();
+    __syncthreads();                            // tile landed for all; the other stage is free
     if (has_next) issue_step(nhh, nqt, nsig, stage ^ 1);
 
-    const int h = h0 + hh;
     const int jq0 = qt * BQ;
     const bf16* Qs = reinterpret_cast<const bf16*>(smem + S::kQ + stage * S::kQTile);
     const bf16* dOs = reinterpret_cast<const bf16*>(smem + S::kdO + stage * S::kQTile);
@@ -554,9 +571,6 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
       }
     }
 
-    // dQ of the previous step (its dS is complete in LDS after the barrier)
-    if (prev_h >= 0) dq_step(stage ^ 1, prev_h, prev_t0);
-
     // P = exp2(S c - lse log2 e), dS = P (dP - Dvec)
     const int jkey = jk0 + key_local;
     const bool need_mask = jk0 + wave * 32 + 31 > jq0;
@@ -581,45 +595,25 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
       }
 
     // dV^T += dO^T P, dK^T += Q^T dS (A operands through transposing reads)
-    bf16x8 pf[4], sf[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      pf[kc] = pack8<bf16>(sacc[kc >> 1], (kc & 1) * 8);
-      sf[kc] = pack8<bf16>(pacc[kc >> 1], (kc & 1) * 8);
-    }
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 pf = pack8<bf16>(sacc[kc >> 1], (kc & 1) * 8);
+      const bf16x8 sf = pack8<bf16>(pacc[kc >> 1], (kc & 1) * 8);
       const int r0 = kc * 16 + hf * 8 + ts, r1 = r0 + 4;
 #pragma unroll
       for (int dt = 0; dt < S::kDT; ++dt) {
         const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
         const int o0 = (r0 * CPR + ((dbase >> 3) ^ swz2<CPR>(r0))) * 8 + (dbase & 7);
         const int o1 = (r1 * CPR + ((dbase >> 3) ^ swz2<CPR>(r1))) * 8 + (dbase & 7);
-        mma32(dvacc[dt], tr_read8(dOs + o0, dOs + o1), pf[kc]);
-        mma32(dkacc[dt], tr_read8(Qs + o0, Qs + o1), sf[kc]);
+        mma32(dvacc[dt], tr_read8(dOs + o0, dOs + o1), pf);
+        mma32(dkacc[dt], tr_read8(Qs + o0, Qs + o1), sf);
       }
     }
 
-    // dS -> LDS as [key][query]: 8 consecutive queries per 16-byte store
-    {
-      bf16x8* dSs = smem + S::kdS + stage * S::kSTile;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int chunk = kc * 2 + hf;       // queries kc*16 + hf*8 .. +7
-        dSs[key_local * SCPR + (chunk ^ swz2<SCPR>(key_local))] = sf[kc];
-      }
-    }
-
-    prev_h = h;
-    prev_t0 = orig_row(jq0, sig, N);
-    last_stage = stage;
     if (!has_next) break;
     hh = nhh; qt = nqt; sig = nsig; jk0 = njk0; qt_b = nqt_b; qt_e = nqt_e;
   }
-  __syncthreads();                               // the last step's dS is complete
-  dq_step(last_stage, prev_h, prev_t0);
 
-  // ---- dK (scaled), dV at the original key rows
   bf16* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
   bf16* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
 #pragma unroll
@@ -631,72 +625,265 @@ __global__ __launch_bounds__(256) void s2attn_bwd_bf16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// dq, bf16: 8 waves x 32 queries (two waves per SIMD), 64-row key / value tiles
+// double-buffered in LDS.  Per tile: S^T = K Q^T and dP^T = V dO^T (queries
+// on lanes, so lse and Dvec are one value per lane), dS^T in registers, and
+// dQ^T += K^T dS^T with K^T read through transposing reads.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqB16Shape {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 512;
+  static constexpr int kBR = 256;
+  static constexpr int kBC = 64;
+  static constexpr int kCPR = D / 8;
+  static constexpr int kTile = kBC * kCPR;               // chunks per K (or V) tile
+  static constexpr int kLoads = kTile / kThreads;
+  static constexpr int kDC = D / 16;
+  static constexpr int kDT = D / 32;
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
+    bf16* __restrict__ dq, int N, int H, int Hkv, int G, int shift_heads, float scale) {
+  using S = DqB16Shape<D>;
+  constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTile;
+  __shared__ bf16x8 smem[2 * 2 * TC];             // [stage][K, V][chunk]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
+
+  const int groups = N / G, tiles_per_group = G / BR;
+  const int x = blockIdx.x;
+  const int pos = tiles_per_group - 1 - x / groups;
+  const int grp = x % groups;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int c = h / (H / Hkv);
+  const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
+  const int j0 = grp * G + pos * BR;
+  const int kv_begin = grp * G;
+  const int ntiles = (j0 + BR - kv_begin) / BC;
+
+  const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
+  const bf16* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
+  const bf16* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
+
+  const int jw = j0 + wave * 32;
+  const int jq = jw + l32;
+  const int tq = orig_row(jq, sigma, N);
+  bf16x8 qf[S::kDC], dof[S::kDC];
+  {
+    const bf16* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+    const bf16* dorow = dO + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+#pragma unroll
+    for (int cc = 0; cc < S::kDC; ++cc) {
+      qf[cc] = *reinterpret_cast<const bf16x8*>(qrow + cc * 16 + hf * 8);
+      dof[cc] = *reinterpret_cast<const bf16x8*>(dorow + cc * 16 + hf * 8);
+    }
+  }
+  const float lse_q = lse2[((size_t)b * H + h) * N + tq];
+  const float dvec_q = dvec[((size_t)b * H + h) * N + tq];
+
+  int toff[S::kLoads];
+#pragma unroll
+  for (int i = 0; i < S::kLoads; ++i) {
+    const int p = (wave + S::kWaves * i) * 64 + lane;
+    const int row = p / CPR, pc = p % CPR;
+    toff[i] = row * (int)kvstride + (pc ^ swz2<CPR>(row)) * 8;
+  }
+  auto issue_tile = [&](int kt0, int stage) {
+    const size_t t0 = (size_t)orig_row(kt0, sigma, N) * kvstride;
+    bf16x8* ks = smem + (2 * stage) * TC;
+    bf16x8* vs = ks + TC;
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) {
+      const int cb = (wave + S::kWaves * i) * 64;
+      load_lds16(kb + t0 + toff[i], ks + cb);
+      load_lds16(vb + t0 + toff[i], vs + cb);
+    }
+  };
+
+  f32x16 dqacc[S::kDT];
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[dt][r] = 0.f;
+  const float c2 = scale * kLog2e;
+  const int krow = perm32(l32);
+  const int ksw = swz2<CPR>(krow);               // same for krow + 32
+
+  issue_tile(kv_begin, 0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt0 = kv_begin + it * BC;
+    wait_vmem_all();
+    __syncthreads();
+    if (it + 1 < ntiles) issue_tile(kt0 + BC, (it + 1) & 1);
+    if (kt0 > jw + 31) continue;
+
+    const bf16* Ks = reinterpret_cast<const bf16*>(smem + (2 * (it & 1)) * TC);
+    const bf16* Vs = Ks + TC * 8;
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { s[ks][r] = 0.f; dp[ks][r] = 0.f; }
+      const int row = ks * 32 + krow;
+#pragma unroll
+      for (int cc = 0; cc < S::kDC; ++cc) {
+        const int off = (row * CPR + ((2 * cc + hf) ^ ksw)) * 8;
+        mma32(s[ks], *reinterpret_cast<const bf16x8*>(Ks + off), qf[cc]);
+        mma32(dp[ks], *reinterpret_cast<const bf16x8*>(Vs + off), dof[cc]);
+      }
+    }
+    const bool need_mask = kt0 + BC - 1 > jw;
+    bf16x8 sf[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      f32x8 dsv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = (kc & 1) * 8 + i;
+        float p = fast_exp2(fmaf(s[kc >> 1][rr], c2, -lse_q));
+        if (need_mask && kt0 + kc * 16 + hf * 8 + i > jq) p = 0.f;
+        dsv[i] = p * (dp[kc >> 1][rr] - dvec_q);
+      }
+      sf[kc] = __builtin_convertvector(dsv, bf16x8);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int r0 = kc * 16 + hf * 8 + ts, r1 = r0 + 4;
+#pragma unroll
+      for (int dt = 0; dt < S::kDT; ++dt) {
+        const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
+        const bf16* p0 = Ks + (r0 * CPR + ((dbase >> 3) ^ swz2<CPR>(r0))) * 8 + (dbase & 7);
+        const bf16* p1 = Ks + (r1 * CPR + ((dbase >> 3) ^ swz2<CPR>(r1))) * 8 + (dbase & 7);
+        mma32(dqacc[dt], tr_read8(p0, p1), sf[kc]);
+      }
+    }
+  }
+
+  bf16* dqrow = dq + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<bf16x8*>(dqrow + dt * 32 + u * 16 + hf * 8) = scale8<bf16>(dqacc[dt], u * 8, scale);
+}
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+template <typename K>
+hipError_t raise_lds_limit(K kernel, size_t bytes, bool& done) {
+  if (done) return hipSuccess;   // idempotent; a race only repeats the call
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
 template <typename T, int D>
 hipError_t launch_bwd_prep(const void* o, const void* dO, const float* lse, float* dvec, float* lse2,
-                           float* dq_acc, int B, int H, int N, hipStream_t stream) {
+                           int B, int H, int N, hipStream_t stream) {
   const long long rows = (long long)B * N * H;
   constexpr int rpb = 256 / (D / 8);
   hipLaunchKernelGGL((s2attn_bwd_pre<T, D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream,
-                     (const T*)o, (const T*)dO, lse, dvec, lse2, dq_acc, N, H, rows);
+                     (const T*)o, (const T*)dO, lse, dvec, lse2, N, H, rows);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_bwd_main_bf16(const void* q, const void* k, const void* v, const float* lse2, const void* dO,
-                                void* dk, void* dv, const float* dvec, float* dq_acc,
-                                int B, int H, int Hkv, int N, int G, int shift_heads, float scale,
-                                hipStream_t stream) {
-  using S = BwdB16Shape<D>;
-  static bool attr_set = false;   // raising the LDS limit is idempotent; a race only repeats it
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&s2attn_bwd_bf16_kernel<D>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((s2attn_bwd_bf16_kernel<D>), dim3(N / S::kBKV, Hkv, B), dim3(S::kThreads), S::kLdsBytes,
-                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, dq_acc,
+hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                            const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
+                            int shift_heads, float scale, hipStream_t stream) {
+  using S = DkdvB16Shape<D>;
+  static bool attr = false;
+  hipError_t e = raise_lds_limit(&s2attn_bwd_dkdv_bf16<D>, S::kLdsBytes, attr);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D>), dim3(N / S::kBKV, Hkv, B), dim3(S::kThreads), S::kLdsBytes,
+                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec,
                      (bf16*)dk, (bf16*)dv, N, H, Hkv, G, shift_heads, scale);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse, const float* lse2,
-                           const void* dO, void* dk, void* dv, const float* dvec, float* dq_acc,
-                           int B, int H, int Hkv, int N, int G, int shift_heads, hipStream_t stream) {
-  using S = BwdShape<T, D>;
-  const float scale = 1.0f / sqrtf((float)D);
-  if constexpr (sizeof(T) == 2)
-    return launch_bwd_main_bf16<D>(q, k, v, lse2, dO, dk, dv, dvec, dq_acc, B, H, Hkv, N, G, shift_heads, scale,
-                                   stream);
-  static bool attr_set = false;   // raising the LDS limit is idempotent; a race only repeats it
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&s2attn_bwd_main<T, D>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((s2attn_bwd_main<T, D>), dim3(N / S::kBKV, Hkv, B), dim3(256), S::kLdsBytes, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse, dvec,
-                     dq_acc, (T*)dk, (T*)dv, N, H, Hkv, G, shift_heads, scale);
+hipError_t launch_dkdv_generic(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                               const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
+                               int shift_heads, float scale, hipStream_t stream) {
+  using S = DkdvShape<T, D>;
+  static bool attr = false;
+  hipError_t e = raise_lds_limit(&s2attn_bwd_dkdv<T, D>, S::kLdsBytes, attr);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), dim3(N / S::kBKV, Hkv, B), dim3(S::kThreads), S::kLdsBytes,
+                     stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dk, (T*)dv, N,
+                     H, Hkv, G, shift_heads, scale);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_bwd_finish(void* dq, const float* dq_acc, int B, int H, int N, hipStream_t stream) {
-  const long long n8 = (long long)B * N * H * D / 8;
-  hipLaunchKernelGGL((s2attn_bwd_cvt<T>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                     dq_acc, (T*)dq, n8, 1.0f / sqrtf((float)D));
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                           const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
+                           int shift_heads, hipStream_t stream) {
+  const float scale = 1.0f / sqrtf((float)D);
+  if constexpr (sizeof(T) == 2)
+    return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, scale, stream);
+  else
+    return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, scale,
+                                     stream);
+}
+
+template <int D>
+hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                          const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
+                          float scale, hipStream_t stream) {
+  using S = DqB16Shape<D>;
+  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D>), dim3(N / S::kBR, H, B), dim3(S::kThreads), 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dq, N, H,
+                     Hkv, G, shift_heads, scale);
   return hipGetLastError();
 }
 
-#define S2A_INST_BWD(T, D)                                                                               \
-  template hipError_t launch_bwd_prep<T, D>(const void*, const void*, const float*, float*, float*,     \
-                                            float*, int, int, int, hipStream_t);                       \
-  template hipError_t launch_bwd_main<T, D>(const void*, const void*, const void*, const float*,        \
-                                            const float*, const void*, void*, void*, const float*,     \
-                                            float*, int, int, int, int, int, int, hipStream_t);         \
-  template hipError_t launch_bwd_finish<T, D>(void*, const float*, int, int, int, hipStream_t);
+template <typename T, int D>
+hipError_t launch_dq_generic(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                             const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
+                             float scale, hipStream_t stream) {
+  using S = DqShape<T, D>;
+  static bool attr = false;
+  hipError_t e = raise_lds_limit(&s2attn_bwd_dq<T, D>, S::kLdsBytes, attr);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((s2attn_bwd_dq<T, D>), dim3(N / S::kBR, H, B), dim3(S::kThreads), S::kLdsBytes, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dq, N, H, Hkv, G,
+                     shift_heads, scale);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                         const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
+                         hipStream_t stream) {
+  const float scale = 1.0f / sqrtf((float)D);
+  if constexpr (sizeof(T) == 2) {
+    if (G % DqB16Shape<D>::kBR == 0)
+      return launch_dq_bf16<D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, scale, stream);
+  }
+  return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, scale, stream);
+}
+
+#define S2A_INST_BWD(T, D)                                                                                 \
+  template hipError_t launch_bwd_prep<T, D>(const void*, const void*, const float*, float*, float*, int,  \
+                                            int, int, hipStream_t);                                        \
+  template hipError_t launch_bwd_dkdv<T, D>(const void*, const void*, const void*, const void*,           \
+                                            const float*, const float*, void*, void*, int, int, int, int,  \
+                                            int, int, hipStream_t);                                        \
+  template hipError_t launch_bwd_dq<T, D>(const void*, const void*, const void*, const void*, const float*, \
+                                          const float*, void*, int, int, int, int, int, int, hipStream_t);
 S2A_INST_BWD(bf16, 64)
 S2A_INST_BWD(bf16, 128)
 S2A_INST_BWD(float, 64)
