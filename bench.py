@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--workload", default="llama2-7b-32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hbm-copy-bytes", type=int, default=0,
+                    help="after timing, run one plain device-to-device copy of this many bytes; under "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it calibrates the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -222,6 +225,14 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if args.hbm_copy_bytes > 0:
+        src = torch.empty(args.hbm_copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["hbm_copy_bytes"] = src.numel() * 4
+        del src, dst
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -26,6 +26,8 @@
 // (direct-to-LDS tile loads, transposing LDS reads).
 #include "s2attn_common.h"
 
+#include <type_traits>
+
 namespace s2a {
 
 // ===========================================================================
@@ -409,44 +411,63 @@ __device__ __forceinline__ int swz2(int row) {
 }
 
 // ---------------------------------------------------------------------------
-// dkdv, bf16: 4 waves x 32 keys, 64-row query steps, Q / dO / lse / Dvec tiles
-// double-buffered (one barrier per step).  K of the wave's keys is read from
-// the LDS key tile, V is held in registers.
+// dkdv, bf16: 8 waves (two per SIMD, so one wave's matrix-core work overlaps
+// its partner's softmax).  Wave w owns keys 32*(w & 3) .. +31 of the 128-key
+// tile and query half w >> 2 of every 64-row query step; the two halves' dK,
+// dV partial sums meet in LDS at the end.  K and V tiles stay in LDS for the
+// whole workgroup; Q, dO, lse*log2(e) and Dvec tiles are double-buffered with
+// one barrier per step.  Every LDS read is a per-lane offset fixed before the
+// loop plus a compile-time immediate (the step loop is unrolled over the two
+// buffer stages); diagonal steps run a masked instantiation and steps whose
+// keys all follow the wave's queries are skipped.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvB16Shape {
-  static constexpr int kThreads = 256;
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 512;
   static constexpr int kBKV = 128;
   static constexpr int kBQ = 64;
   static constexpr int kCPR = D / 8;
-  static constexpr int kQTile = kBQ * kCPR;
-  static constexpr int kKTile = kBKV * kCPR;
-  static constexpr int kK = 0;
-  static constexpr int kQ = kK + kKTile;                // [2 stages]
-  static constexpr int kdO = kQ + 2 * kQTile;           // [2 stages]
-  static constexpr int kChunks = kdO + 2 * kQTile;
-  static constexpr size_t kLdsBytes = (size_t)kChunks * 16 + 2 * 2 * kBQ * sizeof(float);
+  static constexpr int kRowB = D * 2;                     // bytes per tile row
+  static constexpr int kQTileB = kBQ * kRowB;
+  static constexpr int kKTileB = kBKV * kRowB;
+  static constexpr int kK = 0;                            // byte offsets
+  static constexpr int kV = kK + kKTileB;
+  static constexpr int kQ = kV + kKTileB;                 // [2 stages]
+  static constexpr int kdO = kQ + 2 * kQTileB;            // [2 stages]
+  static constexpr int kF = kdO + 2 * kQTileB;            // floats [stage][lse2 | dvec][kBQ]
+  static constexpr size_t kLdsBytes = (size_t)kF + 2 * 2 * kBQ * sizeof(float);
   static constexpr int kDC = D / 16;
   static constexpr int kDT = D / 32;
-  static constexpr int kQLoads = kQTile / kThreads;
-  static constexpr int kKLoads = kKTile / kThreads;
+  static constexpr int kQLoads = kBQ * kCPR / kThreads;   // 16-byte chunks per thread per Q (or dO) tile
+  static constexpr int kKLoads = kBKV * kCPR / kThreads;
+  // end-of-kernel exchange of the dK, dV partial sums: [key group][dK|dV][dt][reg][lane] floats
+  static constexpr size_t kXchgBytes = (size_t)4 * 2 * kDT * 16 * 64 * sizeof(float);
+  static_assert(kXchgBytes <= kLdsBytes, "partial sums must fit in the LDS tiles");
 };
 
+__device__ __forceinline__ bf16x8 lds_b128(const char* base, int off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+__device__ __forceinline__ f32x4 lds_f32x4(const char* base, int off) {
+  return *reinterpret_cast<const f32x4*>(base + off);
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void s2attn_bwd_dkdv_bf16(
+__global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
     bf16* __restrict__ dk, bf16* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, float scale) {
   using S = DkdvB16Shape<D>;
-  constexpr int BKV = S::kBKV, BQ = S::kBQ, CPR = S::kCPR;
+  constexpr int BKV = S::kBKV, BQ = S::kBQ, CPR = S::kCPR, RB = S::kRowB;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16x8* smem = reinterpret_cast<bf16x8*>(smem_raw);
-  float* fsm = reinterpret_cast<float*>(smem + S::kChunks);   // [stage][lse2 | dvec][BQ]
+  char* lds = reinterpret_cast<char*>(smem_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
+  const int kg = wave & 3, qh = wave >> 2;
 
   const int groups = N / G;
   const int x = blockIdx.x;
@@ -461,32 +482,45 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv_bf16(
   const bf16* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
   const bf16* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
 
-  // K tile into LDS (its 128 rows may cross the wrap point: per-row addresses)
-  {
-    bf16x8* Ks = smem + S::kK;
+  // K and V tiles into LDS once (their 128 rows may cross the wrap point)
 #pragma unroll
-    for (int i = 0; i < S::kKLoads; ++i) {
-      const int cb = (wave + 4 * i) * 64;
-      const int p = cb + lane;
-      const int row = p / CPR, pc = p % CPR;
-      const int t = orig_row(j0 + row, sig0, N);
-      load_lds16(kb + (size_t)t * kvstride + (pc ^ swz2<CPR>(row)) * 8, Ks + cb);
-    }
+  for (int i = 0; i < S::kKLoads; ++i) {
+    const int cb = (wave + S::kWaves * i) * 64;
+    const int p = cb + lane;
+    const int row = p / CPR, pc = p % CPR;
+    const size_t g = (size_t)orig_row(j0 + row, sig0, N) * kvstride + (pc ^ swz2<CPR>(row)) * 8;
+    load_lds16(kb + g, lds + S::kK + cb * 16);
+    load_lds16(vb + g, lds + S::kV + cb * 16);
   }
-  const int key_local = wave * 32 + l32;
-  const int tk = orig_row(j0 + key_local, sig0, N);
-  bf16x8 vf[S::kDC];
-#pragma unroll
-  for (int cc = 0; cc < S::kDC; ++cc)
-    vf[cc] = *reinterpret_cast<const bf16x8*>(vb + (size_t)tk * kvstride + cc * 16 + hf * 8);
-
   int qoff[S::kQLoads];
 #pragma unroll
   for (int i = 0; i < S::kQLoads; ++i) {
-    const int p = (wave + 4 * i) * 64 + lane;
+    const int p = (wave + S::kWaves * i) * 64 + lane;
     const int row = p / CPR, pc = p % CPR;
     qoff[i] = row * (int)qstride + (pc ^ swz2<CPR>(row)) * 8;
   }
+
+  // ---- per-lane LDS byte offsets
+  const int key_row = kg * 32 + l32;                  // B operand of S and dP: this lane's key
+  int offB[S::kDC];
+  const int arow = qh * 32 + perm32(l32);             // A operand of S and dP: query rows
+  int offA[S::kDC];
+#pragma unroll
+  for (int cc = 0; cc < S::kDC; ++cc) {
+    offB[cc] = key_row * RB + (((2 * cc + hf) ^ swz2<CPR>(key_row)) << 4);
+    offA[cc] = arow * RB + (((2 * cc + hf) ^ swz2<CPR>(arow)) << 4);
+  }
+  // transposing reads of dO^T / Q^T: rows (queries) qh*32 + 16u + 8hf + 4t + ts, head-dim columns of block dt
+  int offT[S::kDT][2];
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = qh * 32 + hf * 8 + 4 * t + ts;
+      const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
+      offT[dt][t] = row * RB + (((dbase >> 3) ^ swz2<CPR>(row)) << 4) + (dbase & 7) * 2;
+    }
+  const int offL = (qh * 32 + hf * 8) * 4;            // lse / Dvec floats of this lane's queries
 
   auto head_frame = [&](int hh, int& sig, int& jk0, int& qt_b, int& qt_e) {
     const int h = h0 + hh;
@@ -499,20 +533,18 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv_bf16(
   };
   auto issue_step = [&](int hh, int qt, int sig, int stage) {
     const int h = h0 + hh;
-    const int t0 = orig_row(qt * BQ, sig, N);
+    const int t0 = orig_row(qt * BQ, sig, N);         // a 64-row tile is contiguous
     const bf16* qg = q + ((size_t)b * N + t0) * qstride + (size_t)h * D;
     const bf16* dog = dO + ((size_t)b * N + t0) * qstride + (size_t)h * D;
-    bf16x8* Qs = smem + S::kQ + stage * S::kQTile;
-    bf16x8* dOs = smem + S::kdO + stage * S::kQTile;
 #pragma unroll
     for (int i = 0; i < S::kQLoads; ++i) {
-      const int cb = (wave + 4 * i) * 64;
-      load_lds16(qg + qoff[i], Qs + cb);
-      load_lds16(dog + qoff[i], dOs + cb);
+      const int cb = (wave + S::kWaves * i) * 64 * 16;
+      load_lds16(qg + qoff[i], lds + S::kQ + stage * S::kQTileB + cb);
+      load_lds16(dog + qoff[i], lds + S::kdO + stage * S::kQTileB + cb);
     }
     const size_t rowbase = ((size_t)b * H + h) * N + t0;
-    if (wave == 0) load_lds4(lse2 + rowbase + lane, fsm + stage * 2 * BQ);
-    if (wave == 1) load_lds4(dvec + rowbase + lane, fsm + stage * 2 * BQ + BQ);
+    if (wave == 0) load_lds4(lse2 + rowbase + lane, lds + S::kF + stage * 2 * BQ * 4);
+    if (wave == 1) load_lds4(dvec + rowbase + lane, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
   };
 
   f32x16 dkacc[S::kDT], dvacc[S::kDT];
@@ -522,109 +554,124 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv_bf16(
     for (int i = 0; i < 16; ++i) { dkacc[dt][i] = 0.f; dvacc[dt][i] = 0.f; }
   const float c2 = scale * kLog2e;
 
+  // one query step for this wave: STG = LDS stage, MASK = causal mask needed
+  auto compute = [&](auto stg_c, auto mask_c, int jkey, int jq_first) {
+    constexpr int STG = decltype(stg_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    const char* Qs = lds + S::kQ + STG * S::kQTileB;
+    const char* dOs = lds + S::kdO + STG * S::kQTileB;
+    const char* Fs = lds + S::kF + STG * 2 * BQ * 4;
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; pacc[i] = 0.f; }
+#pragma unroll
+    for (int cc = 0; cc < S::kDC; ++cc) {
+      mma32(sacc, lds_b128(Qs, offA[cc]), lds_b128(lds + S::kK, offB[cc]));
+      mma32(pacc, lds_b128(dOs, offA[cc]), lds_b128(lds + S::kV, offB[cc]));
+    }
+    bf16x8 pf[2], sf[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const f32x4 l0 = lds_f32x4(Fs, offL + u * 64), l1 = lds_f32x4(Fs, offL + u * 64 + 16);
+      const f32x4 d0 = lds_f32x4(Fs, BQ * 4 + offL + u * 64), d1 = lds_f32x4(Fs, BQ * 4 + offL + u * 64 + 16);
+      f32x8 pv, sv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float lq = i < 4 ? l0[i] : l1[i - 4];
+        const float dq = i < 4 ? d0[i] : d1[i - 4];
+        float p = fast_exp2(fmaf(sacc[u * 8 + i], c2, -lq));
+        if (MASK && jkey > jq_first + u * 16 + i) p = 0.f;
+        pv[i] = p;
+        sv[i] = p * (pacc[u * 8 + i] - dq);
+      }
+      pf[u] = __builtin_convertvector(pv, bf16x8);
+      sf[u] = __builtin_convertvector(sv, bf16x8);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < S::kDT; ++dt) {
+        const int o0 = offT[dt][0] + u * 16 * RB, o1 = offT[dt][1] + u * 16 * RB;
+        mma32(dvacc[dt], tr_read8(reinterpret_cast<const bf16*>(dOs + o0), reinterpret_cast<const bf16*>(dOs + o1)),
+              pf[u]);
+        mma32(dkacc[dt], tr_read8(reinterpret_cast<const bf16*>(Qs + o0), reinterpret_cast<const bf16*>(Qs + o1)),
+              sf[u]);
+      }
+  };
+  auto step = [&](auto stg_c, int jk0, int qt) {
+    const int jq0 = qt * BQ;
+    const int key_lo = jk0 + kg * 32, q_lo = jq0 + qh * 32;
+    if (key_lo > q_lo + 31) return;                   // every key follows every query: P = 0
+    const int jkey = key_lo + l32, jq_first = q_lo + hf * 8;
+    if (key_lo + 31 > q_lo)
+      compute(stg_c, std::integral_constant<bool, true>(), jkey, jq_first);
+    else
+      compute(stg_c, std::integral_constant<bool, false>(), jkey, jq_first);
+  };
+
   int hh = 0, sig, jk0, qt_b, qt_e;
   head_frame(0, sig, jk0, qt_b, qt_e);
   int qt = qt_b;
   issue_step(hh, qt, sig, 0);
-  for (int step = 0;; ++step) {
-    const int stage = step & 1;
-    int nhh = hh, nqt = qt + 1, nsig = sig, njk0 = jk0, nqt_b = qt_b, nqt_e = qt_e;
+  // advance the cursor to the next (head, query tile); returns false past the end
+  auto advance = [&](int& nhh, int& nqt, int& nsig, int& njk0, int& nqb, int& nqe) {
+    nhh = hh; nqt = qt + 1; nsig = sig; njk0 = jk0; nqb = qt_b; nqe = qt_e;
     if (nqt == qt_e) {
       ++nhh;
       if (nhh < r) {
-        head_frame(nhh, nsig, njk0, nqt_b, nqt_e);
-        nqt = nqt_b;
+        head_frame(nhh, nsig, njk0, nqb, nqe);
+        nqt = nqb;
       }
     }
-    const bool has_next = nhh < r;
-
+    return nhh < r;
+  };
+  auto one = [&](auto stg_c) {
+    constexpr int STG = decltype(stg_c)::value;
+    int nhh, nqt, nsig, njk0, nqb, nqe;
+    const bool more = advance(nhh, nqt, nsig, njk0, nqb, nqe);
     wait_vmem_all();
-    __syncthreads();                            // tile landed for all; the other stage is free
-    if (has_next) issue_step(nhh, nqt, nsig, stage ^ 1);
-
-    const int jq0 = qt * BQ;
-    const bf16* Qs = reinterpret_cast<const bf16*>(smem + S::kQ + stage * S::kQTile);
-    const bf16* dOs = reinterpret_cast<const bf16*>(smem + S::kdO + stage * S::kQTile);
-    const float* lse_s = fsm + stage * 2 * BQ;
-    const float* dvec_s = lse_s + BQ;
-
-    // S = Q K^T, dP = dO V^T : keys on lanes, queries in registers
-    f32x16 sacc[2], pacc[2];
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { sacc[qs][i] = 0.f; pacc[qs][i] = 0.f; }
-    {
-      const bf16* Ks = reinterpret_cast<const bf16*>(smem + S::kK);
-      const int ksw = swz2<CPR>(key_local);
-      const int row = perm32(l32);                 // qs * 32 + row keeps the same swizzle
-      const int sw = swz2<CPR>(row);
-#pragma unroll
-      for (int cc = 0; cc < S::kDC; ++cc) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (key_local * CPR + ((2 * cc + hf) ^ ksw)) * 8);
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          const int off = ((qs * 32 + row) * CPR + ((2 * cc + hf) ^ sw)) * 8;
-          mma32(sacc[qs], *reinterpret_cast<const bf16x8*>(Qs + off), kf);
-          mma32(pacc[qs], *reinterpret_cast<const bf16x8*>(dOs + off), vf[cc]);
-        }
-      }
-    }
-
-    // P = exp2(S c - lse log2 e), dS = P (dP - Dvec)
-    const int jkey = jk0 + key_local;
-    const bool need_mask = jk0 + wave * 32 + 31 > jq0;
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int q8 = qs * 32 + u * 16 + hf * 8;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse_s + q8);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse_s + q8 + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dvec_s + q8);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(dvec_s + q8 + 4);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float lq = i < 4 ? l0[i] : l1[i - 4];
-          const float dq = i < 4 ? d0[i] : d1[i - 4];
-          float p = fast_exp2(fmaf(sacc[qs][u * 8 + i], c2, -lq));
-          if (need_mask && jkey > jq0 + q8 + i) p = 0.f;
-          sacc[qs][u * 8 + i] = p;
-          pacc[qs][u * 8 + i] = p * (pacc[qs][u * 8 + i] - dq);
-        }
-      }
-
-    // dV^T += dO^T P, dK^T += Q^T dS (A operands through transposing reads)
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const bf16x8 pf = pack8<bf16>(sacc[kc >> 1], (kc & 1) * 8);
-      const bf16x8 sf = pack8<bf16>(pacc[kc >> 1], (kc & 1) * 8);
-      const int r0 = kc * 16 + hf * 8 + ts, r1 = r0 + 4;
-#pragma unroll
-      for (int dt = 0; dt < S::kDT; ++dt) {
-        const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
-        const int o0 = (r0 * CPR + ((dbase >> 3) ^ swz2<CPR>(r0))) * 8 + (dbase & 7);
-        const int o1 = (r1 * CPR + ((dbase >> 3) ^ swz2<CPR>(r1))) * 8 + (dbase & 7);
-        mma32(dvacc[dt], tr_read8(dOs + o0, dOs + o1), pf);
-        mma32(dkacc[dt], tr_read8(Qs + o0, Qs + o1), sf);
-      }
-    }
-
-    if (!has_next) break;
-    hh = nhh; qt = nqt; sig = nsig; jk0 = njk0; qt_b = nqt_b; qt_e = nqt_e;
+    __syncthreads();                                  // this stage landed for all; the other is free
+    if (more) issue_step(nhh, nqt, nsig, STG ^ 1);
+    step(stg_c, jk0, qt);
+    hh = nhh; qt = nqt; sig = nsig; jk0 = njk0; qt_b = nqb; qt_e = nqe;
+    return more;
+  };
+  while (one(std::integral_constant<int, 0>()) && one(std::integral_constant<int, 1>())) {
   }
 
-  bf16* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
-  bf16* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
+  // ---- sum the two query halves' partials, store dK (scaled) and dV at the original key rows
+  __syncthreads();                                    // all tiles are dead: reuse LDS
+  float* xs = reinterpret_cast<float*>(lds) + (size_t)kg * 2 * S::kDT * 16 * 64;
+  if (qh == 1) {
 #pragma unroll
-  for (int dt = 0; dt < S::kDT; ++dt)
+    for (int dt = 0; dt < S::kDT; ++dt)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      *reinterpret_cast<bf16x8*>(dkrow + dt * 32 + u * 16 + hf * 8) = scale8<bf16>(dkacc[dt], u * 8, scale);
-      *reinterpret_cast<bf16x8*>(dvrow + dt * 32 + u * 16 + hf * 8) = pack8<bf16>(dvacc[dt], u * 8);
-    }
+      for (int i = 0; i < 16; ++i) {
+        xs[((0 * S::kDT + dt) * 16 + i) * 64 + lane] = dkacc[dt][i];
+        xs[((1 * S::kDT + dt) * 16 + i) * 64 + lane] = dvacc[dt][i];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dkacc[dt][i] += xs[((0 * S::kDT + dt) * 16 + i) * 64 + lane];
+        dvacc[dt][i] += xs[((1 * S::kDT + dt) * 16 + i) * 64 + lane];
+      }
+    const int tk = orig_row(j0 + key_row, sig0, N);
+    bf16* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
+    bf16* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
+#pragma unroll
+    for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        *reinterpret_cast<bf16x8*>(dkrow + dt * 32 + u * 16 + hf * 8) = scale8<bf16>(dkacc[dt], u * 8, scale);
+        *reinterpret_cast<bf16x8*>(dvrow + dt * 32 + u * 16 + hf * 8) = pack8<bf16>(dvacc[dt], u * 8);
+      }
+  }
 }
-
 // ---------------------------------------------------------------------------
 // dq, bf16: 8 waves x 32 queries (two waves per SIMD), 64-row key / value tiles
 // double-buffered in LDS.  Per tile: S^T = K Q^T and dP^T = V dO^T (queries
