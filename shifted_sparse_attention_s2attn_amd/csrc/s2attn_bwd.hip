@@ -698,7 +698,9 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     bf16* __restrict__ dq, int N, int H, int Hkv, int G, int shift_heads, float scale) {
   using S = DqB16Shape<D>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTile;
+  constexpr int RB = D * 2, TILE_B = TC * 16, STAGE_B = 2 * TILE_B;
   __shared__ bf16x8 smem[2 * 2 * TC];             // [stage][K, V][chunk]
+  char* lds = reinterpret_cast<char*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -745,15 +747,29 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   }
   auto issue_tile = [&](int kt0, int stage) {
     const size_t t0 = (size_t)orig_row(kt0, sigma, N) * kvstride;
-    bf16x8* ks = smem + (2 * stage) * TC;
-    bf16x8* vs = ks + TC;
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
-      const int cb = (wave + S::kWaves * i) * 64;
-      load_lds16(kb + t0 + toff[i], ks + cb);
-      load_lds16(vb + t0 + toff[i], vs + cb);
+      const int cb = (wave + S::kWaves * i) * 64 * 16;
+      load_lds16(kb + t0 + toff[i], lds + stage * STAGE_B + cb);
+      load_lds16(vb + t0 + toff[i], lds + stage * STAGE_B + TILE_B + cb);
     }
   };
+
+  // per-lane LDS byte offsets: K / V A-operand rows perm32(l32) (+32 for the
+  // second half of the tile); K^T transposing reads, rows 8hf + 4t + ts (+16 kc)
+  const int krow = perm32(l32);
+  int offA[S::kDC];
+#pragma unroll
+  for (int cc = 0; cc < S::kDC; ++cc) offA[cc] = krow * RB + (((2 * cc + hf) ^ swz2<CPR>(krow)) << 4);
+  int offT[S::kDT][2];
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = hf * 8 + 4 * t + ts;        // + 16 kc: swz2 only sees row bits 0..3
+      const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
+      offT[dt][t] = row * RB + (((dbase >> 3) ^ swz2<CPR>(row)) << 4) + (dbase & 7) * 2;
+    }
 
   f32x16 dqacc[S::kDT];
 #pragma unroll
@@ -761,59 +777,64 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[dt][r] = 0.f;
   const float c2 = scale * kLog2e;
-  const int krow = perm32(l32);
-  const int ksw = swz2<CPR>(krow);               // same for krow + 32
 
-  issue_tile(kv_begin, 0);
-  for (int it = 0; it < ntiles; ++it) {
-    const int kt0 = kv_begin + it * BC;
-    wait_vmem_all();
-    __syncthreads();
-    if (it + 1 < ntiles) issue_tile(kt0 + BC, (it + 1) & 1);
-    if (kt0 > jw + 31) continue;
-
-    const bf16* Ks = reinterpret_cast<const bf16*>(smem + (2 * (it & 1)) * TC);
-    const bf16* Vs = Ks + TC * 8;
-
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { s[ks][r] = 0.f; dp[ks][r] = 0.f; }
-      const int row = ks * 32 + krow;
-#pragma unroll
-      for (int cc = 0; cc < S::kDC; ++cc) {
-        const int off = (row * CPR + ((2 * cc + hf) ^ ksw)) * 8;
-        mma32(s[ks], *reinterpret_cast<const bf16x8*>(Ks + off), qf[cc]);
-        mma32(dp[ks], *reinterpret_cast<const bf16x8*>(Vs + off), dof[cc]);
-      }
-    }
-    const bool need_mask = kt0 + BC - 1 > jw;
+  auto compute = [&](auto stg_c, auto mask_c, int kt0) {
+    constexpr int STG = decltype(stg_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    const char* Ks = lds + STG * STAGE_B;
+    const char* Vs = Ks + TILE_B;
     bf16x8 sf[4];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      f32x8 dsv;
+    for (int ks = 0; ks < 2; ++ks) {             // one 32-key half at a time keeps S, dP small
+      f32x16 s, dp;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int rr = (kc & 1) * 8 + i;
-        float p = fast_exp2(fmaf(s[kc >> 1][rr], c2, -lse_q));
-        if (need_mask && kt0 + kc * 16 + hf * 8 + i > jq) p = 0.f;
-        dsv[i] = p * (dp[kc >> 1][rr] - dvec_q);
+      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+      for (int cc = 0; cc < S::kDC; ++cc) {
+        mma32(s, *reinterpret_cast<const bf16x8*>(Ks + offA[cc] + ks * 32 * RB), qf[cc]);
+        mma32(dp, *reinterpret_cast<const bf16x8*>(Vs + offA[cc] + ks * 32 * RB), dof[cc]);
       }
-      sf[kc] = __builtin_convertvector(dsv, bf16x8);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x8 dsv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float p = fast_exp2(fmaf(s[u * 8 + i], c2, -lse_q));
+          if (MASK && kt0 + ks * 32 + u * 16 + hf * 8 + i > jq) p = 0.f;
+          dsv[i] = p * (dp[u * 8 + i] - dvec_q);
+        }
+        sf[2 * ks + u] = __builtin_convertvector(dsv, bf16x8);
+      }
     }
     // dQ^T += K^T dS^T
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int r0 = kc * 16 + hf * 8 + ts, r1 = r0 + 4;
+    for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int dt = 0; dt < S::kDT; ++dt) {
-        const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
-        const bf16* p0 = Ks + (r0 * CPR + ((dbase >> 3) ^ swz2<CPR>(r0))) * 8 + (dbase & 7);
-        const bf16* p1 = Ks + (r1 * CPR + ((dbase >> 3) ^ swz2<CPR>(r1))) * 8 + (dbase & 7);
-        mma32(dqacc[dt], tr_read8(p0, p1), sf[kc]);
+        const char* p0 = Ks + offT[dt][0] + kc * 16 * RB;
+        const char* p1 = Ks + offT[dt][1] + kc * 16 * RB;
+        mma32(dqacc[dt], tr_read8(reinterpret_cast<const bf16*>(p0), reinterpret_cast<const bf16*>(p1)), sf[kc]);
       }
-    }
+  };
+  auto tile = [&](auto stg_c, int it) {
+    constexpr int STG = decltype(stg_c)::value;
+    const int kt0 = kv_begin + it * BC;
+    wait_vmem_all();
+    __syncthreads();
+    if (it + 1 < ntiles) issue_tile(kt0 + BC, STG ^ 1);
+    if (kt0 > jw + 31) return;
+    if (kt0 + BC - 1 > jw)
+      compute(stg_c, std::integral_constant<bool, true>(), kt0);
+    else
+      compute(stg_c, std::integral_constant<bool, false>(), kt0);
+  };
+
+  issue_tile(kv_begin, 0);
+  for (int it = 0;;) {
+    tile(std::integral_constant<int, 0>(), it);
+    if (++it == ntiles) break;
+    tile(std::integral_constant<int, 1>(), it);
+    if (++it == ntiles) break;
   }
 
   bf16* dqrow = dq + ((size_t)b * N + tq) * qstride + (size_t)h * D;

@@ -20,6 +20,8 @@
 // Finally O = O^T / l is stored at the original rows with lse = m + ln l.
 #include "s2attn_common.h"
 
+#include <type_traits>
+
 namespace s2a {
 
 template <typename T, int D>
@@ -253,11 +255,15 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     int N, int H, int Hkv, int G, int shift_heads, float scale) {
   using S = FwdB16Shape<D>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTileChunks;
+  constexpr int RB = D * 2;                       // bytes per tile row
+  constexpr int TILE_B = TC * 16, STAGE_B = 2 * TILE_B;
   __shared__ bf16x8 smem[2 * 2 * TC];             // [stage][K, V][chunk]
+  char* lds = reinterpret_cast<char*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
+  const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
 
   const int groups = N / G, tiles_per_group = G / BR;
   const int x = blockIdx.x;
@@ -296,19 +302,27 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   }
   auto issue_tile = [&](int kt0, int stage) {
     const size_t t0 = (size_t)orig_row(kt0, sigma, N) * kvstride;   // whole tile is contiguous
-    bf16x8* ks = smem + (2 * stage) * TC;
-    bf16x8* vs = ks + TC;
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
-      const int cbase = (wave + S::kWaves * i) * 64;
-      load_lds16(kb + t0 + koff[i], ks + cbase);
-      load_lds16(vb + t0 + voff[i], vs + cbase);
+      const int cb = (wave + S::kWaves * i) * 64 * 16;
+      load_lds16(kb + t0 + koff[i], lds + stage * STAGE_B + cb);
+      load_lds16(vb + t0 + voff[i], lds + stage * STAGE_B + TILE_B + cb);
     }
   };
 
-  // per-lane LDS element offsets of the K A-operand and V^T transpose reads
-  const int krow0 = perm32(l32);
-  const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
+  // per-lane LDS byte offsets: K A-operand rows perm32(l32) (+32 rows for the
+  // second 32-key half), V^T transposing reads (rows 8hf + 4t + ts (+16 kc))
+  const int krow = perm32(l32);
+  int offK[S::kDC];
+#pragma unroll
+  for (int cc = 0; cc < S::kDC; ++cc) offK[cc] = krow * RB + (((2 * cc + hf) ^ swz_k<CPR>(krow)) << 4);
+  int offV[S::kDT];
+#pragma unroll
+  for (int dt = 0; dt < S::kDT; ++dt) {
+    const int row = hf * 8 + ts;                  // + 4t + 16kc: swz_v only sees row & 3 and bit 1
+    const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
+    offV[dt] = TILE_B + row * RB + (((dbase >> 3) ^ swz_v<CPR>(row)) << 4) + (dbase & 7) * 2;
+  }
 
   f32x16 oacc[S::kDT];
 #pragma unroll
@@ -318,16 +332,10 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = scale * kLog2e;
 
-  issue_tile(kv_begin, 0);
-  for (int it = 0; it < ntiles; ++it) {
-    const int kt0 = kv_begin + it * BC;
-    wait_vmem_all();                             // this lane's tile loads have landed
-    __syncthreads();                             // ... and everyone's; the other stage is free
-    if (it + 1 < ntiles) issue_tile(kt0 + BC, (it + 1) & 1);
-    if (kt0 > jw + 31) continue;                 // tile entirely after this wave's queries
-
-    const bf16* Ks = reinterpret_cast<const bf16*>(smem + (2 * (it & 1)) * TC);
-    const bf16* Vs = Ks + TC * 8;
+  auto compute = [&](auto stg_c, auto mask_c, int kt0) {
+    constexpr int STG = decltype(stg_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    const char* st = lds + STG * STAGE_B;
 
     // S^T = K Q^T
     f32x16 s[2];
@@ -335,17 +343,11 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[ks][r] = 0.f;
-      const int row = ks * 32 + krow0;
-      const int sw = swz_k<CPR>(row);
 #pragma unroll
-      for (int cc = 0; cc < S::kDC; ++cc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (row * CPR + ((2 * cc + hf) ^ sw)) * 8);
-        mma32(s[ks], a, qf[cc]);
-      }
+      for (int cc = 0; cc < S::kDC; ++cc)
+        mma32(s[ks], *reinterpret_cast<const bf16x8*>(st + offK[cc] + ks * 32 * RB), qf[cc]);
     }
-
-    // causal mask on the diagonal tile, running max with lazy rescale
-    if (kt0 + BC - 1 > jw) {
+    if (MASK) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -384,17 +386,33 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int dt = 0; dt < S::kDT; ++dt) {
-        const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
-        const int r0 = kc * 16 + hf * 8 + ts;
-        const int r1 = r0 + 4;
-        const bf16* p0 = Vs + (r0 * CPR + ((dbase >> 3) ^ swz_v<CPR>(r0))) * 8 + (dbase & 7);
-        const bf16* p1 = Vs + (r1 * CPR + ((dbase >> 3) ^ swz_v<CPR>(r1))) * 8 + (dbase & 7);
-        mma32(oacc[dt], tr_read8(p0, p1), pf[kc]);
+        const char* p0 = st + offV[dt] + kc * 16 * RB;
+        mma32(oacc[dt], tr_read8(reinterpret_cast<const bf16*>(p0), reinterpret_cast<const bf16*>(p0 + 4 * RB)),
+              pf[kc]);
       }
-    }
+  };
+  auto tile = [&](auto stg_c, int it) {
+    constexpr int STG = decltype(stg_c)::value;
+    const int kt0 = kv_begin + it * BC;
+    wait_vmem_all();                             // this lane's tile loads have landed
+    __syncthreads();                             // ... and everyone's; the other stage is free
+    if (it + 1 < ntiles) issue_tile(kt0 + BC, STG ^ 1);
+    if (kt0 > jw + 31) return;                   // tile entirely after this wave's queries
+    if (kt0 + BC - 1 > jw)
+      compute(stg_c, std::integral_constant<bool, true>(), kt0);
+    else
+      compute(stg_c, std::integral_constant<bool, false>(), kt0);
+  };
+
+  issue_tile(kv_begin, 0);
+  for (int it = 0;;) {
+    tile(std::integral_constant<int, 0>(), it);
+    if (++it == ntiles) break;
+    tile(std::integral_constant<int, 1>(), it);
+    if (++it == ntiles) break;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
