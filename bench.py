@@ -229,7 +229,7 @@ def main():
         src = torch.empty(args.hbm_copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.add(src, 1.0, out=dst)            # one elementwise kernel: reads and writes N bytes
         torch.cuda.synchronize()
         result["hbm_copy_bytes"] = src.numel() * 4
         del src, dst

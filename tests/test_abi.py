@@ -109,3 +109,24 @@ def test_product_path_has_no_oracle_or_fallback():
             src = open(os.path.join(pkg, name)).read()
             assert not re.search(r"^\s*(from|import)\s+oracle|s2attn_oracle", src, flags=re.M), name
             assert "scaled_dot_product_attention" not in src, name
+
+
+def test_bwd_stage_entry_points_validate(lib):
+    p = GOOD
+    need = lib.s2attn_bwd_workspace_bytes(p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"], 0)
+    dims = [p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"], 0, None]
+    bad_n = list(dims)
+    bad_n[3] = 500
+    # prep(o, lse, dO, ws, bytes, ...)
+    assert lib.s2attn_bwd_prep(DUMMY, None, DUMMY, DUMMY, need, *dims) == _lib.S2ATTN_ERR_NULL
+    assert lib.s2attn_bwd_prep(DUMMY, FDUMMY, DUMMY, DUMMY, need - 4, *dims) == _lib.S2ATTN_ERR_WORKSPACE
+    assert lib.s2attn_bwd_prep(DUMMY, FDUMMY, DUMMY, DUMMY, need, *bad_n) == _lib.S2ATTN_ERR_SHAPE
+    # dkdv(q, k, v, dO, dk, dv, ws, bytes, ...)
+    assert lib.s2attn_bwd_dkdv(DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY, DUMMY, need, *dims) == _lib.S2ATTN_ERR_NULL
+    assert lib.s2attn_bwd_dkdv(*([DUMMY] * 7), need, *bad_n) == _lib.S2ATTN_ERR_SHAPE
+    assert lib.s2attn_bwd_dkdv(*([DUMMY] * 6), None, need, *dims) == _lib.S2ATTN_ERR_WORKSPACE
+    # dq(q, k, v, dO, dq, ws, bytes, ...)
+    assert lib.s2attn_bwd_dq(DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY, need, *dims) == _lib.S2ATTN_ERR_NULL
+    d96 = list(dims)
+    d96[4] = 96
+    assert lib.s2attn_bwd_dq(*([DUMMY] * 6), need, *d96) == _lib.S2ATTN_ERR_UNSUPPORTED
