@@ -125,6 +125,22 @@ __device__ __forceinline__ void buffer_atomic_add(float x, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(x, r, voff, soff, 0);
 }
 
+// max of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the two
+// 32-lane halves without a trip through LDS)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                   __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                   __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
+}
+
+// Wave index as a wave-uniform (scalar) value, so branches on it are scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 __device__ __forceinline__ float dot2_bf16_acc(bf16 a, bf16 b, float acc) {

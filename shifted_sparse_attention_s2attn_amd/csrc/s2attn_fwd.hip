@@ -361,7 +361,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[ks][r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = max_halves(mloc);
     if (wave_any((mloc - m_run) * c2 > 8.f)) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = fast_exp2((m_run - m_new) * c2);
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     if (++it == ntiles) break;
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   const float inv = 1.f / l_tot;
   bf16* orow = o + ((size_t)b * N + tq) * qstride + (size_t)h * D;
 #pragma unroll
