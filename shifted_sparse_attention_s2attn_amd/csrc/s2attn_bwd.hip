@@ -698,9 +698,12 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     bf16* __restrict__ dq, int N, int H, int Hkv, int G, int shift_heads, float scale) {
   using S = DqB16Shape<D>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTile;
-  constexpr int RB = D * 2, TILE_B = TC * 16, STAGE_B = 2 * TILE_B;
-  __shared__ bf16x8 smem[2 * 2 * TC];             // [stage][K, V][chunk]
-  char* lds = reinterpret_cast<char*>(smem);
+  constexpr int RB = D * 2;
+  // one LDS object per (stage, tensor), so reads of one stage are not made to
+  // wait for the direct-to-LDS loads in flight into the other
+  __shared__ bf16x8 k_st0[TC], v_st0[TC], k_st1[TC], v_st1[TC];
+  auto kbuf = [&](int st) { return reinterpret_cast<char*>(st ? k_st1 : k_st0); };
+  auto vbuf = [&](int st) { return reinterpret_cast<char*>(st ? v_st1 : v_st0); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -747,11 +750,13 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   }
   auto issue_tile = [&](int kt0, int stage) {
     const size_t t0 = (size_t)orig_row(kt0, sigma, N) * kvstride;
+    char* kd = kbuf(stage);
+    char* vd = vbuf(stage);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
-      load_lds16(kb + t0 + toff[i], lds + stage * STAGE_B + cb);
-      load_lds16(vb + t0 + toff[i], lds + stage * STAGE_B + TILE_B + cb);
+      load_lds16(kb + t0 + toff[i], kd + cb);
+      load_lds16(vb + t0 + toff[i], vd + cb);
     }
   };
 
@@ -781,8 +786,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   auto compute = [&](auto stg_c, auto mask_c, int kt0) {
     constexpr int STG = decltype(stg_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
-    const char* Ks = lds + STG * STAGE_B;
-    const char* Vs = Ks + TILE_B;
+    const char* Ks = kbuf(STG);
+    const char* Vs = vbuf(STG);
     bf16x8 sf[4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {             // one 32-key half at a time keeps S, dP small

@@ -115,6 +115,14 @@ __device__ __forceinline__ void load_lds4(const void* gptr, void* lds_base) {
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Raw buffer resource over [base, base + nbytes) and an fp32 atomic add into it
 // at byte offset voff (per lane) + soff (wave-uniform, kept in a scalar
 // register).  Offsets past nbytes are dropped by the hardware range check.

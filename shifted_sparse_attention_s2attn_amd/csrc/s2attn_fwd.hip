@@ -256,9 +256,12 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   using S = FwdB16Shape<D>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTileChunks;
   constexpr int RB = D * 2;                       // bytes per tile row
-  constexpr int TILE_B = TC * 16, STAGE_B = 2 * TILE_B;
-  __shared__ bf16x8 smem[2 * 2 * TC];             // [stage][K, V][chunk]
-  char* lds = reinterpret_cast<char*>(smem);
+  // one LDS object per (stage, tensor): the compiler then sees that reads of one
+  // stage do not alias the direct-to-LDS loads in flight into the other, and
+  // does not wait for those loads before reading
+  __shared__ bf16x8 k_st0[TC], v_st0[TC], k_st1[TC], v_st1[TC];
+  auto kbuf = [&](int st) { return reinterpret_cast<char*>(st ? k_st1 : k_st0); };
+  auto vbuf = [&](int st) { return reinterpret_cast<char*>(st ? v_st1 : v_st0); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -302,11 +305,13 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   }
   auto issue_tile = [&](int kt0, int stage) {
     const size_t t0 = (size_t)orig_row(kt0, sigma, N) * kvstride;   // whole tile is contiguous
+    char* kd = kbuf(stage);
+    char* vd = vbuf(stage);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
-      load_lds16(kb + t0 + koff[i], lds + stage * STAGE_B + cb);
-      load_lds16(vb + t0 + voff[i], lds + stage * STAGE_B + TILE_B + cb);
+      load_lds16(kb + t0 + koff[i], kd + cb);
+      load_lds16(vb + t0 + voff[i], vd + cb);
     }
   };
 
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   for (int dt = 0; dt < S::kDT; ++dt) {
     const int row = hf * 8 + ts;                  // + 4t + 16kc: swz_v only sees row & 3 and bit 1
     const int dbase = dt * 32 + perm32(((g16 & 1) << 4) + 4 * tm);
-    offV[dt] = TILE_B + row * RB + (((dbase >> 3) ^ swz_v<CPR>(row)) << 4) + (dbase & 7) * 2;
+    offV[dt] = row * RB + (((dbase >> 3) ^ swz_v<CPR>(row)) << 4) + (dbase & 7) * 2;
   }
 
   f32x16 oacc[S::kDT];
@@ -335,7 +340,8 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   auto compute = [&](auto stg_c, auto mask_c, int kt0) {
     constexpr int STG = decltype(stg_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
-    const char* st = lds + STG * STAGE_B;
+    const char* st = kbuf(STG);
+    const char* vst = vbuf(STG);
 
     // S^T = K Q^T
     f32x16 s[2];
@@ -389,7 +395,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int dt = 0; dt < S::kDT; ++dt) {
-        const char* p0 = st + offV[dt] + kc * 16 * RB;
+        const char* p0 = vst + offV[dt] + kc * 16 * RB;
         mma32(oacc[dt], tr_read8(reinterpret_cast<const bf16*>(p0), reinterpret_cast<const bf16*>(p0 + 4 * RB)),
               pf[kc]);
       }
