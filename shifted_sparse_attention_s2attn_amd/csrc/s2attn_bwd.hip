@@ -119,10 +119,10 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   const int l32 = lane & 31, hf = lane >> 5;
 
   // Key tiles at the start of a group meet the most queries: dispatched first.
-  const int groups = N / G;
-  const int x = blockIdx.x;
-  const int pos = x / groups, grp = x % groups;
-  const int c = blockIdx.y, b = blockIdx.z;
+  const int groups = N / G, tiles_per_group = G / BKV;
+  const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
+  const int pos = to.rank, grp = to.pair % groups;
+  const int c = (to.pair / groups) % Hkv, b = to.pair / (groups * Hkv);
   const int r = H / Hkv;
   const int h0 = c * r;
   const int sig0 = (h0 >= H - shift_heads) ? G / 2 : 0;
@@ -287,10 +287,10 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   const int l32 = lane & 31, hf = lane >> 5;
 
   const int groups = N / G, tiles_per_group = G / BR;
-  const int x = blockIdx.x;
-  const int pos = tiles_per_group - 1 - x / groups;   // heaviest query tiles first
-  const int grp = x % groups;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
+  const int pos = tiles_per_group - 1 - to.rank;   // heaviest query tiles first
+  const int grp = to.pair % groups;
+  const int h = (to.pair / groups) % H, b = to.pair / (groups * H);
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
   const int j0 = grp * G + pos * BR;
@@ -469,10 +469,10 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
   const int kg = wave & 3, qh = wave >> 2;
 
-  const int groups = N / G;
-  const int x = blockIdx.x;
-  const int pos = x / groups, grp = x % groups;       // key tiles early in a group first
-  const int c = blockIdx.y, b = blockIdx.z;
+  const int groups = N / G, tiles_per_group = G / BKV;
+  const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
+  const int pos = to.rank, grp = to.pair % groups;       // key tiles early in a group first
+  const int c = (to.pair / groups) % Hkv, b = to.pair / (groups * Hkv);
   const int r = H / Hkv;
   const int h0 = c * r;
   const int sig0 = (h0 >= H - shift_heads) ? G / 2 : 0;
@@ -711,10 +711,10 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
 
   const int groups = N / G, tiles_per_group = G / BR;
-  const int x = blockIdx.x;
-  const int pos = tiles_per_group - 1 - x / groups;
-  const int grp = x % groups;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
+  const int pos = tiles_per_group - 1 - to.rank;
+  const int grp = to.pair % groups;
+  const int h = (to.pair / groups) % H, b = to.pair / (groups * H);
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
   const int j0 = grp * G + pos * BR;
@@ -880,7 +880,7 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
   static bool attr = false;
   hipError_t e = raise_lds_limit(&s2attn_bwd_dkdv_bf16<D>, S::kLdsBytes, attr);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D>), dim3(N / S::kBKV, Hkv, B), dim3(S::kThreads), S::kLdsBytes,
+  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D>), dim3(B * Hkv * (N / S::kBKV)), dim3(S::kThreads), S::kLdsBytes,
                      stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec,
                      (bf16*)dk, (bf16*)dv, N, H, Hkv, G, shift_heads, scale);
   return hipGetLastError();
@@ -894,7 +894,7 @@ hipError_t launch_dkdv_generic(const void* q, const void* k, const void* v, cons
   static bool attr = false;
   hipError_t e = raise_lds_limit(&s2attn_bwd_dkdv<T, D>, S::kLdsBytes, attr);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), dim3(N / S::kBKV, Hkv, B), dim3(S::kThreads), S::kLdsBytes,
+  hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), dim3(B * Hkv * (N / S::kBKV)), dim3(S::kThreads), S::kLdsBytes,
                      stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dk, (T*)dv, N,
                      H, Hkv, G, shift_heads, scale);
   return hipGetLastError();
@@ -917,7 +917,7 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
                           const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
                           float scale, hipStream_t stream) {
   using S = DqB16Shape<D>;
-  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D>), dim3(N / S::kBR, H, B), dim3(S::kThreads), 0, stream,
+  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D>), dim3(B * H * (N / S::kBR)), dim3(S::kThreads), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dq, N, H,
                      Hkv, G, shift_heads, scale);
   return hipGetLastError();
@@ -931,7 +931,7 @@ hipError_t launch_dq_generic(const void* q, const void* k, const void* v, const 
   static bool attr = false;
   hipError_t e = raise_lds_limit(&s2attn_bwd_dq<T, D>, S::kLdsBytes, attr);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((s2attn_bwd_dq<T, D>), dim3(N / S::kBR, H, B), dim3(S::kThreads), S::kLdsBytes, stream,
+  hipLaunchKernelGGL((s2attn_bwd_dq<T, D>), dim3(B * H * (N / S::kBR)), dim3(S::kThreads), S::kLdsBytes, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dq, N, H, Hkv, G,
                      shift_heads, scale);
   return hipGetLastError();

@@ -149,6 +149,25 @@ __device__ __forceinline__ float sum_halves(float x) {
 // Wave index as a wave-uniform (scalar) value, so branches on it are scalar.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Block numbering shared by the attention kernels.  A launch covers `pairs`
+// (batch, head, group) pairs times `ranks` tiles per pair, rank 0 being the
+// tile with the most work.  Blocks are numbered chunk by chunk, kPairChunk
+// pairs per chunk, rank-major inside a chunk: a chunk's heavy tiles start
+// first and its light ones fill the tail of the launch.  Round-robin dispatch
+// over the 8 XCDs then places every block of one pair of a full chunk on the
+// same XCD (kPairChunk is a multiple of 8), close together in time, so the
+// pair's K/V tiles are reused from that XCD's L2.
+constexpr int kPairChunk = 32;
+struct TileOrder { int pair, rank; };
+__device__ __forceinline__ TileOrder tile_order(int idx, int pairs, int ranks) {
+  const int per_chunk = kPairChunk * ranks;
+  const int chunk = idx / per_chunk;
+  const int first = chunk * kPairChunk;
+  const int n = min(kPairChunk, pairs - first);
+  const int rem = idx - chunk * per_chunk;
+  return {first + rem % n, rem / n};
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 __device__ __forceinline__ float dot2_bf16_acc(bf16 a, bf16 b, float acc) {

@@ -58,10 +58,10 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
 
   // Heaviest query tiles (last in their group) are dispatched first.
   const int groups = N / G, tiles_per_group = G / BR;
-  const int x = blockIdx.x;
-  const int pos = tiles_per_group - 1 - x / groups;
-  const int grp = x % groups;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
+  const int pos = tiles_per_group - 1 - to.rank;
+  const int grp = to.pair % groups;
+  const int h = (to.pair / groups) % H, b = to.pair / (groups * H);
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
 
@@ -269,10 +269,10 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
 
   const int groups = N / G, tiles_per_group = G / BR;
-  const int x = blockIdx.x;
-  const int pos = tiles_per_group - 1 - x / groups;   // heaviest query tiles first
-  const int grp = x % groups;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
+  const int pos = tiles_per_group - 1 - to.rank;     // heaviest query tiles first
+  const int grp = to.pair % groups;
+  const int h = (to.pair / groups) % H, b = to.pair / (groups * H);
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
   const int j0 = grp * G + pos * BR;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
 template <int D>
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Hkv, int N, int G, int shift_heads, float scale, hipStream_t stream) {
-  dim3 grid(N / FwdB16Shape<D>::kBR, H, B);
+  dim3 grid(B * H * (N / FwdB16Shape<D>::kBR));
   hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D>), grid, dim3(FwdB16Shape<D>::kThreads), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads, scale);
   return hipGetLastError();
@@ -449,7 +449,7 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
     if (G % FwdB16Shape<D>::kBR == 0)
       return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, scale, stream);
   }
-  dim3 grid(N / FwdShape<T, D>::kBR, H, B);
+  dim3 grid(B * H * (N / FwdShape<T, D>::kBR));
   hipLaunchKernelGGL((s2attn_fwd_kernel<T, D>), grid, dim3(256), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, scale);
   return hipGetLastError();
