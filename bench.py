@@ -9,8 +9,10 @@ then K steps between two device synchronisations; the wall time of those K
 steps gives ``value`` (effective TFLOP/s: group-local causal pairs only, 4d
 FLOP per pair forward, 10d backward).  HIP events recorded on the launch
 stream around every kernel launch give each kernel's average duration; the
-longest one is the roofline kernel.  Afterwards the float64 CPU oracle is
-timed on a bounded sample of the same workload (rank 0, one GPU only).
+longest one is the roofline kernel.  Afterwards a vendor bf16 GEMM on
+standard-normal operands is timed as the practical matrix-core ceiling for
+data of this distribution, and the float64 CPU oracle is timed on a bounded
+sample of the same workload (rank 0, one GPU only).
 
 Prints one JSON line.
 """
@@ -105,6 +107,30 @@ def cpu_baseline(w, t, seconds):
     }
 
 
+def gemm_reference(torch, dev, n=16384, reps=5):
+    """A vendor bf16 GEMM (torch.matmul, i.e. hipBLASLt) of n x n x n on seeded
+    standard-normal operands: the rate a tuned dense contraction sustains on this
+    chip with data of the inputs' distribution.  The matrix cores' throughput
+    depends on the operand bits (the clock drops under random data), so this,
+    not the nominal peak, is the practical ceiling of an MFMA-bound kernel."""
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn((n, n), generator=g, device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device=dev, dtype=torch.bfloat16)
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return {"tflops": round(2 * n ** 3 / ms / 1e9, 1), "ms": round(ms, 4), "shape": f"{n}x{n}x{n}",
+            "operands": "bf16, seeded standard normal", "library": "torch.matmul (hipBLASLt)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +139,7 @@ def main():
     ap.add_argument("--workload", default="llama2-7b-32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-reference", action="store_true")
     ap.add_argument("--hbm-copy-bytes", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many bytes; under "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it calibrates the HBM byte counters")
@@ -233,6 +260,12 @@ def main():
         torch.cuda.synchronize()
         result["hbm_copy_bytes"] = src.numel() * 4
         del src, dst
+    if w.dtype == "bf16" and not args.no_gemm_reference:
+        ref = gemm_reference(torch, dev)
+        ref["fwd_frac"] = round(fwd_f / fwd_ms / 1e9 / ref["tflops"], 4)
+        if dominant in kern_flops:
+            ref["roofline_kernel_frac"] = round(roof["achieved"] / ref["tflops"], 4)
+        result["gemm_reference"] = ref
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
     print(json.dumps(result), flush=True)
