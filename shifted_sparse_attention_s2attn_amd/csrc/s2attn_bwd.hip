@@ -431,11 +431,14 @@ struct DkdvB16Shape {
   static constexpr int kRowB = D * 2;                     // bytes per tile row
   static constexpr int kQTileB = kBQ * kRowB;
   static constexpr int kKTileB = kBKV * kRowB;
-  static constexpr int kK = 0;                            // byte offsets
-  static constexpr int kV = kK + kKTileB;
-  static constexpr int kQ = kV + kKTileB;                 // [2 stages]
+  // byte offsets: the per-step Q and dO stages first, so that every read of
+  // them is a per-lane offset plus a 16-bit immediate; the resident K and V
+  // tiles above them share one set of per-lane offsets (V = K + immediate)
+  static constexpr int kQ = 0;                            // [2 stages]
   static constexpr int kdO = kQ + 2 * kQTileB;            // [2 stages]
-  static constexpr int kF = kdO + 2 * kQTileB;            // floats [stage][lse2 | dvec][kBQ]
+  static constexpr int kK = kdO + 2 * kQTileB;
+  static constexpr int kV = kK + kKTileB;
+  static constexpr int kF = kV + kKTileB;                 // floats [stage][lse2 | dvec][kBQ]
   static constexpr size_t kLdsBytes = (size_t)kF + 2 * 2 * kBQ * sizeof(float);
   static constexpr int kDC = D / 16;
   static constexpr int kDT = D / 32;
@@ -460,7 +463,9 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     bf16* __restrict__ dk, bf16* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, float scale) {
   using S = DkdvB16Shape<D>;
   constexpr int BKV = S::kBKV, BQ = S::kBQ, CPR = S::kCPR, RB = S::kRowB;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+  // static, so that tile addresses are compile-time constants and every LDS
+  // read is a per-lane offset plus an immediate
+  __shared__ __align__(16) unsigned char smem_raw[S::kLdsBytes];
   char* lds = reinterpret_cast<char*>(smem_raw);
 
   const int tid = threadIdx.x;
@@ -877,11 +882,8 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
                             const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
                             int shift_heads, float scale, hipStream_t stream) {
   using S = DkdvB16Shape<D>;
-  static bool attr = false;
-  hipError_t e = raise_lds_limit(&s2attn_bwd_dkdv_bf16<D>, S::kLdsBytes, attr);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D>), dim3(B * Hkv * (N / S::kBKV)), dim3(S::kThreads), S::kLdsBytes,
-                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec,
+  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D>), dim3(B * Hkv * (N / S::kBKV)), dim3(S::kThreads), 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec,
                      (bf16*)dk, (bf16*)dv, N, H, Hkv, G, shift_heads, scale);
   return hipGetLastError();
 }
