@@ -497,12 +497,18 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     load_lds16(kb + g, lds + S::kK + cb * 16);
     load_lds16(vb + g, lds + S::kV + cb * 16);
   }
+  // Q, dO (this batch) and lse*log2(e), Dvec as buffers: 32-bit byte offsets
+  // (the launcher checks that they fit), per-lane parts fixed here
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(const_cast<bf16*>(q + (size_t)b * N * qstride), (int)((size_t)N * qstride * 2));
+  const __amdgpu_buffer_rsrc_t dors = make_rsrc(const_cast<bf16*>(dO + (size_t)b * N * qstride), (int)((size_t)N * qstride * 2));
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(const_cast<float*>(lse2 + (size_t)b * H * N), H * N * 4);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(const_cast<float*>(dvec + (size_t)b * H * N), H * N * 4);
   int qoff[S::kQLoads];
 #pragma unroll
   for (int i = 0; i < S::kQLoads; ++i) {
     const int p = (wave + S::kWaves * i) * 64 + lane;
     const int row = p / CPR, pc = p % CPR;
-    qoff[i] = row * (int)qstride + (pc ^ swz2<CPR>(row)) * 8;
+    qoff[i] = (row * (int)qstride + (pc ^ swz2<CPR>(row)) * 8) * 2;
   }
 
   // ---- per-lane LDS byte offsets
@@ -527,29 +533,39 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     }
   const int offL = (qh * 32 + hf * 8) * 4;            // lse / Dvec floats of this lane's queries
 
+  // The key tile seen from a query head: only two frames exist (unshifted,
+  // shifted), so they are fixed here: first key row in the head's rolled frame
+  // and the head's query tiles [qt_b, qt_e) of the key tile's group.
+  int fr_jk0[2], fr_qb[2], fr_qe[2];
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh) {
+    int jk = j0 + sig0 - sh * (G / 2);
+    if (jk < 0) jk += N;
+    if (jk >= N) jk -= N;
+    fr_jk0[sh] = jk;
+    fr_qb[sh] = jk / BQ;
+    fr_qe[sh] = (jk / G) * (G / BQ) + G / BQ;
+  }
   auto head_frame = [&](int hh, int& sig, int& jk0, int& qt_b, int& qt_e) {
-    const int h = h0 + hh;
-    sig = (h >= H - shift_heads) ? G / 2 : 0;
-    jk0 = j0 + sig0 - sig;
-    if (jk0 < 0) jk0 += N;
-    if (jk0 >= N) jk0 -= N;
-    qt_b = jk0 / BQ;
-    qt_e = (jk0 / G) * G / BQ + G / BQ;
+    const int sh = h0 + hh >= H - shift_heads;
+    sig = sh ? G / 2 : 0;
+    jk0 = fr_jk0[sh];
+    qt_b = fr_qb[sh];
+    qt_e = fr_qe[sh];
   };
   auto issue_step = [&](int hh, int qt, int sig, int stage) {
     const int h = h0 + hh;
     const int t0 = orig_row(qt * BQ, sig, N);         // a 64-row tile is contiguous
-    const bf16* qg = q + ((size_t)b * N + t0) * qstride + (size_t)h * D;
-    const bf16* dog = dO + ((size_t)b * N + t0) * qstride + (size_t)h * D;
+    const int soff = (t0 * (int)qstride + h * D) * 2;
 #pragma unroll
     for (int i = 0; i < S::kQLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
-      load_lds16(qg + qoff[i], lds + S::kQ + stage * S::kQTileB + cb);
-      load_lds16(dog + qoff[i], lds + S::kdO + stage * S::kQTileB + cb);
+      buffer_load_lds16(qrs, qoff[i], soff, lds + S::kQ + stage * S::kQTileB + cb);
+      buffer_load_lds16(dors, qoff[i], soff, lds + S::kdO + stage * S::kQTileB + cb);
     }
-    const size_t rowbase = ((size_t)b * H + h) * N + t0;
-    if (wave == 0) load_lds4(lse2 + rowbase + lane, lds + S::kF + stage * 2 * BQ * 4);
-    if (wave == 1) load_lds4(dvec + rowbase + lane, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
+    const int loff = (h * N + t0) * 4;
+    if (wave == 0) buffer_load_lds4(lrs, lane * 4, loff, lds + S::kF + stage * 2 * BQ * 4);
+    if (wave == 1) buffer_load_lds4(drs, lane * 4, loff, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
   };
 
   f32x16 dkacc[S::kDT], dvacc[S::kDT];
@@ -907,11 +923,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
                            int shift_heads, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
-  if constexpr (sizeof(T) == 2)
-    return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, scale, stream);
-  else
-    return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, scale,
-                                     stream);
+  if constexpr (sizeof(T) == 2) {
+    // the fast kernel addresses one batch's Q / dO with 31-bit byte offsets
+    if ((size_t)N * H * D * sizeof(T) < (size_t(1) << 31))
+      return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, scale, stream);
+  }
+  return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, scale, stream);
 }
 
 template <int D>

@@ -129,6 +129,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, int nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
 }
+// n bytes per lane (16 or 4) from a buffer straight into LDS: lane i fills
+// bytes [n i, n i + n) after the wave-uniform LDS base, reading resource base
+// + voff (per lane) + soff (wave-uniform) bytes.  The 32-bit offsets keep the
+// address arithmetic in scalar registers.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, voff, soff, 0, 0);
+}
 __device__ __forceinline__ void buffer_atomic_add(float x, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(x, r, voff, soff, 0);
 }
