@@ -762,22 +762,27 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   const float lse_q = lse2[((size_t)b * H + h) * N + tq];
   const float dvec_q = dvec[((size_t)b * H + h) * N + tq];
 
+  // K and V of this (batch, KV head) as buffers (32-bit byte offsets, which
+  // the launcher checks); per-lane byte offsets of the chunks this lane moves
+  const int kvbytes = (int)(((size_t)N * kvstride - (size_t)c * D) * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(const_cast<bf16*>(kb), kvbytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(const_cast<bf16*>(vb), kvbytes);
   int toff[S::kLoads];
 #pragma unroll
   for (int i = 0; i < S::kLoads; ++i) {
     const int p = (wave + S::kWaves * i) * 64 + lane;
     const int row = p / CPR, pc = p % CPR;
-    toff[i] = row * (int)kvstride + (pc ^ swz2<CPR>(row)) * 8;
+    toff[i] = (row * (int)kvstride + (pc ^ swz2<CPR>(row)) * 8) * 2;
   }
   auto issue_tile = [&](int kt0, int stage) {
-    const size_t t0 = (size_t)orig_row(kt0, sigma, N) * kvstride;
+    const int t0 = orig_row(kt0, sigma, N) * (int)kvstride * 2;   // whole tile is contiguous
     char* kd = kbuf(stage);
     char* vd = vbuf(stage);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
-      load_lds16(kb + t0 + toff[i], kd + cb);
-      load_lds16(vb + t0 + toff[i], vd + cb);
+      buffer_load_lds16(krs, toff[i], t0, kd + cb);
+      buffer_load_lds16(vrs, toff[i], t0, vd + cb);
     }
   };
 
@@ -962,7 +967,8 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
-    if (G % DqB16Shape<D>::kBR == 0)
+    // the fast kernel addresses one batch's K / V with 31-bit byte offsets
+    if (G % DqB16Shape<D>::kBR == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
       return launch_dq_bf16<D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, scale, stream);
   }
   return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, scale, stream);

@@ -294,24 +294,28 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     for (int cc = 0; cc < S::kDC; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(qrow + cc * 16 + hf * 8);
   }
 
-  // per-lane global offsets (elements) of the chunks this lane moves into LDS
+  // K and V of this (batch, KV head) as buffers (32-bit byte offsets, which
+  // the launcher checks); per-lane byte offsets of the chunks this lane moves
+  const int kvbytes = (int)(((size_t)N * kvstride - (size_t)c * D) * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(const_cast<bf16*>(kb), kvbytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(const_cast<bf16*>(vb), kvbytes);
   int koff[S::kLoads], voff[S::kLoads];
 #pragma unroll
   for (int i = 0; i < S::kLoads; ++i) {
     const int p = (wave + S::kWaves * i) * 64 + lane;
     const int row = p / CPR, pc = p % CPR;
-    koff[i] = row * (int)kvstride + (pc ^ swz_k<CPR>(row)) * 8;
-    voff[i] = row * (int)kvstride + (pc ^ swz_v<CPR>(row)) * 8;
+    koff[i] = (row * (int)kvstride + (pc ^ swz_k<CPR>(row)) * 8) * 2;
+    voff[i] = (row * (int)kvstride + (pc ^ swz_v<CPR>(row)) * 8) * 2;
   }
   auto issue_tile = [&](int kt0, int stage) {
-    const size_t t0 = (size_t)orig_row(kt0, sigma, N) * kvstride;   // whole tile is contiguous
+    const int t0 = orig_row(kt0, sigma, N) * (int)kvstride * 2;   // whole tile is contiguous
     char* kd = kbuf(stage);
     char* vd = vbuf(stage);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
-      load_lds16(kb + t0 + koff[i], kd + cb);
-      load_lds16(vb + t0 + voff[i], vd + cb);
+      buffer_load_lds16(krs, koff[i], t0, kd + cb);
+      buffer_load_lds16(vrs, voff[i], t0, vd + cb);
     }
   };
 
@@ -446,7 +450,8 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int B, int H, int Hkv, int N, int G, int shift_heads, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
-    if (G % FwdB16Shape<D>::kBR == 0)
+    // the fast kernel addresses one batch's K / V with 31-bit byte offsets
+    if (G % FwdB16Shape<D>::kBR == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
       return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, scale, stream);
   }
   dim3 grid(B * H * (N / FwdShape<T, D>::kBR));
