@@ -590,7 +590,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
       mma32(sacc, lds_b128(Qs, offA[cc]), lds_b128(lds + S::kK, offB[cc]));
       mma32(pacc, lds_b128(dOs, offA[cc]), lds_b128(lds + S::kV, offB[cc]));
     }
-    bf16x8 pf[2], sf[2];
+    // P and dS of each 16-query half, then that half's dV / dK products, so the
+    // second half's vector work can overlap the first half's matrix work
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const f32x4 l0 = lds_f32x4(Fs, offL + u * 64), l1 = lds_f32x4(Fs, offL + u * 64 + 16);
@@ -605,19 +606,17 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
         pv[i] = p;
         sv[i] = p * (pacc[u * 8 + i] - dq);
       }
-      pf[u] = __builtin_convertvector(pv, bf16x8);
-      sf[u] = __builtin_convertvector(sv, bf16x8);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
+      const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
+      const bf16x8 sf = __builtin_convertvector(sv, bf16x8);
 #pragma unroll
       for (int dt = 0; dt < S::kDT; ++dt) {
         const int o0 = offT[dt][0] + u * 16 * RB, o1 = offT[dt][1] + u * 16 * RB;
         mma32(dvacc[dt], tr_read8(reinterpret_cast<const bf16*>(dOs + o0), reinterpret_cast<const bf16*>(dOs + o1)),
-              pf[u]);
+              pf);
         mma32(dkacc[dt], tr_read8(reinterpret_cast<const bf16*>(Qs + o0), reinterpret_cast<const bf16*>(Qs + o1)),
-              sf[u]);
+              sf);
       }
+    }
   };
   auto step = [&](auto stg_c, int jk0, int qt) {
     const int jq0 = qt * BQ;
