@@ -103,29 +103,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // Global memory straight into LDS (no registers): lane i of the wave fills
-// bytes [n i, n i + n) after the wave-uniform LDS base, n = 16 or 4.
+// bytes [16 i, 16 i + 16) after the wave-uniform LDS base.
 // (amdgcn builtins sit in helpers like these, not in kernel bodies, so that
 // the host pass still emits every kernel's launch stub.)
 __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
-__device__ __forceinline__ void load_lds4(const void* gptr, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
-}
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (they complete in issue order), leaving the other counters alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Raw buffer resource over [base, base + nbytes) and an fp32 atomic add into it
-// at byte offset voff (per lane) + soff (wave-uniform, kept in a scalar
-// register).  Offsets past nbytes are dropped by the hardware range check.
+// Raw buffer resource over [base, base + nbytes): loads through it take a
+// 32-bit byte offset, per lane (voff) plus wave-uniform (soff, a scalar
+// register); offsets past nbytes read zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, int nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
 }
@@ -138,9 +127,6 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, int 
 }
 __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void buffer_atomic_add(float x, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(x, r, voff, soff, 0);
 }
 
 // max of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the two
@@ -155,9 +141,6 @@ __device__ __forceinline__ float sum_halves(float x) {
                                                    __builtin_bit_cast(unsigned, x), false, false);
   return __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
 }
-
-// Wave index as a wave-uniform (scalar) value, so branches on it are scalar.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Block numbering shared by the attention kernels.  A launch covers `pairs`
 // (batch, head, group) pairs times `ranks` tiles per pair, rank 0 being the
