@@ -36,7 +36,9 @@
  * to bf16 for the matrix cores) or fp32 (fp32 matrix cores throughout);
  * G a multiple of 128; N a multiple of G; when a key/value head is shared by
  * shifted and unshifted query heads (H - shift_heads not a multiple of
- * H / Hkv), G must also be a multiple of 256.
+ * H / Hkv), G must also be a multiple of 256; B * H * N / 128 < 2^31.
+ * B == 0 or N == 0 is an empty problem: every call validates the other sizes,
+ * then returns S2ATTN_OK without reading any pointer or touching the GPU.
  */
 #ifndef S2ATTN_H
 #define S2ATTN_H
@@ -55,8 +57,10 @@ typedef enum {
 typedef enum {
     S2ATTN_OK = 0,
     S2ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
-    S2ATTN_ERR_SHAPE = 2,        /* a size <= 0, N % G != 0, G odd, shift_heads outside [0, H], H % Hkv != 0 */
-    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype, G % 128 != 0, or the mixed-shift rule above */
+    S2ATTN_ERR_SHAPE = 2,        /* B or N < 0, H, Hkv, d or G <= 0, N % G != 0, G odd,
+                                    shift_heads outside [0, H], H % Hkv != 0 */
+    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype, G % 128 != 0, the mixed-shift rule
+                                    above, or B * H * N / 128 >= 2^31 */
     S2ATTN_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError) */
     S2ATTN_ERR_WORKSPACE = 5     /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
 } s2attn_status;
@@ -74,7 +78,8 @@ int s2attn_fwd(const void* q, const void* k, const void* v,
 /*
  * Bytes of device workspace s2attn_bwd needs: the fp32 row sums
  * Dvec = rowsum(dO * o) [B,H,N] and lse * log2(e) [B,H,N].
- * Returns 0 when the arguments would be rejected by s2attn_bwd.
+ * Returns 0 when the arguments would be rejected by s2attn_bwd, and for an
+ * empty problem (B == 0 or N == 0), which needs no workspace.
  */
 size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G,
                                   int shift_heads, int dtype);

@@ -3,6 +3,8 @@
 // launches nothing.  The library keeps no state besides one flag per kernel
 // instantiation recording that its LDS limit was raised.
 #include "s2attn.h"
+
+#include <stdint.h>
 #include "s2attn_common.h"
 
 namespace s2a {
@@ -23,12 +25,14 @@ namespace {
 
 constexpr int kTileRows = 128;   // query rows per forward workgroup = key rows per backward workgroup
 
+// Sizes only (no pointers).  B == 0 or N == 0 is a valid, empty problem.
 int check_problem(int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype) {
-  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || G <= 0) return S2ATTN_ERR_SHAPE;
+  if (B < 0 || N < 0 || H <= 0 || Hkv <= 0 || d <= 0 || G <= 0) return S2ATTN_ERR_SHAPE;
   if (N % G != 0 || G % 2 != 0) return S2ATTN_ERR_SHAPE;
   if (shift_heads < 0 || shift_heads > H) return S2ATTN_ERR_SHAPE;
   if (H % Hkv != 0) return S2ATTN_ERR_SHAPE;
-  if (B > 65535 || H > 65535) return S2ATTN_ERR_UNSUPPORTED;   // grid y / z limits
+  // one-dimensional grids of (batch, head, 128-row tile) blocks
+  if ((size_t)B * H * (size_t)(N / kTileRows) > (size_t)INT32_MAX) return S2ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return S2ATTN_ERR_UNSUPPORTED;
   if (dtype != S2ATTN_BF16 && dtype != S2ATTN_F32) return S2ATTN_ERR_UNSUPPORTED;
   if (G % kTileRows != 0) return S2ATTN_ERR_UNSUPPORTED;
@@ -40,6 +44,8 @@ int check_problem(int B, int H, int Hkv, int N, int d, int G, int shift_heads, i
   return S2ATTN_OK;
 }
 
+bool empty_problem(int B, int N) { return B == 0 || N == 0; }
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -48,9 +54,10 @@ extern "C" {
 
 int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return S2ATTN_ERR_NULL;
   const int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (st != S2ATTN_OK) return st;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!q || !k || !v || !o || !lse) return S2ATTN_ERR_NULL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == S2ATTN_BF16) {
@@ -125,9 +132,10 @@ extern "C" {
 
 int s2attn_bwd_prep(const void* o, const float* lse, const void* dO, void* workspace, size_t workspace_bytes,
                     int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
-  if (!o || !lse || !dO) return S2ATTN_ERR_NULL;
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (st != S2ATTN_OK) return st;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!o || !lse || !dO) return S2ATTN_ERR_NULL;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
@@ -137,9 +145,10 @@ int s2attn_bwd_prep(const void* o, const float* lse, const void* dO, void* works
 int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes,
                     int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
-  if (!q || !k || !v || !dO || !dk || !dv) return S2ATTN_ERR_NULL;
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (st != S2ATTN_OK) return st;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!q || !k || !v || !dO || !dk || !dv) return S2ATTN_ERR_NULL;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
@@ -150,9 +159,10 @@ int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
 int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq,
                   void* workspace, size_t workspace_bytes,
                   int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
-  if (!q || !k || !v || !dO || !dq) return S2ATTN_ERR_NULL;
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (st != S2ATTN_OK) return st;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!q || !k || !v || !dO || !dq) return S2ATTN_ERR_NULL;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
@@ -163,9 +173,10 @@ int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, v
 int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
                void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
   if (st != S2ATTN_OK) return st;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;

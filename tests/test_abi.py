@@ -59,7 +59,9 @@ def fwd_status(lib, ptrs=True, **kw):
     (dict(S=5), _lib.S2ATTN_ERR_SHAPE),
     (dict(S=-1), _lib.S2ATTN_ERR_SHAPE),
     (dict(Hkv=3), _lib.S2ATTN_ERR_SHAPE),
-    (dict(B=0), _lib.S2ATTN_ERR_SHAPE),
+    (dict(B=-1), _lib.S2ATTN_ERR_SHAPE),
+    (dict(N=-128), _lib.S2ATTN_ERR_SHAPE),
+    (dict(H=0, Hkv=0), _lib.S2ATTN_ERR_SHAPE),
     (dict(d=96), _lib.S2ATTN_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.S2ATTN_ERR_UNSUPPORTED),
     (dict(G=64, N=512), _lib.S2ATTN_ERR_UNSUPPORTED),   # G not a multiple of 128
@@ -71,6 +73,31 @@ def test_fwd_rejects(lib, kw, code):
 
 def test_fwd_null_pointer(lib):
     assert fwd_status(lib, ptrs=False) == _lib.S2ATTN_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(B=0, N=0)])
+def test_empty_problem_is_a_no_op(lib, kw):
+    """B == 0 or N == 0: every entry point validates the other sizes and returns
+    OK without reading a pointer (all NULL here) or calling HIP; no workspace."""
+    p = dict(GOOD)
+    p.update(kw)
+    dims = [p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"], p["dtype"], None]
+    assert fwd_status(lib, ptrs=False, **kw) == _lib.S2ATTN_OK
+    assert lib.s2attn_bwd_workspace_bytes(*dims[:-1]) == 0
+    assert lib.s2attn_bwd(*([None] * 10), 0, *dims) == _lib.S2ATTN_OK
+    assert lib.s2attn_bwd_prep(None, None, None, None, 0, *dims) == _lib.S2ATTN_OK
+    assert lib.s2attn_bwd_dkdv(*([None] * 7), 0, *dims) == _lib.S2ATTN_OK
+    assert lib.s2attn_bwd_dq(*([None] * 6), 0, *dims) == _lib.S2ATTN_OK
+    # the other sizes are still checked
+    assert fwd_status(lib, ptrs=False, d=96, **kw) == _lib.S2ATTN_ERR_UNSUPPORTED
+    assert fwd_status(lib, ptrs=False, S=9, **kw) == _lib.S2ATTN_ERR_SHAPE
+
+
+def test_grid_size_limit(lib):
+    """Grids are one-dimensional over (batch, head, 128-row tile): B and H may be
+    large as long as B * H * N / 128 stays below 2^31."""
+    assert lib.s2attn_bwd_workspace_bytes(70000, 1, 1, 128, 64, 128, 0, 0) == 70000 * 128 * 4 * 2
+    assert fwd_status(lib, B=1 << 20, H=1 << 10, Hkv=1 << 10, S=0, N=256) == _lib.S2ATTN_ERR_UNSUPPORTED
 
 
 def test_mixed_shift_allowed_when_half_group_is_tile_aligned(lib):

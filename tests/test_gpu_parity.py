@@ -207,6 +207,22 @@ def test_autograd_wrapper():
     assert float((q.grad.float() - ref[2].float()).abs().max()) <= 1e-2
 
 
+@pytest.mark.parametrize("B,N", [(0, 512), (2, 0)])
+def test_empty_inputs(B, N):
+    """An empty batch or sequence: outputs of the right (empty) shapes, no error."""
+    say(f"case empty B={B} N={N}")
+    q = torch.zeros((B, N, 4, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((B, N, 2, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = s2attn_fwd(q, k, k, 128, 2)
+    assert o.shape == q.shape and lse.shape == (B, 4, N)
+    dq, dk, dv = s2attn_bwd(q, k, k, o, lse, q, 128, 2)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == k.shape
+    qg, kg, vg = (x.clone().requires_grad_(True) for x in (q, k, k))
+    s2attn(qg, kg, vg, 128, 2).float().sum().backward()
+    assert qg.grad.shape == q.shape and kg.grad.shape == k.shape
+    torch.cuda.synchronize()
+
+
 def test_rejected_shape_raises():
     q = torch.zeros((1, 500, 2, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(S2AttnError):
