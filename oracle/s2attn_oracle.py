@@ -23,6 +23,15 @@ Language Models", paper-graph-ui summary, section 3.4):
   Causality is applied in the rolled frame, exactly as a causal attention call
   on the rolled groups would (section "Information leakage considerations"
   keeps that wrap-around in the main method).
+* Wrap-group option ``wrap="split"`` (section 5, "Ablation Studies and
+  Robustness Checks", Table 8 and Figure 6, Variant 2; section 3.4,
+  "Information leakage considerations"): the tokens that the roll carries from
+  the front of the sequence to its end form a group of their own instead of
+  sharing the last rolled group with the last G/2 tokens.  Reading taken here:
+  in a shifted head the rolled group that wraps from the end of the sequence
+  to its start (the last one: the last G/2 tokens, then the first G/2) is cut
+  at the wrap into two causal groups; every other group, and every unshifted
+  head, is as in the main method (``wrap="roll"``).
 * Grouped-query attention (several query heads sharing one key/value head) is
   not on the pages; query head h reads key/value head h // (H // Hkv) and the
   key/value gradients are summed over the query heads that share them.
@@ -42,26 +51,33 @@ original token coordinates, a roll/regroup/causal-SDPA formulation, full causal
 attention at G = N without shift, exact invariance under reversing the roll
 direction, head-swap equivariance, closed forms (first row of each group),
 finite differences, GQA against repeated-KV MHA, and the worked index example
-of "The shifting mechanism".
+of "The shifting mechanism".  The split wrap option is pinned by the same
+brute-force mask with the split partition, by causal SDPA over each split group
+as a contiguous token range, by finite differences, and by its agreement with
+the main method wherever the two partitions coincide.
 """
 
 import numpy as np
 
+WRAPS = ("roll", "split")
+
 __all__ = [
-    "check_problem", "head_shift", "kv_head", "rolled_order",
+    "WRAPS", "check_problem", "head_shift", "kv_head", "rolled_order", "group_parts",
     "group_forward", "group_backward",
     "forward", "backward",
     "head_group_forward", "head_group_backward",
 ]
 
 
-def check_problem(B, N, H, Hkv, d, G, shift_heads):
+def check_problem(B, N, H, Hkv, d, G, shift_heads, wrap="roll"):
     """Reject problems the method does not define.
 
     Grouping views the sequence as N/G groups of G tokens (Algorithm 1's reshape
     to [B*N/G, G, ...]) and the shift is G/2 tokens, so N must be a multiple of
-    G and G must be even.
+    G and G must be even.  ``wrap`` is "roll" (the main method) or "split".
     """
+    if wrap not in WRAPS:
+        raise ValueError(f"wrap must be one of {WRAPS}, got {wrap!r}")
     for name, val in (("B", B), ("N", N), ("H", H), ("Hkv", Hkv), ("d", d), ("G", G)):
         if val <= 0:
             raise ValueError(f"{name} must be positive, got {val}")
@@ -96,6 +112,24 @@ def rolled_order(N, sigma):
     position j (the first key line of Algorithm 1 with sigma = G/2).
     """
     return (np.arange(N) + sigma) % N
+
+
+def group_parts(rows, sigma, wrap):
+    """The causal groups that one rolled group (original rows ``rows``, in
+    rolled order) is made of.
+
+    One group, except under ``wrap="split"`` for the group of a shifted head in
+    which the rolled order wraps from the last token of the sequence to the
+    first: it is cut at the wrap, so the tokens the roll carried from the front
+    form a group apart from the tokens of the end.  Returns consecutive slices
+    of ``rows`` that cover it.
+    """
+    if wrap == "split" and sigma:
+        wraps = np.nonzero(np.diff(rows) < 0)[0]
+        if len(wraps):
+            cut = int(wraps[0]) + 1
+            return [slice(0, cut), slice(cut, len(rows))]
+    return [slice(0, len(rows))]
 
 
 def group_forward(Qg, Kg, Vg, scale, chunk=1024):
@@ -142,52 +176,63 @@ def group_backward(Qg, Kg, Vg, Og, lseg, dOg, scale, chunk=1024):
     return dQ, dK, dV
 
 
-def _dims(q, k, v, G, shift_heads):
+def _dims(q, k, v, G, shift_heads, wrap="roll"):
     B, N, H, d = q.shape
     Hkv = k.shape[2]
     if k.shape != (B, N, Hkv, d) or v.shape != (B, N, Hkv, d):
         raise ValueError(f"k {k.shape} / v {v.shape} do not match q {q.shape}")
-    check_problem(B, N, H, Hkv, d, G, shift_heads)
+    check_problem(B, N, H, Hkv, d, G, shift_heads, wrap)
     return B, N, H, Hkv, d
 
 
-def head_group_forward(q, k, v, G, shift_heads, b, h, g):
+def head_group_forward(q, k, v, G, shift_heads, b, h, g, wrap="roll"):
     """Forward of one (batch b, query head h, group g of h's rolled frame).
 
     Returns (rows, O, lse): ``rows`` are the original token indices of the group
     in rolled order; O[i] and lse[i] belong to original token rows[i].
     """
-    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads)
-    rows = rolled_order(N, head_shift(h, H, shift_heads, G))[g * G:(g + 1) * G]
+    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads, wrap)
+    sigma = head_shift(h, H, shift_heads, G)
+    rows = rolled_order(N, sigma)[g * G:(g + 1) * G]
     c = kv_head(h, H, Hkv)
-    Qg = np.asarray(q[b, rows, h], dtype=np.float64)
-    Kg = np.asarray(k[b, rows, c], dtype=np.float64)
-    Vg = np.asarray(v[b, rows, c], dtype=np.float64)
-    O, lse = group_forward(Qg, Kg, Vg, 1.0 / np.sqrt(d))
+    O = np.empty((G, d), dtype=np.float64)
+    lse = np.empty(G, dtype=np.float64)
+    for part in group_parts(rows, sigma, wrap):
+        pr = rows[part]
+        Qg = np.asarray(q[b, pr, h], dtype=np.float64)
+        Kg = np.asarray(k[b, pr, c], dtype=np.float64)
+        Vg = np.asarray(v[b, pr, c], dtype=np.float64)
+        O[part], lse[part] = group_forward(Qg, Kg, Vg, 1.0 / np.sqrt(d))
     return rows, O, lse
 
 
-def head_group_backward(q, k, v, do, G, shift_heads, b, h, g):
+def head_group_backward(q, k, v, do, G, shift_heads, b, h, g, wrap="roll"):
     """Backward of one (b, h, g) slice.
 
     Returns (rows, dQ, dK_part, dV_part): dQ is complete for those rows (a query
     only sees its own group); dK_part / dV_part are head h's contribution to the
     gradients of key/value head kv_head(h) at the same original rows.
     """
-    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads)
-    rows = rolled_order(N, head_shift(h, H, shift_heads, G))[g * G:(g + 1) * G]
+    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads, wrap)
+    sigma = head_shift(h, H, shift_heads, G)
+    rows = rolled_order(N, sigma)[g * G:(g + 1) * G]
     c = kv_head(h, H, Hkv)
     scale = 1.0 / np.sqrt(d)
-    Qg = np.asarray(q[b, rows, h], dtype=np.float64)
-    Kg = np.asarray(k[b, rows, c], dtype=np.float64)
-    Vg = np.asarray(v[b, rows, c], dtype=np.float64)
-    dOg = np.asarray(do[b, rows, h], dtype=np.float64)
-    O, lse = group_forward(Qg, Kg, Vg, scale)
-    dQ, dK, dV = group_backward(Qg, Kg, Vg, O, lse, dOg, scale)
+    dQ = np.empty((G, d), dtype=np.float64)
+    dK = np.empty((G, d), dtype=np.float64)
+    dV = np.empty((G, d), dtype=np.float64)
+    for part in group_parts(rows, sigma, wrap):
+        pr = rows[part]
+        Qg = np.asarray(q[b, pr, h], dtype=np.float64)
+        Kg = np.asarray(k[b, pr, c], dtype=np.float64)
+        Vg = np.asarray(v[b, pr, c], dtype=np.float64)
+        dOg = np.asarray(do[b, pr, h], dtype=np.float64)
+        O, lse = group_forward(Qg, Kg, Vg, scale)
+        dQ[part], dK[part], dV[part] = group_backward(Qg, Kg, Vg, O, lse, dOg, scale)
     return rows, dQ, dK, dV
 
 
-def forward(q, k, v, G, shift_heads):
+def forward(q, k, v, G, shift_heads, wrap="roll"):
     """S2-Attn forward.
 
     q [B, N, H, d], k and v [B, N, Hkv, d] (any float dtype; computed in float64).
@@ -195,24 +240,24 @@ def forward(q, k, v, G, shift_heads):
     token order: writing each group's rows back through ``rows`` is the roll-back
     (Step 2, last sentence; Algorithm 1's second key line).
     """
-    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads)
+    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads, wrap)
     o = np.empty((B, N, H, d), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             for g in range(N // G):
-                rows, Og, lseg = head_group_forward(q, k, v, G, shift_heads, b, h, g)
+                rows, Og, lseg = head_group_forward(q, k, v, G, shift_heads, b, h, g, wrap)
                 o[b, rows, h] = Og
                 lse[b, h, rows] = lseg
     return o, lse
 
 
-def backward(q, k, v, do, G, shift_heads):
+def backward(q, k, v, do, G, shift_heads, wrap="roll"):
     """S2-Attn backward: (dq, dk, dv) of L = sum(o * do), float64.
 
     dk and dv sum the contributions of every query head that reads them.
     """
-    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads)
+    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads, wrap)
     dq = np.empty((B, N, H, d), dtype=np.float64)
     dk = np.zeros((B, N, Hkv, d), dtype=np.float64)
     dv = np.zeros((B, N, Hkv, d), dtype=np.float64)
@@ -220,7 +265,7 @@ def backward(q, k, v, do, G, shift_heads):
         for h in range(H):
             c = kv_head(h, H, Hkv)
             for g in range(N // G):
-                rows, dQg, dKg, dVg = head_group_backward(q, k, v, do, G, shift_heads, b, h, g)
+                rows, dQg, dKg, dVg = head_group_backward(q, k, v, do, G, shift_heads, b, h, g, wrap)
                 dq[b, rows, h] = dQg
                 dk[b, rows, c] += dKg
                 dv[b, rows, c] += dVg

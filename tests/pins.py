@@ -49,14 +49,16 @@ def _close(a, b, tol, what):
 # P1: brute force in original coordinates
 # ---------------------------------------------------------------------------
 
-def allowed_mask_original(N, G, shifted):
+def allowed_mask_original(N, G, shifted, split=False):
     """M[t, u] = token t may attend token u, written without any roll.
 
     Unshifted heads: groups are [kG, (k+1)G) and a token sees the earlier tokens
     of its group and itself.  Shifted heads: the group boundaries move by G/2,
     so groups are [kG + G/2, (k+1)G + G/2) taken cyclically; the last one holds
     the final G/2 tokens followed by the first G/2, in that order, and "earlier"
-    means earlier in that order.
+    means earlier in that order.  Shifted heads with ``split`` (Table 8's
+    Variant 2): the same boundaries without the wrap, so [0, G/2) and
+    [N - G/2, N) are groups of their own and "earlier" is plain token order.
     """
     M = np.zeros((N, N), dtype=bool)
     half = G // 2
@@ -64,6 +66,9 @@ def allowed_mask_original(N, G, shifted):
         for u in range(N):
             if not shifted:
                 same = (t // G) == (u // G)
+                before = u <= t
+            elif split:
+                same = ((t + half) // G) == ((u + half) // G)
                 before = u <= t
             else:
                 # offset of each token from the start of the shifted grid
@@ -75,7 +80,7 @@ def allowed_mask_original(N, G, shifted):
     return M
 
 
-def dense_masked_attention(q, k, v, G, S, grad_do=None):
+def dense_masked_attention(q, k, v, G, S, grad_do=None, split=False):
     """Dense N x N masked softmax attention in torch float64 (autograd for grads)."""
     B, N, H, d = q.shape
     Hkv = k.shape[2]
@@ -84,7 +89,7 @@ def dense_masked_attention(q, k, v, G, S, grad_do=None):
     tk = torch.tensor(k, dtype=torch.float64, requires_grad=True)
     tv = torch.tensor(v, dtype=torch.float64, requires_grad=True)
     masks = {False: torch.tensor(allowed_mask_original(N, G, False)),
-             True: torch.tensor(allowed_mask_original(N, G, True))}
+             True: torch.tensor(allowed_mask_original(N, G, True, split))}
     outs, lses = [], []
     for h in range(H):
         shifted = h >= H - S
@@ -405,8 +410,113 @@ def pin_worked_example_reach(orc):
     _close(o[0, t, 0], [1.0 / n_un, 1.0 / n_un, 0.0, 1.0 / n_un], 1e-15, "unshifted head reach")
 
 
+# ---------------------------------------------------------------------------
+# Split wrap option (Table 8, Variant 2): the wrapped tokens form their own group
+# ---------------------------------------------------------------------------
+
+def pin_split_bruteforce(orc):
+    """Oracle with wrap="split" against the dense mask of the split partition."""
+    for i, (B, N, H, Hkv, d, G, S) in enumerate(SMALL_CASES):
+        q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=110 + i)
+        o, lse = orc.forward(q, k, v, G, S, "split")
+        dq, dk, dv = orc.backward(q, k, v, do, G, S, "split")
+        o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(q, k, v, G, S, grad_do=do, split=True)
+        _close(o, o_ref, 1e-12, f"split brute-force O case {i}")
+        _close(lse, lse_ref, 1e-12, f"split brute-force lse case {i}")
+        _close(dq, dq_ref, 1e-11, f"split brute-force dQ case {i}")
+        _close(dk, dk_ref, 1e-11, f"split brute-force dK case {i}")
+        _close(dv, dv_ref, 1e-11, f"split brute-force dV case {i}")
+
+
+def pin_split_segments_sdpa(orc):
+    """Every split group is a contiguous token range: causal SDPA on each range.
+
+    Shifted heads: [0, G/2), [G/2 + jG, G/2 + (j+1)G), [N - G/2, N); unshifted
+    heads: [jG, (j+1)G).  torch's scaled_dot_product_attention (float64, causal)
+    on each range, autograd for the gradients; K/V repeated for grouped queries.
+    """
+    for i, (B, N, H, Hkv, d, G, S) in enumerate([(1, 32, 4, 2, 4, 8, 2), (2, 24, 2, 1, 3, 12, 1),
+                                                  (1, 16, 2, 2, 4, 16, 2)]):
+        q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=120 + i)
+        o, lse = orc.forward(q, k, v, G, S, "split")
+        dq, dk, dv = orc.backward(q, k, v, do, G, S, "split")
+        r = H // Hkv
+        tq = torch.tensor(q, requires_grad=True)
+        tk = torch.tensor(k, requires_grad=True)
+        tv = torch.tensor(v, requires_grad=True)
+        kk = torch.repeat_interleave(tk, r, dim=2)
+        vv = torch.repeat_interleave(tv, r, dim=2)
+        heads = []
+        for h in range(H):
+            cuts = [0] + (list(range(G // 2, N, G)) if h >= H - S else list(range(G, N, G))) + [N]
+            segs = []
+            for a, e in zip(cuts[:-1], cuts[1:]):
+                segs.append(F.scaled_dot_product_attention(tq[:, a:e, h][:, None], kk[:, a:e, h][:, None],
+                                                           vv[:, a:e, h][:, None], is_causal=True)[:, 0])
+            heads.append(torch.cat(segs, dim=1))
+        ref = torch.stack(heads, dim=2)
+        (ref * torch.tensor(do)).sum().backward()
+        _close(o, ref.detach().numpy(), 1e-12, f"split SDPA O case {i}")
+        _close(dq, tq.grad.numpy(), 1e-11, f"split SDPA dQ case {i}")
+        _close(dk, tk.grad.numpy(), 1e-11, f"split SDPA dK case {i}")
+        _close(dv, tv.grad.numpy(), 1e-11, f"split SDPA dV case {i}")
+
+
+def pin_split_agrees_with_roll(orc):
+    """The two wrap options differ only where their partitions differ.
+
+    S = 0: no head is shifted, so every output is identical.  S > 0: unshifted
+    heads are identical; in shifted heads O and lse differ only on tokens
+    [0, G/2) (the wrapped tokens, which no longer see the last G/2 tokens), and
+    the first wrapped token then attends to itself only (O = V, lse = scale q.k).
+    """
+    B, N, H, Hkv, d, G = 1, 32, 4, 2, 4, 8
+    q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=130)
+    for S in (0, 2):
+        o_r, lse_r = orc.forward(q, k, v, G, S)
+        o_s, lse_s = orc.forward(q, k, v, G, S, "split")
+        if S == 0:
+            assert np.array_equal(o_r, o_s) and np.array_equal(lse_r, lse_s), "split changed an unshifted problem"
+            for a, b, n in zip(orc.backward(q, k, v, do, G, S), orc.backward(q, k, v, do, G, S, "split"),
+                               ("dQ", "dK", "dV")):
+                assert np.array_equal(a, b), f"split changed {n} of an unshifted problem"
+            continue
+        _close(o_s[:, :, :H - S], o_r[:, :, :H - S], 1e-14, "split: unshifted heads O")
+        _close(o_s[:, G // 2:], o_r[:, G // 2:], 1e-13, "split: rows past the wrapped tokens")
+        _close(lse_s[:, :, G // 2:], lse_r[:, :, G // 2:], 1e-13, "split: lse past the wrapped tokens")
+        assert np.max(np.abs(o_s[:, :G // 2, H - S:] - o_r[:, :G // 2, H - S:])) > 1e-3, \
+            "split did not change the wrapped tokens"
+        r = H // Hkv
+        for h in range(H - S, H):
+            _close(o_s[0, 0, h], v[0, 0, h // r], 1e-14, f"split: first wrapped token O head {h}")
+            _close(lse_s[0, h, 0], np.dot(q[0, 0, h], k[0, 0, h // r]) / np.sqrt(d), 1e-14,
+                   f"split: first wrapped token lse head {h}")
+
+
+def pin_split_finite_differences(orc):
+    B, N, H, Hkv, d, G, S = 1, 16, 2, 1, 3, 8, 1
+    q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=140)
+    grads = orc.backward(q, k, v, do, G, S, "split")
+    eps = 1e-6
+    for pos, name in enumerate(("dQ", "dK", "dV")):
+        x = (q, k, v)[pos]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args_p, args_m = [q, k, v], [q, k, v]
+            args_p[pos] = x.copy()
+            args_p[pos][idx] += eps
+            args_m[pos] = x.copy()
+            args_m[pos][idx] -= eps
+            lp = float(np.sum(orc.forward(*args_p, G, S, "split")[0] * do))
+            lm = float(np.sum(orc.forward(*args_m, G, S, "split")[0] * do))
+            num[idx] = (lp - lm) / (2 * eps)
+        err = np.linalg.norm(num - grads[pos]) / np.linalg.norm(num)
+        assert err <= 1e-6, f"split finite differences {name}: rel {err:.2e}"
+
+
 ALL_PINS = [
     pin_bruteforce_forward, pin_bruteforce_backward, pin_roll_regroup, pin_full_causal,
     pin_direction_reversal, pin_head_swap, pin_closed_forms, pin_finite_differences,
     pin_gqa_repeat, pin_worked_example_index_map, pin_worked_example_reach,
+    pin_split_bruteforce, pin_split_segments_sdpa, pin_split_agrees_with_roll, pin_split_finite_differences,
 ]

@@ -32,6 +32,12 @@ def test_oracle_rejects_undefined_problems(bad):
         orc.forward(q, k, k, p["G"], p["S"])
 
 
+def test_oracle_rejects_unknown_wrap():
+    q = np.zeros((1, 16, 2, 4))
+    with pytest.raises(ValueError):
+        orc.forward(q, q, q, 8, 1, "swap")
+
+
 def test_table11_attention_flops():
     """The pages' attention FLOPs (dense forward convention) are 4 N G d H L exactly."""
     path = os.path.join(pins.GOLDEN, "table11_attention_flops.txt")
@@ -54,21 +60,22 @@ def test_pair_count_matches_bruteforce_mask(N, G, H, S):
     assert flops.allowed_pairs(1, H, N, G) == total
 
 
-def test_sampled_slices_agree_with_full_oracle():
+@pytest.mark.parametrize("wrap", orc.WRAPS)
+def test_sampled_slices_agree_with_full_oracle(wrap):
     """head_group_* (used for sampled parity at full size) agree with forward/backward."""
     B, N, H, Hkv, d, G, S = 2, 32, 4, 2, 4, 8, 2
     q, k, v, do = pins.rand_problem(B, N, H, Hkv, d, seed=5)
-    o, lse = orc.forward(q, k, v, G, S)
-    dq, dk, dv = orc.backward(q, k, v, do, G, S)
+    o, lse = orc.forward(q, k, v, G, S, wrap)
+    dq, dk, dv = orc.backward(q, k, v, do, G, S, wrap)
     dk_acc = np.zeros_like(dk)
     dv_acc = np.zeros_like(dv)
     for b in range(B):
         for h in range(H):
             for g in range(N // G):
-                rows, Og, lseg = orc.head_group_forward(q, k, v, G, S, b, h, g)
+                rows, Og, lseg = orc.head_group_forward(q, k, v, G, S, b, h, g, wrap)
                 assert np.array_equal(o[b, rows, h], Og)
                 assert np.array_equal(lse[b, h, rows], lseg)
-                rows, dQg, dKg, dVg = orc.head_group_backward(q, k, v, do, G, S, b, h, g)
+                rows, dQg, dKg, dVg = orc.head_group_backward(q, k, v, do, G, S, b, h, g, wrap)
                 assert np.array_equal(dq[b, rows, h], dQg)
                 dk_acc[b, rows, orc.kv_head(h, H, Hkv)] += dKg
                 dv_acc[b, rows, orc.kv_head(h, H, Hkv)] += dVg

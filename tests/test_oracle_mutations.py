@@ -26,8 +26,8 @@ MUTATIONS = [
      "allowed = np.arange(r1)[None, :] < np.arange(r0, r1)[:, None]", 0),
     ("anti-causal-bwd", "allowed = np.arange(r1)[None, :] <= np.arange(r0, r1)[:, None]",
      "allowed = np.arange(r1)[None, :] >= np.arange(r0, r1)[:, None]", 1),
-    ("no-scale-fwd", "O, lse = group_forward(Qg, Kg, Vg, 1.0 / np.sqrt(d))",
-     "O, lse = group_forward(Qg, Kg, Vg, 1.0)", 0),
+    ("no-scale-fwd", "group_forward(Qg, Kg, Vg, 1.0 / np.sqrt(d))",
+     "group_forward(Qg, Kg, Vg, 1.0)", 0),
     ("kv-head-modulo", "return h // (H // Hkv)", "return h % Hkv", 0),
     ("drop-dvec", "dS = P * (dP - Dvec[r0:r1, None])", "dS = P * dP", 0),
     ("dvec-wrong-operand", "Dvec = np.sum(dOg * Og, axis=1)", "Dvec = np.sum(dOg * Qg, axis=1)", 0),
@@ -42,6 +42,13 @@ MUTATIONS = [
     ("transposed-scores", "S = scale * (Qg[r0:r1] @ Kg[:r1].T)\n        allowed",
      "S = scale * (Kg[r0:r1] @ Qg[:r1].T)\n        allowed", 0),
     ("lse-of-rolled-row", "lse[b, h, rows] = lseg", "lse[b, h, g * G:(g + 1) * G] = lseg", 0),
+    ("split-ignored", 'if wrap == "split" and sigma:', 'if wrap == "none" and sigma:', 0),
+    ("split-in-roll-mode", 'if wrap == "split" and sigma:', 'if sigma:', 0),
+    ("split-at-quarter", "cut = int(wraps[0]) + 1", "cut = (int(wraps[0]) + 1) // 2", 0),
+    ("split-every-group", "        if len(wraps):\n            cut = int(wraps[0]) + 1",
+     "        if True:\n            cut = len(rows) // 2", 0),
+    ("split-keeps-wrap-keys", "return [slice(0, cut), slice(cut, len(rows))]",
+     "return [slice(0, cut), slice(0, len(rows))]", 0),
 ]
 
 NEUTRAL = ("reverse-roll-direction", "return (np.arange(N) + sigma) % N", "return (np.arange(N) - sigma) % N", 0)
