@@ -59,11 +59,29 @@ typedef enum {
     S2ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
     S2ATTN_ERR_SHAPE = 2,        /* B or N < 0, H, Hkv, d or G <= 0, N % G != 0, G odd,
                                     shift_heads outside [0, H], H % Hkv != 0 */
-    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype, G % 128 != 0, the mixed-shift rule
-                                    above, or B * H * N / 128 >= 2^31 */
+    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype or wrap option, G % 128 != 0, the
+                                    mixed-shift rule above, or B * H * N / 128 >= 2^31 */
     S2ATTN_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError) */
     S2ATTN_ERR_WORKSPACE = 5     /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
 } s2attn_status;
+
+/*
+ * Wrap handling of the shifted heads (the `wrap` argument of the _ex calls).
+ *   S2ATTN_WRAP_ROLL  : the method described above (Algorithm 1): a shifted
+ *                       head's last rolled group is tokens N-G/2..N-1 followed
+ *                       by tokens 0..G/2-1, one causal group.
+ *   S2ATTN_WRAP_SPLIT : Variant 2 of Table 8 / Figure 6 (page section 5,
+ *                       "Ablation Studies and Robustness Checks"; section 3.4,
+ *                       "Information leakage considerations"): the tokens the
+ *                       roll carries from the front form a group of their own,
+ *                       so that last rolled group is cut at G/2 into two causal
+ *                       groups, tokens [N-G/2, N) and tokens [0, G/2).  Every
+ *                       other group, and every unshifted head, is unchanged.
+ */
+typedef enum {
+    S2ATTN_WRAP_ROLL = 0,
+    S2ATTN_WRAP_SPLIT = 1
+} s2attn_wrap;
 
 /*
  * Forward.  Writes o[B,N,H,d] and lse[B,H,N].
@@ -122,6 +140,32 @@ int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                   void* dq, void* workspace, size_t workspace_bytes,
                   int B, int H, int Hkv, int N, int d, int G, int shift_heads,
                   int dtype, void* stream);
+
+/*
+ * The forward, the backward and its dkdv and dq stages with a wrap option
+ * (an s2attn_wrap value; any other value returns S2ATTN_ERR_UNSUPPORTED before
+ * any other work).  Arguments are otherwise those of the calls without _ex,
+ * which are these with S2ATTN_WRAP_ROLL.  s2attn_bwd_prep and the workspace do
+ * not depend on the option; the backward must use the forward's option.
+ */
+int s2attn_fwd_ex(const void* q, const void* k, const void* v,
+                  void* o, float* lse,
+                  int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                  int dtype, void* stream);
+int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dO,
+                  void* dq, void* dk, void* dv,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                  int dtype, void* stream);
+int s2attn_bwd_dkdv_ex(const void* q, const void* k, const void* v, const void* dO,
+                       void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                       int dtype, void* stream);
+int s2attn_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO,
+                     void* dq, void* workspace, size_t workspace_bytes,
+                     int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                     int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* s2attn_status_str(int status);

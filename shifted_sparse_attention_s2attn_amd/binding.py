@@ -54,12 +54,19 @@ def _check_tensors(q, k, v, extra=()):
         raise TypeError("q, k, v must share one dtype")
 
 
+def _wrap_code(wrap):
+    """Wrap handling of the shifted heads: "roll" (the method) or "split" (Table 8, Variant 2)."""
+    if wrap not in _lib.WRAPS:
+        raise ValueError(f"wrap must be one of {sorted(_lib.WRAPS)}, got {wrap!r}")
+    return _lib.WRAPS[wrap]
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def s2attn_fwd(q, k, v, G, shift_heads=None, out=None, lse=None, stream=None):
+def s2attn_fwd(q, k, v, G, shift_heads=None, out=None, lse=None, stream=None, wrap="roll"):
     """S2-Attn forward.  Returns (o [B,N,H,d], lse [B,H,N] float32)."""
     _check_tensors(q, k, v)
     B, N, H, d = q.shape
@@ -69,8 +76,9 @@ def s2attn_fwd(q, k, v, G, shift_heads=None, out=None, lse=None, stream=None):
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     with torch.cuda.device(q.device):
-        st = _lib.load().s2attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse_t),
-                                    B, H, Hkv, N, d, G, shift_heads, _dtype_code(q), _stream(stream))
+        st = _lib.load().s2attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse_t),
+                                       B, H, Hkv, N, d, G, shift_heads, _wrap_code(wrap), _dtype_code(q),
+                                       _stream(stream))
     if st != _lib.S2ATTN_OK:
         raise S2AttnError(st, "s2attn_fwd")
     return o, lse_t
@@ -81,7 +89,7 @@ def s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype):
     return int(_lib.load().s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, code))
 
 
-def s2attn_bwd(q, k, v, o, lse, do, G, shift_heads=None, workspace=None, stream=None, grads=None):
+def s2attn_bwd(q, k, v, o, lse, do, G, shift_heads=None, workspace=None, stream=None, grads=None, wrap="roll"):
     """S2-Attn backward of sum(o * do).  Returns (dq, dk, dv)."""
     _check_tensors(q, k, v, (("o", o), ("lse", lse), ("do", do)))
     B, N, H, d = q.shape
@@ -96,9 +104,10 @@ def s2attn_bwd(q, k, v, o, lse, do, G, shift_heads=None, workspace=None, stream=
     else:
         dq, dk, dv = grads
     with torch.cuda.device(q.device):
-        st = _lib.load().s2attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), _ptr(do),
-                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-                                    B, H, Hkv, N, d, G, shift_heads, _dtype_code(q), _stream(stream))
+        st = _lib.load().s2attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), _ptr(do),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                       B, H, Hkv, N, d, G, shift_heads, _wrap_code(wrap), _dtype_code(q),
+                                       _stream(stream))
     if st != _lib.S2ATTN_OK:
         raise S2AttnError(st, "s2attn_bwd")
     return dq, dk, dv
@@ -123,23 +132,25 @@ def s2attn_bwd_prep(q, k, o, lse, do, workspace, G, shift_heads=None, stream=Non
                "s2attn_bwd_prep")
 
 
-def s2attn_bwd_dkdv(q, k, v, do, dk, dv, workspace, G, shift_heads=None, stream=None):
+def s2attn_bwd_dkdv(q, k, v, do, dk, dv, workspace, G, shift_heads=None, stream=None, wrap="roll"):
     """Stage 2 of the backward: dk, dv (needs prep's workspace)."""
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
-        _check(_lib.load().s2attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
-                                           _ptr(workspace), workspace.numel(),
-                                           B, H, Hkv, N, d, G, S, _dtype_code(q), _stream(stream)),
+        _check(_lib.load().s2attn_bwd_dkdv_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
+                                              _ptr(workspace), workspace.numel(),
+                                              B, H, Hkv, N, d, G, S, _wrap_code(wrap), _dtype_code(q),
+                                              _stream(stream)),
                "s2attn_bwd_dkdv")
 
 
-def s2attn_bwd_dq(q, k, v, do, dq, workspace, G, shift_heads=None, stream=None):
+def s2attn_bwd_dq(q, k, v, do, dq, workspace, G, shift_heads=None, stream=None, wrap="roll"):
     """Stage 3 of the backward: dq (needs prep's workspace)."""
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
-        _check(_lib.load().s2attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
-                                         _ptr(workspace), workspace.numel(),
-                                         B, H, Hkv, N, d, G, S, _dtype_code(q), _stream(stream)),
+        _check(_lib.load().s2attn_bwd_dq_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
+                                            _ptr(workspace), workspace.numel(),
+                                            B, H, Hkv, N, d, G, S, _wrap_code(wrap), _dtype_code(q),
+                                            _stream(stream)),
                "s2attn_bwd_dq")
 
 
@@ -147,19 +158,23 @@ class S2Attn(torch.autograd.Function):
     """autograd wrapper: forward and backward both run in libs2attn."""
 
     @staticmethod
-    def forward(ctx, q, k, v, G, shift_heads):
-        o, lse = s2attn_fwd(q, k, v, G, shift_heads)
+    def forward(ctx, q, k, v, G, shift_heads, wrap="roll"):
+        o, lse = s2attn_fwd(q, k, v, G, shift_heads, wrap=wrap)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.G, ctx.shift_heads = G, shift_heads
+        ctx.G, ctx.shift_heads, ctx.wrap = G, shift_heads, wrap
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = s2attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.G, ctx.shift_heads)
-        return dq, dk, dv, None, None
+        dq, dk, dv = s2attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.G, ctx.shift_heads, wrap=ctx.wrap)
+        return dq, dk, dv, None, None, None
 
 
-def s2attn(q, k, v, G, shift_heads=None):
-    """Differentiable S2-Attn on [B, N, H, d] tensors (shift_heads defaults to H // 2)."""
-    return S2Attn.apply(q, k, v, G, q.shape[2] // 2 if shift_heads is None else shift_heads)
+def s2attn(q, k, v, G, shift_heads=None, wrap="roll"):
+    """Differentiable S2-Attn on [B, N, H, d] tensors (shift_heads defaults to H // 2).
+
+    ``wrap="split"`` selects Variant 2 of Table 8: the tokens the roll carries
+    from the front of the sequence form their own group.
+    """
+    return S2Attn.apply(q, k, v, G, q.shape[2] // 2 if shift_heads is None else shift_heads, wrap)

@@ -9,16 +9,16 @@
 
 namespace s2a {
 template <typename T, int D>
-hipError_t launch_fwd(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
+hipError_t launch_fwd(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, int,
                       hipStream_t);
 template <typename T, int D>
 hipError_t launch_bwd_prep(const void*, const void*, const float*, float*, float*, int, int, int, hipStream_t);
 template <typename T, int D>
 hipError_t launch_bwd_dkdv(const void*, const void*, const void*, const void*, const float*, const float*, void*,
-                           void*, int, int, int, int, int, int, hipStream_t);
+                           void*, int, int, int, int, int, int, int, hipStream_t);
 template <typename T, int D>
 hipError_t launch_bwd_dq(const void*, const void*, const void*, const void*, const float*, const float*, void*,
-                         int, int, int, int, int, int, hipStream_t);
+                         int, int, int, int, int, int, int, hipStream_t);
 }  // namespace s2a
 
 namespace {
@@ -46,28 +46,38 @@ int check_problem(int B, int H, int Hkv, int N, int d, int G, int shift_heads, i
 
 bool empty_problem(int B, int N) { return B == 0 || N == 0; }
 
+int check_wrap(int wrap) {
+  return (wrap == S2ATTN_WRAP_ROLL || wrap == S2ATTN_WRAP_SPLIT) ? S2ATTN_OK : S2ATTN_ERR_UNSUPPORTED;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
 extern "C" {
 
-int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-               int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
-  const int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+int s2attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype, void* stream) {
+  int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st == S2ATTN_OK) st = check_wrap(wrap);
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !o || !lse) return S2ATTN_ERR_NULL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == S2ATTN_BF16) {
-    e = d == 64 ? s2a::launch_fwd<s2a::bf16, 64>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, s)
-                : s2a::launch_fwd<s2a::bf16, 128>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, s);
+    e = d == 64 ? s2a::launch_fwd<s2a::bf16, 64>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, s)
+                : s2a::launch_fwd<s2a::bf16, 128>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, s);
   } else {
-    e = d == 64 ? s2a::launch_fwd<float, 64>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, s)
-                : s2a::launch_fwd<float, 128>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, s);
+    e = d == 64 ? s2a::launch_fwd<float, 64>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, s)
+                : s2a::launch_fwd<float, 128>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, s);
   }
   return e == hipSuccess ? S2ATTN_OK : S2ATTN_ERR_HIP;
+}
+
+int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  return s2attn_fwd_ex(q, k, v, o, lse, B, H, Hkv, N, d, G, shift_heads, S2ATTN_WRAP_ROLL, dtype, stream);
 }
 
 size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype) {
@@ -112,15 +122,15 @@ struct Prep {
 template <typename T, int D>
 struct Dkdv {
   static hipError_t run(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
-                        Workspace ws, int B, int H, int Hkv, int N, int G, int S, hipStream_t s) {
-    return s2a::launch_bwd_dkdv<T, D>(q, k, v, dO, ws.lse2, ws.dvec, dk, dv, B, H, Hkv, N, G, S, s);
+                        Workspace ws, int B, int H, int Hkv, int N, int G, int S, int wrap, hipStream_t s) {
+    return s2a::launch_bwd_dkdv<T, D>(q, k, v, dO, ws.lse2, ws.dvec, dk, dv, B, H, Hkv, N, G, S, wrap, s);
   }
 };
 template <typename T, int D>
 struct Dq {
   static hipError_t run(const void* q, const void* k, const void* v, const void* dO, void* dq, Workspace ws,
-                        int B, int H, int Hkv, int N, int G, int S, hipStream_t s) {
-    return s2a::launch_bwd_dq<T, D>(q, k, v, dO, ws.lse2, ws.dvec, dq, B, H, Hkv, N, G, S, s);
+                        int B, int H, int Hkv, int N, int G, int S, int wrap, hipStream_t s) {
+    return s2a::launch_bwd_dq<T, D>(q, k, v, dO, ws.lse2, ws.dvec, dq, B, H, Hkv, N, G, S, wrap, s);
   }
 };
 
@@ -142,38 +152,57 @@ int s2attn_bwd_prep(const void* o, const float* lse, const void* dO, void* works
   return status_of(dispatch<Prep>(dtype, d, o, dO, lse, ws, B, H, N, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
-                    void* workspace, size_t workspace_bytes,
-                    int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+int s2attn_bwd_dkdv_ex(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes,
+                       int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype,
+                       void* stream) {
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st == S2ATTN_OK) st = check_wrap(wrap);
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !dO || !dk || !dv) return S2ATTN_ERR_NULL;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
-  return status_of(dispatch<Dkdv>(dtype, d, q, k, v, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads,
+  return status_of(dispatch<Dkdv>(dtype, d, q, k, v, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads, wrap,
                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
-int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq,
-                  void* workspace, size_t workspace_bytes,
-                  int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes,
+                    int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  return s2attn_bwd_dkdv_ex(q, k, v, dO, dk, dv, workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads,
+                            S2ATTN_WRAP_ROLL, dtype, stream);
+}
+
+int s2attn_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO, void* dq,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype,
+                     void* stream) {
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st == S2ATTN_OK) st = check_wrap(wrap);
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !dO || !dq) return S2ATTN_ERR_NULL;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
-  return status_of(dispatch<Dq>(dtype, d, q, k, v, dO, dq, ws, B, H, Hkv, N, G, shift_heads,
+  return status_of(dispatch<Dq>(dtype, d, q, k, v, dO, dq, ws, B, H, Hkv, N, G, shift_heads, wrap,
                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
-int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
-               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-               int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  return s2attn_bwd_dq_ex(q, k, v, dO, dq, workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads,
+                          S2ATTN_WRAP_ROLL, dtype, stream);
+}
+
+int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                  int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype, void* stream) {
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st == S2ATTN_OK) st = check_wrap(wrap);
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
@@ -182,16 +211,24 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
   if (st != S2ATTN_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = dispatch<Prep>(dtype, d, o, dO, lse, ws, B, H, N, s);
-  if (e == hipSuccess) e = dispatch<Dkdv>(dtype, d, q, k, v, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads, s);
-  if (e == hipSuccess) e = dispatch<Dq>(dtype, d, q, k, v, dO, dq, ws, B, H, Hkv, N, G, shift_heads, s);
+  if (e == hipSuccess)
+    e = dispatch<Dkdv>(dtype, d, q, k, v, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads, wrap, s);
+  if (e == hipSuccess) e = dispatch<Dq>(dtype, d, q, k, v, dO, dq, ws, B, H, Hkv, N, G, shift_heads, wrap, s);
   return status_of(e);
+}
+
+int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+               int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype, void* stream) {
+  return s2attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, H, Hkv, N, d, G,
+                       shift_heads, S2ATTN_WRAP_ROLL, dtype, stream);
 }
 
 const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_OK: return "ok";
     case S2ATTN_ERR_NULL: return "a required pointer is NULL";
     case S2ATTN_ERR_SHAPE: return "invalid shape (size <= 0, N % G != 0, odd G, shift_heads outside [0,H], or H % Hkv != 0)";
-    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype, G % 128 != 0, or mixed-shift KV head with (G/2) % 128 != 0)";
+    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, G % 128 != 0, mixed-shift KV head with (G/2) % 128 != 0, or grid too large)";
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     default: return "unknown status";

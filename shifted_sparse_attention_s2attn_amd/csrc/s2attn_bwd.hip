@@ -101,7 +101,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
-    T* __restrict__ dk, T* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, float scale) {
+    T* __restrict__ dk, T* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, int split,
+    float scale) {
   using S = DkdvShape<T, D>;
   constexpr int BKV = S::kBKV, BQ = S::kBQ, NQS = S::kNQS;
   constexpr int QCPR = S::kQCPR, TCPR = S::kTCPR, QRPT = S::kQRowsPerThread;
@@ -157,8 +158,10 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     int jk0 = j0 + sig0 - sig;                  // same key rows in head h's rolled frame
     if (jk0 < 0) jk0 += N;
     if (jk0 >= N) jk0 -= N;
-    const int gstart = (jk0 / G) * G;
-    const int qt_begin = jk0 / BQ, qt_end = (gstart + G) / BQ;
+    const bool split_head = split && sig != 0;
+    // query tiles meeting the workgroup's keys, and the end of this wave's queries
+    const int qt_begin = jk0 / BQ, qt_end = query_end_row(jk0 + BKV - 32, G, N, split_head) / BQ;
+    const int q_end_w = query_end_row(jk0 + wave * 32, G, N, split_head);
     const T* qb = q + (size_t)b * N * qstride + (size_t)h * D;
     const T* dob = dO + (size_t)b * N * qstride + (size_t)h * D;
     const float* lse_h = lse2 + ((size_t)b * H + h) * N;
@@ -196,6 +199,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
       if (tid < BQ) { lse_s[tid] = lse_r; dvec_s[tid] = dvec_r; }
       __syncthreads();
       if (qt + 1 < qt_end) load_q(jq0 + BQ);
+      if (jq0 >= q_end_w) continue;             // these queries are in another group than the wave's keys
 
       // S = Q K^T and dP = dO V^T, keys on lanes, queries in registers
       f32x16 sacc[NQS], pacc[NQS];
@@ -273,7 +277,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void s2attn_bwd_dq(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ dvec, T* __restrict__ dq,
-    int N, int H, int Hkv, int G, int shift_heads, float scale) {
+    int N, int H, int Hkv, int G, int shift_heads, int split, float scale) {
   using S = DqShape<T, D>;
   constexpr int BR = S::kBR, BC = S::kBC, KCPR = S::kKCPR, TCPR = S::kTCPR, KRPT = S::kKRowsPerThread;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -293,8 +297,9 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   const int h = (to.pair / groups) % H, b = to.pair / (groups * H);
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
+  const bool split_head = split && sigma != 0;
   const int j0 = grp * G + pos * BR;
-  const int kv_begin = grp * G;
+  const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
   const int ntiles = (j0 + BR - kv_begin) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
@@ -305,6 +310,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
   const int tq = orig_row(jq, sigma, N);
+  const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
   v8<T> qf[S::kDC], dof[S::kDC];
   {
     const T* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
     store_transposed<T, KRPT, TCPR>(Kt, kr, k_dc, k_kg * KRPT);
     __syncthreads();
     if (it + 1 < ntiles) load_tile(kt0 + BC);
-    if (kt0 > jw + 31) continue;                // tile entirely after this wave's queries
+    if (kt0 > jw + 31 || kt0 < kw0) continue;   // tile after this wave's queries, or outside its group
 
     // S^T = K Q^T, dP^T = V dO^T : keys on tile rows, queries on lanes
     f32x16 s[2], dp[2];
@@ -456,7 +462,9 @@ __device__ __forceinline__ f32x4 lds_f32x4(const char* base, int off) {
   return *reinterpret_cast<const f32x4*>(base + off);
 }
 
-template <int D>
+// SPLIT: the split wrap option (compiled separately, so that the main method's
+// step loop carries no trace of it).
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
@@ -534,24 +542,28 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   const int offL = (qh * 32 + hf * 8) * 4;            // lse / Dvec floats of this lane's queries
 
   // The key tile seen from a query head: only two frames exist (unshifted,
-  // shifted), so they are fixed here: first key row in the head's rolled frame
-  // and the head's query tiles [qt_b, qt_e) of the key tile's group.
-  int fr_jk0[2], fr_qb[2], fr_qe[2];
+  // shifted), so they are fixed here: first key row in the head's rolled frame,
+  // the head's query tiles [qt_b, qt_e) meeting the tile's keys, and the end
+  // row of the queries meeting this wave's keys.
+  int fr_jk0[2], fr_qb[2], fr_qe[2], fr_wqe[2];
 #pragma unroll
   for (int sh = 0; sh < 2; ++sh) {
     int jk = j0 + sig0 - sh * (G / 2);
     if (jk < 0) jk += N;
     if (jk >= N) jk -= N;
+    const bool split_head = SPLIT && sh;
     fr_jk0[sh] = jk;
     fr_qb[sh] = jk / BQ;
-    fr_qe[sh] = (jk / G) * (G / BQ) + G / BQ;
+    fr_qe[sh] = query_end_row(jk + BKV - 32, G, N, split_head) / BQ;
+    fr_wqe[sh] = query_end_row(jk + kg * 32, G, N, split_head);
   }
-  auto head_frame = [&](int hh, int& sig, int& jk0, int& qt_b, int& qt_e) {
+  auto head_frame = [&](int hh, int& sig, int& jk0, int& qt_b, int& qt_e, int& wqe) {
     const int sh = h0 + hh >= H - shift_heads;
     sig = sh ? G / 2 : 0;
     jk0 = fr_jk0[sh];
     qt_b = fr_qb[sh];
     qt_e = fr_qe[sh];
+    wqe = fr_wqe[sh];
   };
   auto issue_step = [&](int hh, int qt, int sig, int stage) {
     const int h = h0 + hh;
@@ -618,10 +630,11 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
       }
     }
   };
-  auto step = [&](auto stg_c, int jk0, int qt) {
+  auto step = [&](auto stg_c, int jk0, int wqe, int qt) {
     const int jq0 = qt * BQ;
     const int key_lo = jk0 + kg * 32, q_lo = jq0 + qh * 32;
     if (key_lo > q_lo + 31) return;                   // every key follows every query: P = 0
+    if (SPLIT && q_lo >= wqe) return;                 // queries of another group than the wave's keys
     const int jkey = key_lo + l32, jq_first = q_lo + hf * 8;
     if (key_lo + 31 > q_lo)
       compute(stg_c, std::integral_constant<bool, true>(), jkey, jq_first);
@@ -629,17 +642,17 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
       compute(stg_c, std::integral_constant<bool, false>(), jkey, jq_first);
   };
 
-  int hh = 0, sig, jk0, qt_b, qt_e;
-  head_frame(0, sig, jk0, qt_b, qt_e);
+  int hh = 0, sig, jk0, qt_b, qt_e, wqe;
+  head_frame(0, sig, jk0, qt_b, qt_e, wqe);
   int qt = qt_b;
   issue_step(hh, qt, sig, 0);
   // advance the cursor to the next (head, query tile); returns false past the end
-  auto advance = [&](int& nhh, int& nqt, int& nsig, int& njk0, int& nqb, int& nqe) {
-    nhh = hh; nqt = qt + 1; nsig = sig; njk0 = jk0; nqb = qt_b; nqe = qt_e;
+  auto advance = [&](int& nhh, int& nqt, int& nsig, int& njk0, int& nqb, int& nqe, int& nwqe) {
+    nhh = hh; nqt = qt + 1; nsig = sig; njk0 = jk0; nqb = qt_b; nqe = qt_e; nwqe = wqe;
     if (nqt == qt_e) {
       ++nhh;
       if (nhh < r) {
-        head_frame(nhh, nsig, njk0, nqb, nqe);
+        head_frame(nhh, nsig, njk0, nqb, nqe, nwqe);
         nqt = nqb;
       }
     }
@@ -647,13 +660,13 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   };
   auto one = [&](auto stg_c) {
     constexpr int STG = decltype(stg_c)::value;
-    int nhh, nqt, nsig, njk0, nqb, nqe;
-    const bool more = advance(nhh, nqt, nsig, njk0, nqb, nqe);
+    int nhh, nqt, nsig, njk0, nqb, nqe, nwqe;
+    const bool more = advance(nhh, nqt, nsig, njk0, nqb, nqe, nwqe);
     wait_vmem_all();
     __syncthreads();                                  // this stage landed for all; the other is free
     if (more) issue_step(nhh, nqt, nsig, STG ^ 1);
-    step(stg_c, jk0, qt);
-    hh = nhh; qt = nqt; sig = nsig; jk0 = njk0; qt_b = nqb; qt_e = nqe;
+    step(stg_c, jk0, wqe, qt);
+    hh = nhh; qt = nqt; sig = nsig; jk0 = njk0; qt_b = nqb; qt_e = nqe; wqe = nwqe;
     return more;
   };
   while (one(std::integral_constant<int, 0>()) && one(std::integral_constant<int, 1>())) {
@@ -715,7 +728,7 @@ template <int D>
 __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
-    bf16* __restrict__ dq, int N, int H, int Hkv, int G, int shift_heads, float scale) {
+    bf16* __restrict__ dq, int N, int H, int Hkv, int G, int shift_heads, int split, float scale) {
   using S = DqB16Shape<D>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTile;
   constexpr int RB = D * 2;
@@ -737,8 +750,9 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   const int h = (to.pair / groups) % H, b = to.pair / (groups * H);
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
+  const bool split_head = split && sigma != 0;
   const int j0 = grp * G + pos * BR;
-  const int kv_begin = grp * G;
+  const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
   const int ntiles = (j0 + BR - kv_begin) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
@@ -748,6 +762,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
   const int tq = orig_row(jq, sigma, N);
+  const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
   bf16x8 qf[S::kDC], dof[S::kDC];
   {
     const bf16* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
@@ -852,7 +867,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     wait_vmem_all();
     __syncthreads();
     if (it + 1 < ntiles) issue_tile(kt0 + BC, STG ^ 1);
-    if (kt0 > jw + 31) return;
+    if (kt0 > jw + 31 || kt0 < kw0) return;      // tile after this wave's queries, or outside its group
     if (kt0 + BC - 1 > jw)
       compute(stg_c, std::integral_constant<bool, true>(), kt0);
     else
@@ -900,77 +915,83 @@ hipError_t launch_bwd_prep(const void* o, const void* dO, const float* lse, floa
 template <int D>
 hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                             const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                            int shift_heads, float scale, hipStream_t stream) {
+                            int shift_heads, int split, float scale, hipStream_t stream) {
   using S = DkdvB16Shape<D>;
-  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D>), dim3(B * Hkv * (N / S::kBKV)), dim3(S::kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec,
-                     (bf16*)dk, (bf16*)dv, N, H, Hkv, G, shift_heads, scale);
+  const dim3 grid(B * Hkv * (N / S::kBKV)), block(S::kThreads);
+  if (split)
+    hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, true>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk, (bf16*)dv, N, H, Hkv, G, shift_heads,
+                       scale);
+  else
+    hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, false>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk, (bf16*)dv, N, H, Hkv, G, shift_heads,
+                       scale);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_dkdv_generic(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                                const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                               int shift_heads, float scale, hipStream_t stream) {
+                               int shift_heads, int split, float scale, hipStream_t stream) {
   using S = DkdvShape<T, D>;
   static bool attr = false;
   hipError_t e = raise_lds_limit(&s2attn_bwd_dkdv<T, D>, S::kLdsBytes, attr);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), dim3(B * Hkv * (N / S::kBKV)), dim3(S::kThreads), S::kLdsBytes,
                      stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dk, (T*)dv, N,
-                     H, Hkv, G, shift_heads, scale);
+                     H, Hkv, G, shift_heads, split, scale);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                            const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                           int shift_heads, hipStream_t stream) {
+                           int shift_heads, int split, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
     // the fast kernel addresses one batch's Q / dO with 31-bit byte offsets
     if ((size_t)N * H * D * sizeof(T) < (size_t(1) << 31))
-      return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, scale, stream);
+      return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, split, scale, stream);
   }
-  return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, scale, stream);
+  return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, split, scale, stream);
 }
 
 template <int D>
 hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                           const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
-                          float scale, hipStream_t stream) {
+                          int split, float scale, hipStream_t stream) {
   using S = DqB16Shape<D>;
   hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D>), dim3(B * H * (N / S::kBR)), dim3(S::kThreads), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dq, N, H,
-                     Hkv, G, shift_heads, scale);
+                     Hkv, G, shift_heads, split, scale);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_dq_generic(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                              const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
-                             float scale, hipStream_t stream) {
+                             int split, float scale, hipStream_t stream) {
   using S = DqShape<T, D>;
   static bool attr = false;
   hipError_t e = raise_lds_limit(&s2attn_bwd_dq<T, D>, S::kLdsBytes, attr);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((s2attn_bwd_dq<T, D>), dim3(B * H * (N / S::kBR)), dim3(S::kThreads), S::kLdsBytes, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dq, N, H, Hkv, G,
-                     shift_heads, scale);
+                     shift_heads, split, scale);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                          const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
-                         hipStream_t stream) {
+                         int split, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
     // the fast kernel addresses one batch's K / V with 31-bit byte offsets
     if (G % DqB16Shape<D>::kBR == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
-      return launch_dq_bf16<D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, scale, stream);
+      return launch_dq_bf16<D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split, scale, stream);
   }
-  return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, scale, stream);
+  return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split, scale, stream);
 }
 
 #define S2A_INST_BWD(T, D)                                                                                 \
@@ -978,9 +999,9 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                                             int, int, hipStream_t);                                        \
   template hipError_t launch_bwd_dkdv<T, D>(const void*, const void*, const void*, const void*,           \
                                             const float*, const float*, void*, void*, int, int, int, int,  \
-                                            int, int, hipStream_t);                                        \
+                                            int, int, int, hipStream_t);                                   \
   template hipError_t launch_bwd_dq<T, D>(const void*, const void*, const void*, const void*, const float*, \
-                                          const float*, void*, int, int, int, int, int, int, hipStream_t);
+                                          const float*, void*, int, int, int, int, int, int, int, hipStream_t);
 S2A_INST_BWD(bf16, 64)
 S2A_INST_BWD(bf16, 128)
 S2A_INST_BWD(float, 64)

@@ -98,6 +98,24 @@ __device__ __forceinline__ int orig_row(int j, int sigma, int N) {
   return t >= N ? t - N : t;
 }
 
+// Wrap option of the shifted heads (page section 5, "Ablation Studies and
+// Robustness Checks", Table 8 / Figure 6, Variant 2).  With `split_head` (the
+// option is on and the head is shifted), the last rolled group -- the last G/2
+// tokens followed by the first G/2, which the roll carried from the front --
+// is cut at G/2 into two causal groups; every other group is unchanged.
+// Rows are in the head's rolled frame and G/2 is a multiple of 32, so a run of
+// 32 rows starting at j lies in one half.
+// First key row visible to the query rows starting at j:
+__device__ __forceinline__ int first_key_row(int j, int G, int N, bool split_head) {
+  const int gs = j - j % G;
+  return (split_head && gs == N - G && j - gs >= G / 2) ? gs + G / 2 : gs;
+}
+// One past the last query row that sees the key rows starting at j:
+__device__ __forceinline__ int query_end_row(int j, int G, int N, bool split_head) {
+  const int gs = j - j % G;
+  return (split_head && gs == N - G && j - gs < G / 2) ? gs + G / 2 : gs + G;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));

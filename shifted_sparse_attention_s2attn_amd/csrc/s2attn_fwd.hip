@@ -7,6 +7,8 @@
 // independent causal attention over G tokens; heads h >= H - shift_heads read
 // their tokens rolled by G/2, so rolled row j is original token (j + G/2) mod N,
 // and write their outputs back at the original rows (the roll-back).
+// With `split` (Table 8 / Figure 6, Variant 2) the shifted heads' last rolled
+// group is cut at G/2: its second-half queries start at key G/2 of the group.
 //
 // One workgroup = 4 waves = 128 consecutive query rows (rolled frame) of one
 // (batch, head).  Each wave owns 32 query rows; its Q operand stays in
@@ -45,7 +47,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     T* __restrict__ o, float* __restrict__ lse,
-    int N, int H, int Hkv, int G, int shift_heads, float scale) {
+    int N, int H, int Hkv, int G, int shift_heads, int split, float scale) {
   using S = FwdShape<T, D>;
   constexpr int BR = S::kBR, BC = S::kBC, KCPR = S::kKCPR, VCPR = S::kVCPR;
   constexpr int KPT = S::kKChunksPerThread, VKPT = S::kVKeysPerThread;
@@ -65,8 +67,9 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
 
+  const bool split_head = split && sigma != 0;
   const int j0 = grp * G + pos * BR;            // first query row (rolled)
-  const int kv_begin = grp * G;                 // first key row of the group (rolled)
+  const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
   const int ntiles = (j0 + BR - kv_begin) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
@@ -78,6 +81,7 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
   const int jw = j0 + wave * 32;                // wave's first query (rolled)
   const int jq = jw + l32;                      // this lane's query (rolled)
   const int tq = orig_row(jq, sigma, N);
+  const int kw0 = first_key_row(jw, G, N, split_head);        // ... and this wave's first key
   v8<T> qf[S::kDC];
 #pragma unroll
   for (int cc = 0; cc < S::kDC; ++cc)
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
     __syncthreads();
     if (it + 1 < ntiles) load_tile(kt0 + BC);
 
-    if (kt0 > jw + 31) continue;                // tile entirely after this wave's queries
+    if (kt0 > jw + 31 || kt0 < kw0) continue;   // tile after this wave's queries, or outside its group
     const bool need_mask = kt0 + BC - 1 > jw;
 
     // S^T = K Q^T
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
         mloc = fmaxf(mloc, s[ks][r]);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);     // finite: the group's first key is in the first tile
+    const float m_new = fmaxf(m_run, mloc);     // finite: the wave's first key is in its first tile
     const float alpha = fast_exp2((m_run - m_new) * c2);
     const float nm = -m_new * c2;
     float lsum = 0.f;
@@ -252,7 +256,7 @@ template <int D>
 __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse,
-    int N, int H, int Hkv, int G, int shift_heads, float scale) {
+    int N, int H, int Hkv, int G, int shift_heads, int split, float scale) {
   using S = FwdB16Shape<D>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTileChunks;
   constexpr int RB = D * 2;                       // bytes per tile row
@@ -275,8 +279,9 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   const int h = (to.pair / groups) % H, b = to.pair / (groups * H);
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
+  const bool split_head = split && sigma != 0;
   const int j0 = grp * G + pos * BR;
-  const int kv_begin = grp * G;
+  const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
   const int ntiles = (j0 + BR - kv_begin) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
@@ -287,6 +292,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
   const int tq = orig_row(jq, sigma, N);
+  const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
   bf16x8 qf[S::kDC];
   {
     const bf16* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
@@ -410,7 +416,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     wait_vmem_all();                             // this lane's tile loads have landed
     __syncthreads();                             // ... and everyone's; the other stage is free
     if (it + 1 < ntiles) issue_tile(kt0 + BC, STG ^ 1);
-    if (kt0 > jw + 31) return;                   // tile entirely after this wave's queries
+    if (kt0 > jw + 31 || kt0 < kw0) return;      // tile after this wave's queries, or outside its group
     if (kt0 + BC - 1 > jw)
       compute(stg_c, std::integral_constant<bool, true>(), kt0);
     else
@@ -438,31 +444,33 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
 
 template <int D>
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int H, int Hkv, int N, int G, int shift_heads, float scale, hipStream_t stream) {
+                           int B, int H, int Hkv, int N, int G, int shift_heads, int split, float scale,
+                           hipStream_t stream) {
   dim3 grid(B * H * (N / FwdB16Shape<D>::kBR));
   hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D>), grid, dim3(FwdB16Shape<D>::kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads, scale);
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads, split,
+                     scale);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int H, int Hkv, int N, int G, int shift_heads, hipStream_t stream) {
+                      int B, int H, int Hkv, int N, int G, int shift_heads, int split, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
     // the fast kernel addresses one batch's K / V with 31-bit byte offsets
     if (G % FwdB16Shape<D>::kBR == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
-      return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, scale, stream);
+      return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, split, scale, stream);
   }
   dim3 grid(B * H * (N / FwdShape<T, D>::kBR));
   hipLaunchKernelGGL((s2attn_fwd_kernel<T, D>), grid, dim3(256), 0, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, scale);
+                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, split, scale);
   return hipGetLastError();
 }
 
-template hipError_t launch_fwd<bf16, 64>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, hipStream_t);
-template hipError_t launch_fwd<bf16, 128>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, hipStream_t);
-template hipError_t launch_fwd<float, 64>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, hipStream_t);
-template hipError_t launch_fwd<float, 128>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, hipStream_t);
+template hipError_t launch_fwd<bf16, 64>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, int, hipStream_t);
+template hipError_t launch_fwd<bf16, 128>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, int, hipStream_t);
+template hipError_t launch_fwd<float, 64>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, int, hipStream_t);
+template hipError_t launch_fwd<float, 128>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, int, hipStream_t);
 
 }  // namespace s2a

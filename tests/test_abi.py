@@ -100,6 +100,27 @@ def test_grid_size_limit(lib):
     assert fwd_status(lib, B=1 << 20, H=1 << 10, Hkv=1 << 10, S=0, N=256) == _lib.S2ATTN_ERR_UNSUPPORTED
 
 
+def test_wrap_option_validation(lib):
+    """The _ex calls take wrap in {ROLL, SPLIT}; anything else is unsupported,
+    checked after the sizes and before the pointers."""
+    p = dict(GOOD)
+    dims = [p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"]]
+    need = lib.s2attn_bwd_workspace_bytes(*dims, 0)
+    for wrap, code in ((2, _lib.S2ATTN_ERR_UNSUPPORTED), (-1, _lib.S2ATTN_ERR_UNSUPPORTED),
+                       (_lib.S2ATTN_WRAP_SPLIT, _lib.S2ATTN_ERR_NULL), (_lib.S2ATTN_WRAP_ROLL, _lib.S2ATTN_ERR_NULL)):
+        assert lib.s2attn_fwd_ex(None, None, None, None, None, *dims, wrap, 0, None) == code
+        assert lib.s2attn_bwd_ex(*([None] * 10), need, *dims, wrap, 0, None) == code
+        assert lib.s2attn_bwd_dkdv_ex(*([None] * 7), need, *dims, wrap, 0, None) == code
+        assert lib.s2attn_bwd_dq_ex(*([None] * 6), need, *dims, wrap, 0, None) == code
+    bad = list(dims)
+    bad[3] = 500                                         # shape errors come first
+    assert lib.s2attn_fwd_ex(None, None, None, None, None, *bad, 7, 0, None) == _lib.S2ATTN_ERR_SHAPE
+    empty = list(dims)
+    empty[0] = 0                                         # empty problem: validated, then a no-op
+    assert lib.s2attn_fwd_ex(None, None, None, None, None, *empty, _lib.S2ATTN_WRAP_SPLIT, 0, None) == _lib.S2ATTN_OK
+    assert lib.s2attn_fwd_ex(None, None, None, None, None, *empty, 9, 0, None) == _lib.S2ATTN_ERR_UNSUPPORTED
+
+
 def test_mixed_shift_allowed_when_half_group_is_tile_aligned(lib):
     assert lib.s2attn_bwd_workspace_bytes(1, 6, 2, 1024, 64, 256, 2, 0) > 0
     assert lib.s2attn_bwd_workspace_bytes(1, 6, 2, 1024, 64, 128, 2, 0) == 0

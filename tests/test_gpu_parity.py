@@ -35,9 +35,9 @@ def to_gpu(inp):
     return {k: v.cuda() for k, v in inp.items()}
 
 
-def run_gpu(w, t):
-    o, lse = s2attn_fwd(t["q"], t["k"], t["v"], w.G, w.shift_heads)
-    dq, dk, dv = s2attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], w.G, w.shift_heads)
+def run_gpu(w, t, wrap="roll"):
+    o, lse = s2attn_fwd(t["q"], t["k"], t["v"], w.G, w.shift_heads, wrap=wrap)
+    dq, dk, dv = s2attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], w.G, w.shift_heads, wrap=wrap)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
@@ -50,12 +50,12 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
-def check_full(w, inp, out):
+def check_full(w, inp, out, wrap="roll"):
     tol = TOL[w.dtype]
     o, lse, dq, dk, dv = (f64(x) for x in out)
     q, k, v, do = (f64(inp[n]) for n in ("q", "k", "v", "do"))
-    o_ref, lse_ref = orc.forward(q, k, v, w.G, w.shift_heads)
-    dq_ref, dk_ref, dv_ref = orc.backward(q, k, v, do, w.G, w.shift_heads)
+    o_ref, lse_ref = orc.forward(q, k, v, w.G, w.shift_heads, wrap)
+    dq_ref, dk_ref, dv_ref = orc.backward(q, k, v, do, w.G, w.shift_heads, wrap)
     err_o = float(np.max(np.abs(o - o_ref)))
     err_lse = float(np.max(np.abs(lse - lse_ref)))
     errs = {n: rel_l2(a, b) for n, a, b in (("dq", dq, dq_ref), ("dk", dk, dk_ref), ("dv", dv, dv_ref))}
@@ -89,6 +89,24 @@ def test_small_parity(w):
     check_full(w, inp, out)
 
 
+# the split wrap option (Table 8, Variant 2) on every kernel path: bf16 fast
+# kernels (G a multiple of 256: the last group's G/2 boundary inside a 256-row
+# query tile; G = 128: inside a 128-key tile), the generic kernels (fp32, and
+# bf16 with G = 128), GQA with mixed shifts
+SPLIT = [w for w in SMALL if w.shift_heads > 0] + [
+    small_workload("bf16-g128-split", B=1, H=4, Hkv=2, d=128, N=512, G=128, shift_heads=2),
+    small_workload("bf16-d64-g384", B=1, H=2, Hkv=2, d=64, N=768, G=384, shift_heads=2),
+]
+
+
+@pytest.mark.parametrize("w", SPLIT, ids=[w.name for w in SPLIT])
+def test_small_parity_split(w):
+    say(f"case {w} wrap=split")
+    inp = make_inputs(w, seed=2)
+    out = run_gpu(w, to_gpu(inp), wrap="split")
+    check_full(w, inp, out, wrap="split")
+
+
 @pytest.mark.parametrize("seed", range(10))
 def test_tiny_f32_workload(seed):
     """B=1, H=4 (2 shifted), d=64, N=512, G=128, fp32; seeds 0-9."""
@@ -111,7 +129,7 @@ SAMPLES = {   # (key/value head, group index in the frame of that KV head's firs
 }
 
 
-def check_sampled(w, t, out, c, g0, b=0):
+def check_sampled(w, t, out, c, g0, b=0, wrap="roll"):
     tol = TOL[w.dtype]
     o, lse, dq, dk, dv = out
     r = w.H // w.Hkv
@@ -131,11 +149,11 @@ def check_sampled(w, t, out, c, g0, b=0):
         h = c * r + hh
         sig = orc.head_shift(hh, r, S_sub, G)
         for g in sorted(set(((R - sig) % N) // G)):
-            rows, Og, lseg = orc.head_group_forward(q, k, v, G, S_sub, b, hh, g)
+            rows, Og, lseg = orc.head_group_forward(q, k, v, G, S_sub, b, hh, g, wrap)
             ridx = torch.as_tensor(rows, device=o.device)
             o_err = max(o_err, float(np.max(np.abs(f64(o[b, ridx, h]) - Og))))
             lse_err = max(lse_err, float(np.max(np.abs(f64(lse[b, h, ridx]) - lseg))))
-            rows, dQg, dKg, dVg = orc.head_group_backward(q, k, v, do, G, S_sub, b, hh, g)
+            rows, dQg, dKg, dVg = orc.head_group_backward(q, k, v, do, G, S_sub, b, hh, g, wrap)
             dq_num += float(np.sum((f64(dq[b, ridx, h]) - dQg) ** 2))
             dq_den += float(np.sum(dQg ** 2))
             dk_acc[rows] += dKg
@@ -144,7 +162,7 @@ def check_sampled(w, t, out, c, g0, b=0):
     e_dk = rel_l2(f64(dk[b, Ridx, c]), dk_acc[R])
     e_dv = rel_l2(f64(dv[b, Ridx, c]), dv_acc[R])
     e_dq = (dq_num / dq_den) ** 0.5
-    say(f"  kv head {c} group {g0}: max|dO|={o_err:.3e} max|dlse|={lse_err:.3e} "
+    say(f"  kv head {c} group {g0} ({wrap}): max|dO|={o_err:.3e} max|dlse|={lse_err:.3e} "
         f"relL2 dq={e_dq:.3e} dk={e_dk:.3e} dv={e_dv:.3e}")
     assert o_err <= tol["o"]
     assert lse_err <= tol["lse"]
@@ -178,6 +196,23 @@ def test_full_size_workload(name):
         check_sampled(w, t, out, c, g0)
 
 
+def test_full_size_split():
+    """The split option at the 7B-32k size: the wrap group of a shifted head
+    (its group 3, whose second half is tokens 0..G/2-1) and a plain group."""
+    w = WORKLOADS["llama2-7b-32k"]
+    say(f"case {w} wrap=split (generating inputs on the GPU)")
+    t = make_inputs(w, seed=0, device="cuda")
+    out = run_gpu(w, t, wrap="split")
+    say("  kernels done")
+    for name, x in zip(("o", "lse", "dq", "dk", "dv"), out):
+        assert bool(torch.isfinite(x).all()), f"non-finite values in {name}"
+    # the first wrapped token of a shifted head attends to itself only
+    h = w.H - 1
+    assert torch.equal(out[0][:, 0, h], t["v"][:, 0, h // (w.H // w.Hkv)])
+    for c, g0 in [(31, 3), (0, 3)]:
+        check_sampled(w, t, out, c, g0, wrap="split")
+
+
 # ---------------------------------------------------------------------------
 # determinism, autograd wrapper, error path
 # ---------------------------------------------------------------------------
@@ -194,14 +229,15 @@ def test_repeatability():
     assert float((a[2].float() - b[2].float()).abs().max()) <= 1e-2
 
 
-def test_autograd_wrapper():
+@pytest.mark.parametrize("wrap", ["roll", "split"])
+def test_autograd_wrapper(wrap):
     w = small_workload("autograd", B=1, H=4, Hkv=4, d=64, N=512, G=256, shift_heads=2)
-    say(f"case {w}")
+    say(f"case {w} wrap={wrap}")
     t = to_gpu(make_inputs(w, seed=4))
     q, k, v = (t[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
-    o = s2attn(q, k, v, w.G, w.shift_heads)
+    o = s2attn(q, k, v, w.G, w.shift_heads, wrap=wrap)
     (o.float() * t["do"].float()).sum().backward()
-    ref = run_gpu(w, t)
+    ref = run_gpu(w, t, wrap=wrap)
     assert torch.equal(o, ref[0])
     assert torch.equal(k.grad, ref[3]) and torch.equal(v.grad, ref[4])
     assert float((q.grad.float() - ref[2].float()).abs().max()) <= 1e-2
