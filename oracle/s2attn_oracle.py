@@ -51,7 +51,8 @@ original token coordinates, a roll/regroup/causal-SDPA formulation, full causal
 attention at G = N without shift, exact invariance under reversing the roll
 direction, head-swap equivariance, closed forms (first row of each group),
 finite differences, GQA against repeated-KV MHA, and the worked index example
-of "The shifting mechanism".  The split wrap option is pinned by the same
+of "The shifting mechanism"; ``row_attention`` against the brute-force
+attention row by row.  The split wrap option is pinned by the same
 brute-force mask with the split partition, by causal SDPA over each split group
 as a contiguous token range, by finite differences, and by its agreement with
 the main method wherever the two partitions coincide.
@@ -65,7 +66,7 @@ __all__ = [
     "WRAPS", "check_problem", "head_shift", "kv_head", "rolled_order", "group_parts",
     "group_forward", "group_backward",
     "forward", "backward",
-    "head_group_forward", "head_group_backward",
+    "head_group_forward", "head_group_backward", "row_attention",
 ]
 
 
@@ -230,6 +231,43 @@ def head_group_backward(q, k, v, do, G, shift_heads, b, h, g, wrap="roll"):
         O, lse = group_forward(Qg, Kg, Vg, scale)
         dQ[part], dK[part], dV[part] = group_backward(Qg, Kg, Vg, O, lse, dOg, scale)
     return rows, dQ, dK, dV
+
+
+def row_attention(q, k, v, do, G, shift_heads, b, h, t, wrap="roll"):
+    """Everything about one query token t of head h, from its own row only.
+
+    The keys token t attends to are the tokens of its causal group that come at
+    or before it in the group's rolled order.  Returns a dict: ``keys`` (their
+    original indices, in that order), ``o`` and ``lse`` of token t, the row of
+    attention weights ``p`` and of score gradients ``ds`` over ``keys`` (for L =
+    sum(o * do)), and ``dq`` of token t.  Key/value gradients of key u are then
+    sums over the tokens whose ``keys`` contain u (p * do for dv, scale * ds * q
+    for dk), which is how long groups are checked a few rows at a time.
+    """
+    B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads, wrap)
+    sigma = head_shift(h, H, shift_heads, G)
+    order = rolled_order(N, sigma)
+    j = int(np.nonzero(order == t)[0][0])   # rolled position of token t
+    g = j // G
+    rows = order[g * G:(g + 1) * G]
+    pos = j - g * G
+    part = next(pt for pt in group_parts(rows, sigma, wrap) if pt.start <= pos < pt.stop)
+    keys = rows[part.start:pos + 1]
+    c = kv_head(h, H, Hkv)
+    scale = 1.0 / np.sqrt(d)
+    qt = np.asarray(q[b, t, h], dtype=np.float64)
+    dot = np.asarray(do[b, t, h], dtype=np.float64)
+    Kr = np.asarray(k[b, keys, c], dtype=np.float64)
+    Vr = np.asarray(v[b, keys, c], dtype=np.float64)
+    s = scale * (Kr @ qt)
+    m = s.max()
+    e = np.exp(s - m)
+    l = e.sum()
+    p = e / l
+    o = p @ Vr
+    dp = Vr @ dot
+    ds = p * (dp - np.dot(dot, o))
+    return {"keys": keys, "o": o, "lse": m + np.log(l), "p": p, "ds": ds, "dq": scale * (ds @ Kr)}
 
 
 def forward(q, k, v, G, shift_heads, wrap="roll"):

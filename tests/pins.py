@@ -514,9 +514,39 @@ def pin_split_finite_differences(orc):
         assert err <= 1e-6, f"split finite differences {name}: rel {err:.2e}"
 
 
+# ---------------------------------------------------------------------------
+# One token's row (used for sampled checks of long groups)
+# ---------------------------------------------------------------------------
+
+def pin_row_attention(orc):
+    """row_attention of every token against the brute-force dense attention:
+    o, lse and dq per row; dk and dv assembled from the rows' p and ds."""
+    for i, (B, N, H, Hkv, d, G, S) in enumerate(SMALL_CASES[:4] + [(1, 16, 2, 1, 3, 16, 0)]):
+        for split in (False, True):
+            q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=150 + i)
+            o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(q, k, v, G, S, grad_do=do,
+                                                                              split=split)
+            wrap = "split" if split else "roll"
+            dk = np.zeros_like(k)
+            dv = np.zeros_like(v)
+            r = H // Hkv
+            for b in range(B):
+                for h in range(H):
+                    for t in range(N):
+                        row = orc.row_attention(q, k, v, do, G, S, b, h, t, wrap)
+                        _close(row["o"], o_ref[b, t, h], 1e-12, f"row O case {i} {wrap}")
+                        _close(row["lse"], lse_ref[b, h, t], 1e-12, f"row lse case {i} {wrap}")
+                        _close(row["dq"], dq_ref[b, t, h], 1e-11, f"row dQ case {i} {wrap}")
+                        dv[b, row["keys"], h // r] += row["p"][:, None] * do[b, t, h][None, :]
+                        dk[b, row["keys"], h // r] += row["ds"][:, None] * q[b, t, h][None, :] / np.sqrt(d)
+            _close(dk, dk_ref, 1e-11, f"rows -> dK case {i} {wrap}")
+            _close(dv, dv_ref, 1e-11, f"rows -> dV case {i} {wrap}")
+
+
 ALL_PINS = [
     pin_bruteforce_forward, pin_bruteforce_backward, pin_roll_regroup, pin_full_causal,
     pin_direction_reversal, pin_head_swap, pin_closed_forms, pin_finite_differences,
     pin_gqa_repeat, pin_worked_example_index_map, pin_worked_example_reach,
     pin_split_bruteforce, pin_split_segments_sdpa, pin_split_agrees_with_roll, pin_split_finite_differences,
+    pin_row_attention,
 ]

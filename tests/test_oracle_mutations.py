@@ -47,6 +47,9 @@ MUTATIONS = [
     ("split-at-quarter", "cut = int(wraps[0]) + 1", "cut = (int(wraps[0]) + 1) // 2", 0),
     ("split-every-group", "        if len(wraps):\n            cut = int(wraps[0]) + 1",
      "        if True:\n            cut = len(rows) // 2", 0),
+    ("row-drops-own-key", "keys = rows[part.start:pos + 1]", "keys = rows[part.start:pos]", 0),
+    ("row-group-start", "keys = rows[part.start:pos + 1]", "keys = rows[0:pos + 1]", 0),
+    ("row-drops-dvec", "ds = p * (dp - np.dot(dot, o))", "ds = p * dp", 0),
     ("split-keeps-wrap-keys", "return [slice(0, cut), slice(cut, len(rows))]",
      "return [slice(0, cut), slice(0, len(rows))]", 0),
 ]
