@@ -73,7 +73,7 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, t, seconds):
+def cpu_baseline(w, t, seconds, wrap="roll"):
     """Time the float64 oracle (fwd + bwd) on whole (batch, head, group) slices of the inputs."""
     import numpy as np
     from oracle import s2attn_oracle as orc
@@ -88,8 +88,8 @@ def cpu_baseline(w, t, seconds):
         S1 = 1 if h >= w.H - w.shift_heads else 0
         for g in range(w.N // w.G):
             t0 = time.perf_counter()
-            orc.head_group_forward(q, k, v, w.G, S1, 0, 0, g)
-            orc.head_group_backward(q, k, v, do, w.G, S1, 0, 0, g)
+            orc.head_group_forward(q, k, v, w.G, S1, 0, 0, g, wrap)
+            orc.head_group_backward(q, k, v, do, w.G, S1, 0, 0, g, wrap)
             el += time.perf_counter() - t0
             done += 1
             flop += 14 * w.d * w.G * (w.G + 1) // 2
@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama2-7b-32k")
+    ap.add_argument("--wrap", default="roll", choices=["roll", "split"],
+                    help="wrap handling of the shifted heads (split: Table 8's Variant 2)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-reference", action="store_true")
@@ -172,16 +174,16 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        s2attn_fwd(q, k, v, w.G, w.shift_heads, out=o, lse=lse)
+        s2attn_fwd(q, k, v, w.G, w.shift_heads, out=o, lse=lse, wrap=args.wrap)
         if ev:
             ev[1].record(stream)
         s2attn_bwd_prep(q, k, o, lse, do, ws, w.G, w.shift_heads)
         if ev:
             ev[2].record(stream)
-        s2attn_bwd_dkdv(q, k, v, do, dk, dv, ws, w.G, w.shift_heads)
+        s2attn_bwd_dkdv(q, k, v, do, dk, dv, ws, w.G, w.shift_heads, wrap=args.wrap)
         if ev:
             ev[3].record(stream)
-        s2attn_bwd_dq(q, k, v, do, dq, ws, w.G, w.shift_heads)
+        s2attn_bwd_dq(q, k, v, do, dq, ws, w.G, w.shift_heads, wrap=args.wrap)
         if ev:
             ev[4].record(stream)
 
@@ -197,14 +199,14 @@ def main():
     ms_step = el * 1e3 / args.steps
 
     kern_ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
-    fwd_f = F.fwd_flops(w.B, w.H, w.N, w.G, w.d)
-    bwd_f = F.bwd_flops(w.B, w.H, w.N, w.G, w.d)
+    fwd_f = F.fwd_flops(w.B, w.H, w.N, w.G, w.d, w.shift_heads, args.wrap)
+    bwd_f = F.bwd_flops(w.B, w.H, w.N, w.G, w.d, w.shift_heads, args.wrap)
     peak = F.MI355X_BF16_PEAK_TFLOPS if w.dtype == "bf16" else F.MI355X_F32_PEAK_TFLOPS
     elt = 2 if w.dtype == "bf16" else 4
     # algorithmic FLOP per launch: the backward's five contractions are S, dP, dV, dK
     # (the dK/dV kernel, 8d per pair) and dQ (the dQ kernel, 2d per pair; that kernel
     # also recomputes S and dP, which are not counted again)
-    pairs = F.allowed_pairs(w.B, w.H, w.N, w.G)
+    pairs = F.allowed_pairs(w.B, w.H, w.N, w.G, w.shift_heads, args.wrap)
     kern_flops = {"fwd": fwd_f, "bwd_dkdv": 8 * w.d * pairs, "bwd_dq": 2 * w.d * pairs}
     dominant = max(kern_ms, key=kern_ms.get)
     kernels = {}
@@ -242,7 +244,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "d": w.d, "N": w.N, "G": w.G,
-                   "shift_heads": w.shift_heads, "parallelism": "none"},
+                   "shift_heads": w.shift_heads, "wrap": args.wrap, "parallelism": "none"},
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_f / fwd_ms / 1e9, 1),
                 "frac_of_peak": round(fwd_f / fwd_ms / 1e9 / peak, 4)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_f / bwd_ms / 1e9, 1),
@@ -267,7 +269,7 @@ def main():
             ref["roofline_kernel_frac"] = round(roof["achieved"] / ref["tflops"], 4)
         result["gemm_reference"] = ref
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds, args.wrap)
     print(json.dumps(result), flush=True)
 
 

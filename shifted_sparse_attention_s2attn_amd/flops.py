@@ -14,19 +14,26 @@ MI355X_F32_PEAK_TFLOPS = 157.3     # dense fp32 MFMA
 MI355X_HBM_PEAK_GBS = 8000.0
 
 
-def allowed_pairs(B, H, N, G):
-    """B * H * (N/G) groups, each a causal G x G triangle with G(G+1)/2 pairs."""
-    return B * H * (N // G) * G * (G + 1) // 2
+def allowed_pairs(B, H, N, G, shift_heads=0, wrap="roll"):
+    """B * H * (N/G) groups, each a causal G x G triangle with G(G+1)/2 pairs.
+
+    With the split wrap option each shifted head's wrap group loses the pairs of
+    its second-half queries with its first-half keys, (G/2)^2 of them.
+    """
+    pairs = B * H * (N // G) * G * (G + 1) // 2
+    if wrap == "split":
+        pairs -= B * shift_heads * (G // 2) ** 2
+    return pairs
 
 
-def fwd_flops(B, H, N, G, d):
+def fwd_flops(B, H, N, G, d, shift_heads=0, wrap="roll"):
     """QK^T (2d) and PV (2d) per allowed pair."""
-    return 4 * d * allowed_pairs(B, H, N, G)
+    return 4 * d * allowed_pairs(B, H, N, G, shift_heads, wrap)
 
 
-def bwd_flops(B, H, N, G, d):
+def bwd_flops(B, H, N, G, d, shift_heads=0, wrap="roll"):
     """Five contractions per allowed pair (QK^T, dO V^T, P^T dO, dS^T Q, dS K); recompute not counted."""
-    return 10 * d * allowed_pairs(B, H, N, G)
+    return 10 * d * allowed_pairs(B, H, N, G, shift_heads, wrap)
 
 
 def fwd_bytes(B, H, Hkv, N, d, elt):

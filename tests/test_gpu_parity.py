@@ -213,6 +213,49 @@ def test_full_size_split():
         check_sampled(w, t, out, c, g0, wrap="split")
 
 
+def test_full_size_full_attention():
+    """G = N = 102400, no shift: full causal attention at the 7B 100k shape.
+
+    One group holds the whole sequence, so the oracle checks rows: o, lse and dq
+    of sampled tokens of two heads, and dk, dv of the last 64 keys (which only
+    the last 64 tokens see), each from the tokens' own rows.
+    """
+    w = WORKLOADS["llama2-7b-100k-fullattn"]
+    tol = TOL[w.dtype]
+    say(f"case {w} (generating inputs on the GPU)")
+    t = make_inputs(w, seed=0, device="cuda")
+    o, lse, dq, dk, dv = run_gpu(w, t)
+    say("  kernels done")
+    N, d = w.N, w.d
+    for h in (0, w.H - 1):
+        # this head alone, as a one-head problem (its own KV head: H = Hkv here)
+        qh, kh, vh, doh = (f64(t[n][:, :, h:h + 1]) for n in ("q", "k", "v", "do"))
+        o_err = lse_err = 0.0
+        num = den = 0.0
+        for tok in (0, 1, 4095, 51200, N - 1):
+            row = orc.row_attention(qh, kh, vh, doh, N, 0, 0, 0, tok)
+            o_err = max(o_err, float(np.max(np.abs(f64(o[0, tok, h]) - row["o"]))))
+            lse_err = max(lse_err, abs(float(lse[0, h, tok]) - row["lse"]))
+            num += float(np.sum((f64(dq[0, tok, h]) - row["dq"]) ** 2))
+            den += float(np.sum(row["dq"] ** 2))
+        last = 64
+        dk_ref = np.zeros((last, d))
+        dv_ref = np.zeros((last, d))
+        for tok in range(N - last, N):
+            row = orc.row_attention(qh, kh, vh, doh, N, 0, 0, 0, tok)
+            sel = row["keys"] >= N - last
+            idx = row["keys"][sel] - (N - last)
+            dv_ref[idx] += row["p"][sel][:, None] * doh[0, tok, 0][None, :]
+            dk_ref[idx] += row["ds"][sel][:, None] * qh[0, tok, 0][None, :] / np.sqrt(d)
+        e_dk = rel_l2(f64(dk[0, N - last:, h]), dk_ref)
+        e_dv = rel_l2(f64(dv[0, N - last:, h]), dv_ref)
+        e_dq = (num / den) ** 0.5
+        say(f"  head {h}: max|dO|={o_err:.3e} max|dlse|={lse_err:.3e} relL2 dq={e_dq:.3e} "
+            f"dk={e_dk:.3e} dv={e_dv:.3e}")
+        assert o_err <= tol["o"] and lse_err <= tol["lse"]
+        assert e_dq <= tol["grad"] and e_dk <= tol["grad"] and e_dv <= tol["grad"]
+
+
 # ---------------------------------------------------------------------------
 # determinism, autograd wrapper, error path
 # ---------------------------------------------------------------------------

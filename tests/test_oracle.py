@@ -51,13 +51,14 @@ def test_table11_attention_flops():
         16 * flops.dense_fwd_attention_flops(2048, 2048, 128, 32, 32)
 
 
-@pytest.mark.parametrize("N,G,H,S", [(16, 8, 2, 1), (24, 8, 3, 2), (32, 32, 2, 0), (12, 4, 4, 4)])
-def test_pair_count_matches_bruteforce_mask(N, G, H, S):
+@pytest.mark.parametrize("wrap", ["roll", "split"])
+@pytest.mark.parametrize("N,G,H,S", [(16, 8, 2, 1), (24, 8, 3, 2), (32, 32, 2, 0), (12, 4, 4, 4), (16, 16, 2, 2)])
+def test_pair_count_matches_bruteforce_mask(N, G, H, S, wrap):
     """allowed_pairs counts exactly the entries the method lets attend."""
     total = 0
     for h in range(H):
-        total += int(pins.allowed_mask_original(N, G, h >= H - S).sum())
-    assert flops.allowed_pairs(1, H, N, G) == total
+        total += int(pins.allowed_mask_original(N, G, h >= H - S, wrap == "split").sum())
+    assert flops.allowed_pairs(1, H, N, G, S, wrap) == total
 
 
 @pytest.mark.parametrize("wrap", orc.WRAPS)
