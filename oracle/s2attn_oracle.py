@@ -32,6 +32,13 @@ Language Models", paper-graph-ui summary, section 3.4):
   to its start (the last one: the last G/2 tokens, then the first G/2) is cut
   at the wrap into two causal groups; every other group, and every unshifted
   head, is as in the main method (``wrap="roll"``).
+* Group sizes that do not divide the sequence (section 5, "Ablation Studies
+  and Robustness Checks", Table 7: a 1/6 group, 1365 tokens, at context 8192;
+  Algorithm 1's reshape needs N to be a multiple of G there, and the pages do
+  not say what was done).  Reading taken here: the (rolled) sequence is cut
+  into consecutive groups of G tokens and the last group holds the N mod G
+  tokens that remain; the shift is floor(G/2) tokens when G is odd.  Aligned
+  shapes (N a multiple of an even G) are unchanged by this reading.
 * Grouped-query attention (several query heads sharing one key/value head) is
   not on the pages; query head h reads key/value head h // (H // Hkv) and the
   key/value gradients are summed over the query heads that share them.
@@ -63,7 +70,7 @@ import numpy as np
 WRAPS = ("roll", "split")
 
 __all__ = [
-    "WRAPS", "check_problem", "head_shift", "kv_head", "rolled_order", "group_parts",
+    "WRAPS", "check_problem", "num_groups", "head_shift", "kv_head", "rolled_order", "group_parts",
     "group_forward", "group_backward",
     "forward", "backward",
     "head_group_forward", "head_group_backward", "row_attention",
@@ -73,23 +80,26 @@ __all__ = [
 def check_problem(B, N, H, Hkv, d, G, shift_heads, wrap="roll"):
     """Reject problems the method does not define.
 
-    Grouping views the sequence as N/G groups of G tokens (Algorithm 1's reshape
-    to [B*N/G, G, ...]) and the shift is G/2 tokens, so N must be a multiple of
-    G and G must be even.  ``wrap`` is "roll" (the main method) or "split".
+    Grouping cuts the sequence into groups of G tokens (Algorithm 1's reshape to
+    [B*N/G, G, ...]; a last, shorter group when G does not divide N), so G must
+    lie in [1, N].  ``wrap`` is "roll" (the main method) or "split".
     """
     if wrap not in WRAPS:
         raise ValueError(f"wrap must be one of {WRAPS}, got {wrap!r}")
     for name, val in (("B", B), ("N", N), ("H", H), ("Hkv", Hkv), ("d", d), ("G", G)):
         if val <= 0:
             raise ValueError(f"{name} must be positive, got {val}")
-    if N % G:
-        raise ValueError(f"N={N} is not a multiple of the group size G={G}")
-    if G % 2:
-        raise ValueError(f"G={G} must be even (the shift is G/2)")
+    if G > N:
+        raise ValueError(f"the group size G={G} exceeds the sequence length N={N}")
     if not 0 <= shift_heads <= H:
         raise ValueError(f"shift_heads={shift_heads} must lie in [0, H={H}]")
     if H % Hkv:
         raise ValueError(f"H={H} is not a multiple of Hkv={Hkv}")
+
+
+def num_groups(N, G):
+    """Groups of one head: N/G rounded up (the last one may be shorter)."""
+    return (N + G - 1) // G
 
 
 def head_shift(h, H, shift_heads, G):
@@ -196,8 +206,8 @@ def head_group_forward(q, k, v, G, shift_heads, b, h, g, wrap="roll"):
     sigma = head_shift(h, H, shift_heads, G)
     rows = rolled_order(N, sigma)[g * G:(g + 1) * G]
     c = kv_head(h, H, Hkv)
-    O = np.empty((G, d), dtype=np.float64)
-    lse = np.empty(G, dtype=np.float64)
+    O = np.empty((len(rows), d), dtype=np.float64)
+    lse = np.empty(len(rows), dtype=np.float64)
     for part in group_parts(rows, sigma, wrap):
         pr = rows[part]
         Qg = np.asarray(q[b, pr, h], dtype=np.float64)
@@ -219,9 +229,9 @@ def head_group_backward(q, k, v, do, G, shift_heads, b, h, g, wrap="roll"):
     rows = rolled_order(N, sigma)[g * G:(g + 1) * G]
     c = kv_head(h, H, Hkv)
     scale = 1.0 / np.sqrt(d)
-    dQ = np.empty((G, d), dtype=np.float64)
-    dK = np.empty((G, d), dtype=np.float64)
-    dV = np.empty((G, d), dtype=np.float64)
+    dQ = np.empty((len(rows), d), dtype=np.float64)
+    dK = np.empty((len(rows), d), dtype=np.float64)
+    dV = np.empty((len(rows), d), dtype=np.float64)
     for part in group_parts(rows, sigma, wrap):
         pr = rows[part]
         Qg = np.asarray(q[b, pr, h], dtype=np.float64)
@@ -283,7 +293,7 @@ def forward(q, k, v, G, shift_heads, wrap="roll"):
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            for g in range(N // G):
+            for g in range(num_groups(N, G)):
                 rows, Og, lseg = head_group_forward(q, k, v, G, shift_heads, b, h, g, wrap)
                 o[b, rows, h] = Og
                 lse[b, h, rows] = lseg
@@ -302,7 +312,7 @@ def backward(q, k, v, do, G, shift_heads, wrap="roll"):
     for b in range(B):
         for h in range(H):
             c = kv_head(h, H, Hkv)
-            for g in range(N // G):
+            for g in range(num_groups(N, G)):
                 rows, dQg, dKg, dVg = head_group_backward(q, k, v, do, G, shift_heads, b, h, g, wrap)
                 dq[b, rows, h] = dQg
                 dk[b, rows, c] += dKg

@@ -57,8 +57,11 @@ def allowed_mask_original(N, G, shifted, split=False):
     so groups are [kG + G/2, (k+1)G + G/2) taken cyclically; the last one holds
     the final G/2 tokens followed by the first G/2, in that order, and "earlier"
     means earlier in that order.  Shifted heads with ``split`` (Table 8's
-    Variant 2): the same boundaries without the wrap, so [0, G/2) and
-    [N - G/2, N) are groups of their own and "earlier" is plain token order.
+    Variant 2): additionally both tokens must lie on the same side of the wrap
+    (both among the first G/2 tokens, or both not), so for N a multiple of G the
+    groups are [0, G/2), [G/2 + jG, G/2 + (j+1)G) and [N - G/2, N).
+    When G does not divide N the groups are counted from the start of the
+    (shifted) grid and the last one is short; the shift is floor(G/2).
     """
     M = np.zeros((N, N), dtype=bool)
     half = G // 2
@@ -68,8 +71,10 @@ def allowed_mask_original(N, G, shifted, split=False):
                 same = (t // G) == (u // G)
                 before = u <= t
             elif split:
-                same = ((t + half) // G) == ((u + half) // G)
-                before = u <= t
+                ot = (t - half) % N
+                ou = (u - half) % N
+                same = (ot // G) == (ou // G) and ((t < half) == (u < half))
+                before = ou <= ot
             else:
                 # offset of each token from the start of the shifted grid
                 ot = (t - half) % N
@@ -521,7 +526,7 @@ def pin_split_finite_differences(orc):
 def pin_row_attention(orc):
     """row_attention of every token against the brute-force dense attention:
     o, lse and dq per row; dk and dv assembled from the rows' p and ds."""
-    for i, (B, N, H, Hkv, d, G, S) in enumerate(SMALL_CASES[:4] + [(1, 16, 2, 1, 3, 16, 0)]):
+    for i, (B, N, H, Hkv, d, G, S) in enumerate(SMALL_CASES[:4] + [(1, 16, 2, 1, 3, 16, 0), (1, 23, 3, 3, 4, 7, 2)]):
         for split in (False, True):
             q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=150 + i)
             o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(q, k, v, G, S, grad_do=do,
@@ -543,10 +548,78 @@ def pin_row_attention(orc):
             _close(dv, dv_ref, 1e-11, f"rows -> dV case {i} {wrap}")
 
 
+# ---------------------------------------------------------------------------
+# Group sizes that do not divide the sequence (Table 7's 1/6 group): the last
+# group is short, the shift is floor(G/2)
+# ---------------------------------------------------------------------------
+
+UNALIGNED_CASES = [   # (B, N, H, Hkv, d, G, S)
+    (1, 30, 2, 2, 4, 8, 1),      # remainder 6
+    (1, 21, 2, 1, 3, 7, 2),      # odd G dividing N
+    (1, 23, 3, 3, 4, 7, 2),      # odd G, remainder 2
+    (1, 13, 2, 2, 3, 13, 1),     # G = N, odd
+    (2, 18, 2, 2, 2, 5, 1),      # remainder 3, B = 2
+    (1, 9, 2, 2, 3, 1, 2),       # G = 1: every token alone
+    (1, 26, 4, 2, 3, 6, 2),      # GQA, remainder 2
+]
+
+
+def pin_unaligned_bruteforce(orc):
+    for i, (B, N, H, Hkv, d, G, S) in enumerate(UNALIGNED_CASES):
+        for split in (False, True):
+            q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=160 + i)
+            wrap = "split" if split else "roll"
+            o, lse = orc.forward(q, k, v, G, S, wrap)
+            dq, dk, dv = orc.backward(q, k, v, do, G, S, wrap)
+            o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(q, k, v, G, S, grad_do=do,
+                                                                              split=split)
+            _close(o, o_ref, 1e-12, f"unaligned brute-force O case {i} {wrap}")
+            _close(lse, lse_ref, 1e-12, f"unaligned brute-force lse case {i} {wrap}")
+            _close(dq, dq_ref, 1e-11, f"unaligned brute-force dQ case {i} {wrap}")
+            _close(dk, dk_ref, 1e-11, f"unaligned brute-force dK case {i} {wrap}")
+            _close(dv, dv_ref, 1e-11, f"unaligned brute-force dV case {i} {wrap}")
+
+
+def pin_unaligned_cut_sdpa(orc):
+    """Roll the shifted heads by floor(G/2), cut the sequence at every multiple
+    of G (and, for split, at the wrap), run torch's causal SDPA on every piece,
+    roll back; autograd for the gradients."""
+    for i, (B, N, H, Hkv, d, G, S) in enumerate(UNALIGNED_CASES):
+        for split in (False, True):
+            q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=170 + i)
+            wrap = "split" if split else "roll"
+            o, _ = orc.forward(q, k, v, G, S, wrap)
+            dq, dk, dv = orc.backward(q, k, v, do, G, S, wrap)
+            r = H // Hkv
+            tq = torch.tensor(q, requires_grad=True)
+            tk = torch.tensor(k, requires_grad=True)
+            tv = torch.tensor(v, requires_grad=True)
+            kk = torch.repeat_interleave(tk, r, dim=2)
+            vv = torch.repeat_interleave(tv, r, dim=2)
+            heads = []
+            for h in range(H):
+                sh = G // 2 if h >= H - S else 0
+                xs = [torch.roll(x[:, :, h], -sh, dims=1) for x in (tq, kk, vv)]
+                cuts = set(range(0, N, G)) | {N}
+                if split and sh:
+                    cuts.add(N - sh)
+                cuts = sorted(cuts)
+                pieces = [F.scaled_dot_product_attention(xs[0][:, a:e][:, None], xs[1][:, a:e][:, None],
+                                                         xs[2][:, a:e][:, None], is_causal=True)[:, 0]
+                          for a, e in zip(cuts[:-1], cuts[1:])]
+                heads.append(torch.roll(torch.cat(pieces, dim=1), sh, dims=1))
+            ref = torch.stack(heads, dim=2)
+            (ref * torch.tensor(do)).sum().backward()
+            _close(o, ref.detach().numpy(), 1e-12, f"cut/SDPA O case {i} {wrap}")
+            _close(dq, tq.grad.numpy(), 1e-11, f"cut/SDPA dQ case {i} {wrap}")
+            _close(dk, tk.grad.numpy(), 1e-11, f"cut/SDPA dK case {i} {wrap}")
+            _close(dv, tv.grad.numpy(), 1e-11, f"cut/SDPA dV case {i} {wrap}")
+
+
 ALL_PINS = [
     pin_bruteforce_forward, pin_bruteforce_backward, pin_roll_regroup, pin_full_causal,
     pin_direction_reversal, pin_head_swap, pin_closed_forms, pin_finite_differences,
     pin_gqa_repeat, pin_worked_example_index_map, pin_worked_example_reach,
     pin_split_bruteforce, pin_split_segments_sdpa, pin_split_agrees_with_roll, pin_split_finite_differences,
-    pin_row_attention,
+    pin_row_attention, pin_unaligned_bruteforce, pin_unaligned_cut_sdpa,
 ]

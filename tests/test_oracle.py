@@ -16,8 +16,7 @@ def test_pin(pin):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(N=30, G=8),          # N not a multiple of G
-    dict(N=21, G=7),          # odd G
+    dict(N=8, G=16),          # group longer than the sequence
     dict(S=5),                # more shifted heads than heads
     dict(S=-1),
     dict(Hkv=3),              # H not a multiple of Hkv

@@ -50,6 +50,9 @@ MUTATIONS = [
     ("row-drops-own-key", "keys = rows[part.start:pos + 1]", "keys = rows[part.start:pos]", 0),
     ("row-group-start", "keys = rows[part.start:pos + 1]", "keys = rows[0:pos + 1]", 0),
     ("row-drops-dvec", "ds = p * (dp - np.dot(dot, o))", "ds = p * dp", 0),
+    ("groups-rounded-down", "return (N + G - 1) // G", "return N // G", 0),
+    ("odd-shift-rounded-up", "return G // 2 if h >= H - shift_heads else 0",
+     "return (G + 1) // 2 if h >= H - shift_heads else 0", 0),
     ("split-keeps-wrap-keys", "return [slice(0, cut), slice(cut, len(rows))]",
      "return [slice(0, cut), slice(0, len(rows))]", 0),
 ]
@@ -81,10 +84,17 @@ def test_pins_catch_planted_mistake(mutation):
 
 
 def test_direction_reversal_is_not_a_mistake():
-    """Every output is invariant; only the index map itself shows the direction."""
+    """Every output is invariant; only the index map itself shows the direction.
+
+    That holds when G divides N (the two rolls differ by one whole group).  When
+    it does not, the reversed roll puts the group grid elsewhere, so the
+    unaligned pins must notice it (the pages' direction, -G/2, is the one taken).
+    """
     mod = _mutant(*NEUTRAL)
+    direction_sensitive = (pins.pin_worked_example_index_map, pins.pin_unaligned_bruteforce,
+                           pins.pin_unaligned_cut_sdpa)
     for pin in pins.ALL_PINS:
-        if pin is pins.pin_worked_example_index_map:
+        if pin in direction_sensitive:
             with pytest.raises(AssertionError):
                 pin(mod)
         else:
