@@ -523,10 +523,10 @@ def pin_split_finite_differences(orc):
 # One token's row (used for sampled checks of long groups)
 # ---------------------------------------------------------------------------
 
-def pin_row_attention(orc):
+def pin_row_attention(orc, cases=SMALL_CASES[:4] + [(1, 16, 2, 1, 3, 16, 0)]):
     """row_attention of every token against the brute-force dense attention:
     o, lse and dq per row; dk and dv assembled from the rows' p and ds."""
-    for i, (B, N, H, Hkv, d, G, S) in enumerate(SMALL_CASES[:4] + [(1, 16, 2, 1, 3, 16, 0), (1, 23, 3, 3, 4, 7, 2)]):
+    for i, (B, N, H, Hkv, d, G, S) in enumerate(cases):
         for split in (False, True):
             q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=150 + i)
             o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(q, k, v, G, S, grad_do=do,
@@ -580,6 +580,10 @@ def pin_unaligned_bruteforce(orc):
             _close(dv, dv_ref, 1e-11, f"unaligned brute-force dV case {i} {wrap}")
 
 
+def pin_unaligned_row_attention(orc):
+    pin_row_attention(orc, cases=[(1, 23, 3, 3, 4, 7, 2), (1, 26, 4, 2, 3, 6, 2)])
+
+
 def pin_unaligned_cut_sdpa(orc):
     """Roll the shifted heads by floor(G/2), cut the sequence at every multiple
     of G (and, for split, at the wrap), run torch's causal SDPA on every piece,
@@ -621,5 +625,5 @@ ALL_PINS = [
     pin_direction_reversal, pin_head_swap, pin_closed_forms, pin_finite_differences,
     pin_gqa_repeat, pin_worked_example_index_map, pin_worked_example_reach,
     pin_split_bruteforce, pin_split_segments_sdpa, pin_split_agrees_with_roll, pin_split_finite_differences,
-    pin_row_attention, pin_unaligned_bruteforce, pin_unaligned_cut_sdpa,
+    pin_row_attention, pin_unaligned_bruteforce, pin_unaligned_cut_sdpa, pin_unaligned_row_attention,
 ]

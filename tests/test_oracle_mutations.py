@@ -92,7 +92,7 @@ def test_direction_reversal_is_not_a_mistake():
     """
     mod = _mutant(*NEUTRAL)
     direction_sensitive = (pins.pin_worked_example_index_map, pins.pin_unaligned_bruteforce,
-                           pins.pin_unaligned_cut_sdpa)
+                           pins.pin_unaligned_cut_sdpa, pins.pin_unaligned_row_attention)
     for pin in pins.ALL_PINS:
         if pin in direction_sensitive:
             with pytest.raises(AssertionError):
