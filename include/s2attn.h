@@ -16,6 +16,11 @@
  *     holds tokens N-G/2..N-1 followed by tokens 0..G/2-1.
  *   - Grouped-query attention (not on the pages): query head h reads key/value
  *     head h / (H / Hkv); dk and dv sum over the query heads sharing them.
+ *   - Group sizes that do not divide the sequence (section 5, "Ablation
+ *     Studies and Robustness Checks", Table 7's 1/6 group; the pages do not say
+ *     how it was cut): the rolled sequence is cut into consecutive groups of G
+ *     tokens, the last one holding the N mod G tokens left; for odd G the shift
+ *     is floor(G/2).
  * The roll is never materialised: it is folded into the row addresses of every
  * tile load and store, so all tensors stay in original token order.
  *
@@ -34,9 +39,12 @@
  *
  * Supported: d in {64, 128}; dtype bf16 (fp32 accumulation, P and dS rounded
  * to bf16 for the matrix cores) or fp32 (fp32 matrix cores throughout);
- * G a multiple of 128; N a multiple of G; when a key/value head is shared by
- * shifted and unshifted query heads (H - shift_heads not a multiple of
- * H / Hkv), G must also be a multiple of 256; B * H * N / 128 < 2^31.
+ * 1 <= G <= N.  Shapes whose groups are whole 128-row tiles (G a multiple of
+ * 128, N a multiple of G) run the fast bf16 kernels; any other G runs the
+ * generic kernels.  When a key/value head is shared by shifted and unshifted
+ * query heads (H - shift_heads not a multiple of H / Hkv), and for the split
+ * wrap option, the groups must be whole tiles (for the shared head, G a
+ * multiple of 256).  Grids: B * H * ceil(N / G) * ceil(G / 128) < 2^31.
  * B == 0 or N == 0 is an empty problem: every call validates the other sizes,
  * then returns S2ATTN_OK without reading any pointer or touching the GPU.
  */
@@ -57,10 +65,10 @@ typedef enum {
 typedef enum {
     S2ATTN_OK = 0,
     S2ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
-    S2ATTN_ERR_SHAPE = 2,        /* B or N < 0, H, Hkv, d or G <= 0, N % G != 0, G odd,
+    S2ATTN_ERR_SHAPE = 2,        /* B or N < 0, H, Hkv, d or G <= 0, G > N (N > 0),
                                     shift_heads outside [0, H], H % Hkv != 0 */
-    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype or wrap option, G % 128 != 0, the
-                                    mixed-shift rule above, or B * H * N / 128 >= 2^31 */
+    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype or wrap option, the mixed-shift or
+                                    split rule above, or the grid size limit */
     S2ATTN_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError) */
     S2ATTN_ERR_WORKSPACE = 5     /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
 } s2attn_status;

@@ -25,29 +25,37 @@ namespace {
 
 constexpr int kTileRows = 128;   // query rows per forward workgroup = key rows per backward workgroup
 
+// Whole groups of whole 128-row tiles.  Other shapes (G not dividing N, so the
+// last group is short, or G not a multiple of 128) run on the generic kernels.
+bool aligned(int N, int G) { return N % G == 0 && G % kTileRows == 0; }
+
 // Sizes only (no pointers).  B == 0 or N == 0 is a valid, empty problem.
 int check_problem(int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype) {
   if (B < 0 || N < 0 || H <= 0 || Hkv <= 0 || d <= 0 || G <= 0) return S2ATTN_ERR_SHAPE;
-  if (N % G != 0 || G % 2 != 0) return S2ATTN_ERR_SHAPE;
+  if (N > 0 && G > N) return S2ATTN_ERR_SHAPE;
   if (shift_heads < 0 || shift_heads > H) return S2ATTN_ERR_SHAPE;
   if (H % Hkv != 0) return S2ATTN_ERR_SHAPE;
-  // one-dimensional grids of (batch, head, 128-row tile) blocks
-  if ((size_t)B * H * (size_t)(N / kTileRows) > (size_t)INT32_MAX) return S2ATTN_ERR_UNSUPPORTED;
+  // one-dimensional grids of (batch, head, group, 128-row tile) blocks
+  const size_t blocks = (size_t)B * H * (size_t)((N + G - 1) / G) * (size_t)((G + kTileRows - 1) / kTileRows);
+  if (blocks > (size_t)INT32_MAX) return S2ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return S2ATTN_ERR_UNSUPPORTED;
   if (dtype != S2ATTN_BF16 && dtype != S2ATTN_F32) return S2ATTN_ERR_UNSUPPORTED;
-  if (G % kTileRows != 0) return S2ATTN_ERR_UNSUPPORTED;
   const int r = H / Hkv;
   // A key/value head read by both shifted and unshifted query heads is tiled in
   // the first head's frame; the other frame is offset by G/2, which must then
-  // be a whole number of tiles.
-  if (r > 1 && (H - shift_heads) % r != 0 && (G / 2) % kTileRows != 0) return S2ATTN_ERR_UNSUPPORTED;
+  // be a whole number of tiles of whole groups.
+  if (r > 1 && (H - shift_heads) % r != 0 && (!aligned(N, G) || (G / 2) % kTileRows != 0))
+    return S2ATTN_ERR_UNSUPPORTED;
   return S2ATTN_OK;
 }
 
 bool empty_problem(int B, int N) { return B == 0 || N == 0; }
 
-int check_wrap(int wrap) {
-  return (wrap == S2ATTN_WRAP_ROLL || wrap == S2ATTN_WRAP_SPLIT) ? S2ATTN_OK : S2ATTN_ERR_UNSUPPORTED;
+// The split option cuts the last group at G/2; it needs aligned shapes.
+int check_wrap(int wrap, int N, int G) {
+  if (wrap == S2ATTN_WRAP_ROLL) return S2ATTN_OK;
+  if (wrap == S2ATTN_WRAP_SPLIT) return (N == 0 || aligned(N, G)) ? S2ATTN_OK : S2ATTN_ERR_UNSUPPORTED;
+  return S2ATTN_ERR_UNSUPPORTED;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -59,7 +67,7 @@ extern "C" {
 int s2attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype, void* stream) {
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
-  if (st == S2ATTN_OK) st = check_wrap(wrap);
+  if (st == S2ATTN_OK) st = check_wrap(wrap, N, G);
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !o || !lse) return S2ATTN_ERR_NULL;
@@ -157,7 +165,7 @@ int s2attn_bwd_dkdv_ex(const void* q, const void* k, const void* v, const void* 
                        int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype,
                        void* stream) {
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
-  if (st == S2ATTN_OK) st = check_wrap(wrap);
+  if (st == S2ATTN_OK) st = check_wrap(wrap, N, G);
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !dO || !dk || !dv) return S2ATTN_ERR_NULL;
@@ -180,7 +188,7 @@ int s2attn_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO
                      int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype,
                      void* stream) {
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
-  if (st == S2ATTN_OK) st = check_wrap(wrap);
+  if (st == S2ATTN_OK) st = check_wrap(wrap, N, G);
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !dO || !dq) return S2ATTN_ERR_NULL;
@@ -202,7 +210,7 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, co
                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                   int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype, void* stream) {
   int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
-  if (st == S2ATTN_OK) st = check_wrap(wrap);
+  if (st == S2ATTN_OK) st = check_wrap(wrap, N, G);
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
@@ -227,8 +235,8 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
 const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_OK: return "ok";
     case S2ATTN_ERR_NULL: return "a required pointer is NULL";
-    case S2ATTN_ERR_SHAPE: return "invalid shape (size <= 0, N % G != 0, odd G, shift_heads outside [0,H], or H % Hkv != 0)";
-    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, G % 128 != 0, mixed-shift KV head with (G/2) % 128 != 0, or grid too large)";
+    case S2ATTN_ERR_SHAPE: return "invalid shape (a size < 0, H, Hkv, d or G <= 0, G > N, shift_heads outside [0,H], or H % Hkv != 0)";
+    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, or grid too large)";
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     default: return "unknown status";

@@ -120,22 +120,26 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   const int l32 = lane & 31, hf = lane >> 5;
 
   // Key tiles at the start of a group meet the most queries: dispatched first.
-  const int groups = N / G, tiles_per_group = G / BKV;
+  const int groups = num_groups(N, G), tiles_per_group = (G + BKV - 1) / BKV;
   const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
   const int pos = to.rank, grp = to.pair % groups;
   const int c = (to.pair / groups) % Hkv, b = to.pair / (groups * Hkv);
   const int r = H / Hkv;
   const int h0 = c * r;
   const int sig0 = (h0 >= H - shift_heads) ? G / 2 : 0;
+  const int ge0 = min(grp * G + G, N);          // end of the group (a last group may be short)
   const int j0 = grp * G + pos * BKV;           // first key row, rolled frame of head h0
+  if (j0 >= ge0) return;                        // a tile past the end of a short group
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
   const T* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
   const T* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
 
-  // this wave's 32 keys as B operands (key on lanes, head dim in k-slots)
+  // this wave's 32 keys as B operands (key on lanes, head dim in k-slots);
+  // keys past the group compute on a copy of its last row and are not stored
   const int key_local = wave * 32 + l32;
-  const int tk = orig_row(j0 + key_local, sig0, N);
+  const bool k_ok = j0 + key_local < ge0;
+  const int tk = orig_row(k_ok ? j0 + key_local : ge0 - 1, sig0, N);
   v8<T> kf[S::kDC], vf[S::kDC];
 #pragma unroll
   for (int cc = 0; cc < S::kDC; ++cc) {
@@ -160,7 +164,10 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     if (jk0 >= N) jk0 -= N;
     const bool split_head = split && sig != 0;
     // query tiles meeting the workgroup's keys, and the end of this wave's queries
-    const int qt_begin = jk0 / BQ, qt_end = query_end_row(jk0 + BKV - 32, G, N, split_head) / BQ;
+    // (queries from the next group in the last tile are masked)
+    const int q_end_g = query_end_row(jk0, G, N, false);
+    const int qt_begin = jk0 / BQ;
+    const int qt_end = (min(query_end_row(jk0 + BKV - 32, G, N, split_head), q_end_g) + BQ - 1) / BQ;
     const int q_end_w = query_end_row(jk0 + wave * 32, G, N, split_head);
     const T* qb = q + (size_t)b * N * qstride + (size_t)h * D;
     const T* dob = dO + (size_t)b * N * qstride + (size_t)h * D;
@@ -173,12 +180,12 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     auto load_q = [&](int jq0) {
 #pragma unroll
       for (int i = 0; i < QRPT; ++i) {
-        const int t = orig_row(jq0 + q_qg * QRPT + i, sig, N);
+        const int t = orig_row(min(jq0 + q_qg * QRPT + i, N - 1), sig, N);   // rows past N are masked
         qr[i] = *reinterpret_cast<const v8<T>*>(qb + (size_t)t * qstride + q_dc * 8);
         dr[i] = *reinterpret_cast<const v8<T>*>(dob + (size_t)t * qstride + q_dc * 8);
       }
       if (tid < BQ) {
-        const int t = orig_row(jq0 + tid, sig, N);
+        const int t = orig_row(min(jq0 + tid, N - 1), sig, N);
         lse_r = lse_h[t];
         dvec_r = dvec_h[t];
       }
@@ -215,14 +222,14 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
         }
       }
       // P and dS
-      const bool need_mask = jk0 + wave * 32 + 31 > jq0;
+      const bool need_mask = jk0 + wave * 32 + 31 > jq0 || jq0 + BQ > q_end_g;
 #pragma unroll
       for (int qs = 0; qs < NQS; ++qs)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qi = qs * 32 + (i >> 3) * 16 + hf * 8 + (i & 7);
           float p = fast_exp2(fmaf(sacc[qs][i], c2, -lse_s[qi]));
-          if (need_mask && jkey > jq0 + qi) p = 0.f;
+          if (need_mask && (jkey > jq0 + qi || jq0 + qi >= q_end_g)) p = 0.f;
           sacc[qs][i] = p;
           pacc[qs][i] = p * (pacc[qs][i] - dvec_s[qi]);
         }
@@ -242,6 +249,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     __syncthreads();                            // next head restages the tiles
   }
 
+  if (!k_ok) return;
   T* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
   T* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
 #pragma unroll
@@ -290,7 +298,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
 
-  const int groups = N / G, tiles_per_group = G / BR;
+  const int groups = num_groups(N, G), tiles_per_group = (G + BR - 1) / BR;
   const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
   const int pos = tiles_per_group - 1 - to.rank;   // heaviest query tiles first
   const int grp = to.pair % groups;
@@ -298,18 +306,22 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
   const bool split_head = split && sigma != 0;
+  const int ge = min(grp * G + G, N);           // end of the group (a last group may be short)
   const int j0 = grp * G + pos * BR;
+  if (j0 >= ge) return;                         // a tile past the end of a short group
   const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
-  const int ntiles = (j0 + BR - kv_begin) / BC;
+  const int ntiles = (min(j0 + BR, ge) - kv_begin + BC - 1) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
   const T* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
   const T* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
 
-  // Q and dO operands (B of S^T = K Q^T and dP^T = V dO^T): query on lanes
+  // Q and dO operands (B of S^T = K Q^T and dP^T = V dO^T): query on lanes;
+  // rows past the group compute on a copy of its last row and are not stored
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
-  const int tq = orig_row(jq, sigma, N);
+  const bool q_ok = jq < ge;
+  const int tq = orig_row(q_ok ? jq : ge - 1, sigma, N);
   const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
   v8<T> qf[S::kDC], dof[S::kDC];
   {
@@ -329,7 +341,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   auto load_tile = [&](int kt0) {
 #pragma unroll
     for (int i = 0; i < KRPT; ++i) {
-      const int t = orig_row(kt0 + k_kg * KRPT + i, sigma, N);
+      const int t = orig_row(min(kt0 + k_kg * KRPT + i, N - 1), sigma, N);   // rows past N are masked keys
       kr[i] = *reinterpret_cast<const v8<T>*>(kb + (size_t)t * kvstride + k_dc * 8);
       vr[i] = *reinterpret_cast<const v8<T>*>(vb + (size_t)t * kvstride + k_dc * 8);
     }
@@ -355,7 +367,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
     store_transposed<T, KRPT, TCPR>(Kt, kr, k_dc, k_kg * KRPT);
     __syncthreads();
     if (it + 1 < ntiles) load_tile(kt0 + BC);
-    if (kt0 > jw + 31 || kt0 < kw0) continue;   // tile after this wave's queries, or outside its group
+    if (kt0 > jw + 31 || kt0 < kw0 || jw >= ge) continue;   // nothing of this tile for this wave
 
     // S^T = K Q^T, dP^T = V dO^T : keys on tile rows, queries on lanes
     f32x16 s[2], dp[2];
@@ -391,6 +403,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
     }
   }
 
+  if (!q_ok) return;
   T* dqrow = dq + ((size_t)b * N + tq) * qstride + (size_t)h * D;
 #pragma unroll
   for (int dt = 0; dt < S::kDT; ++dt)
@@ -937,7 +950,8 @@ hipError_t launch_dkdv_generic(const void* q, const void* k, const void* v, cons
   static bool attr = false;
   hipError_t e = raise_lds_limit(&s2attn_bwd_dkdv<T, D>, S::kLdsBytes, attr);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), dim3(B * Hkv * (N / S::kBKV)), dim3(S::kThreads), S::kLdsBytes,
+  const dim3 grid(B * Hkv * ((N + G - 1) / G) * ((G + S::kBKV - 1) / S::kBKV));
+  hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), grid, dim3(S::kThreads), S::kLdsBytes,
                      stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dk, (T*)dv, N,
                      H, Hkv, G, shift_heads, split, scale);
   return hipGetLastError();
@@ -949,8 +963,9 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            int shift_heads, int split, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
-    // the fast kernel addresses one batch's Q / dO with 31-bit byte offsets
-    if ((size_t)N * H * D * sizeof(T) < (size_t(1) << 31))
+    // the fast kernel takes whole 128-key tiles of whole groups, and addresses
+    // one batch's Q / dO with 31-bit byte offsets
+    if (G % DkdvB16Shape<D>::kBKV == 0 && N % G == 0 && (size_t)N * H * D * sizeof(T) < (size_t(1) << 31))
       return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, split, scale, stream);
   }
   return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, split, scale, stream);
@@ -975,7 +990,8 @@ hipError_t launch_dq_generic(const void* q, const void* k, const void* v, const 
   static bool attr = false;
   hipError_t e = raise_lds_limit(&s2attn_bwd_dq<T, D>, S::kLdsBytes, attr);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((s2attn_bwd_dq<T, D>), dim3(B * H * (N / S::kBR)), dim3(S::kThreads), S::kLdsBytes, stream,
+  const dim3 grid(B * H * ((N + G - 1) / G) * ((G + S::kBR - 1) / S::kBR));
+  hipLaunchKernelGGL((s2attn_bwd_dq<T, D>), grid, dim3(S::kThreads), S::kLdsBytes, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dq, N, H, Hkv, G,
                      shift_heads, split, scale);
   return hipGetLastError();
@@ -987,8 +1003,9 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          int split, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
-    // the fast kernel addresses one batch's K / V with 31-bit byte offsets
-    if (G % DqB16Shape<D>::kBR == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
+    // the fast kernel takes whole 256-row tiles of whole groups, and addresses
+    // one batch's K / V with 31-bit byte offsets
+    if (G % DqB16Shape<D>::kBR == 0 && N % G == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
       return launch_dq_bf16<D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split, scale, stream);
   }
   return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split, scale, stream);

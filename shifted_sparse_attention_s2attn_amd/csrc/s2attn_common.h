@@ -98,6 +98,11 @@ __device__ __forceinline__ int orig_row(int j, int sigma, int N) {
   return t >= N ? t - N : t;
 }
 
+// Groups of one head: N / G rounded up.  When G does not divide N the last
+// group holds the N mod G rows that remain (the reading taken for group sizes
+// like Table 7's 1/6 of the context); such shapes run on the generic kernels.
+__device__ __forceinline__ int num_groups(int N, int G) { return (N + G - 1) / G; }
+
 // Wrap option of the shifted heads (page section 5, "Ablation Studies and
 // Robustness Checks", Table 8 / Figure 6, Variant 2).  With `split_head` (the
 // option is on and the head is shifted), the last rolled group -- the last G/2
@@ -110,10 +115,11 @@ __device__ __forceinline__ int first_key_row(int j, int G, int N, bool split_hea
   const int gs = j - j % G;
   return (split_head && gs == N - G && j - gs >= G / 2) ? gs + G / 2 : gs;
 }
-// One past the last query row that sees the key rows starting at j:
+// One past the last query row that sees the key rows starting at j (a group
+// that G does not fill ends at N):
 __device__ __forceinline__ int query_end_row(int j, int G, int N, bool split_head) {
   const int gs = j - j % G;
-  return (split_head && gs == N - G && j - gs < G / 2) ? gs + G / 2 : gs + G;
+  return (split_head && gs == N - G && j - gs < G / 2) ? gs + G / 2 : min(gs + G, N);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

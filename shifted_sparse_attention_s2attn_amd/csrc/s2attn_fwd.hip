@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
   const int l32 = lane & 31, hf = lane >> 5;
 
   // Heaviest query tiles (last in their group) are dispatched first.
-  const int groups = N / G, tiles_per_group = G / BR;
+  const int groups = num_groups(N, G), tiles_per_group = (G + BR - 1) / BR;
   const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
   const int pos = tiles_per_group - 1 - to.rank;
   const int grp = to.pair % groups;
@@ -68,9 +68,11 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
 
   const bool split_head = split && sigma != 0;
+  const int ge = min(grp * G + G, N);           // end of the group (a last group may be short)
   const int j0 = grp * G + pos * BR;            // first query row (rolled)
+  if (j0 >= ge) return;                         // a tile past the end of a short group
   const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
-  const int ntiles = (j0 + BR - kv_begin) / BC;
+  const int ntiles = (min(j0 + BR, ge) - kv_begin + BC - 1) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
   const T* qb = q + (size_t)b * N * qstride + (size_t)h * D;
@@ -80,7 +82,8 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
   // ---- Q operand (B of S^T = K Q^T): query (l32), 8 head-dim values per k-step
   const int jw = j0 + wave * 32;                // wave's first query (rolled)
   const int jq = jw + l32;                      // this lane's query (rolled)
-  const int tq = orig_row(jq, sigma, N);
+  const bool q_ok = jq < ge;                    // rows past the group compute on a copy, are not stored
+  const int tq = orig_row(q_ok ? jq : ge - 1, sigma, N);
   const int kw0 = first_key_row(jw, G, N, split_head);        // ... and this wave's first key
   v8<T> qf[S::kDC];
 #pragma unroll
@@ -98,12 +101,12 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
     for (int i = 0; i < KPT; ++i) {
       const int ci = tid + i * 256;
       const int row = ci / KCPR, cc = ci % KCPR;
-      const int t = orig_row(kt0 + row, sigma, N);
+      const int t = orig_row(min(kt0 + row, N - 1), sigma, N);   // rows past N are masked keys
       kreg[i] = *reinterpret_cast<const v8<T>*>(kb + (size_t)t * kvstride + cc * 8);
     }
 #pragma unroll
     for (int i = 0; i < VKPT; ++i) {
-      const int t = orig_row(kt0 + v_kg * VKPT + i, sigma, N);
+      const int t = orig_row(min(kt0 + v_kg * VKPT + i, N - 1), sigma, N);
       vreg[i] = *reinterpret_cast<const v8<T>*>(vb + (size_t)t * kvstride + v_dc * 8);
     }
   };
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
     __syncthreads();
     if (it + 1 < ntiles) load_tile(kt0 + BC);
 
-    if (kt0 > jw + 31 || kt0 < kw0) continue;   // tile after this wave's queries, or outside its group
+    if (kt0 > jw + 31 || kt0 < kw0 || jw >= ge) continue;   // nothing of this tile for this wave
     const bool need_mask = kt0 + BC - 1 > jw;
 
     // S^T = K Q^T
@@ -203,6 +206,7 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
 
   // ---- epilogue: normalise, store O and lse at the original row
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!q_ok) return;
   const float inv = 1.f / l_tot;
   T* orow = o + ((size_t)b * N + tq) * qstride + (size_t)h * D;
 #pragma unroll
@@ -458,11 +462,13 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int B, int H, int Hkv, int N, int G, int shift_heads, int split, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
-    // the fast kernel addresses one batch's K / V with 31-bit byte offsets
-    if (G % FwdB16Shape<D>::kBR == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
+    // the fast kernel takes whole 256-row tiles of whole groups, and addresses
+    // one batch's K / V with 31-bit byte offsets
+    if (G % FwdB16Shape<D>::kBR == 0 && N % G == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
       return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, split, scale, stream);
   }
-  dim3 grid(B * H * (N / FwdShape<T, D>::kBR));
+  constexpr int BR = FwdShape<T, D>::kBR;
+  dim3 grid(B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
   hipLaunchKernelGGL((s2attn_fwd_kernel<T, D>), grid, dim3(256), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, split, scale);
   return hipGetLastError();

@@ -54,8 +54,8 @@ def fwd_status(lib, ptrs=True, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(N=500), _lib.S2ATTN_ERR_SHAPE),          # N % G != 0
-    (dict(G=129, N=129 * 4), _lib.S2ATTN_ERR_SHAPE),  # odd G
+    (dict(G=1024), _lib.S2ATTN_ERR_SHAPE),         # G > N
+    (dict(G=0), _lib.S2ATTN_ERR_SHAPE),
     (dict(S=5), _lib.S2ATTN_ERR_SHAPE),
     (dict(S=-1), _lib.S2ATTN_ERR_SHAPE),
     (dict(Hkv=3), _lib.S2ATTN_ERR_SHAPE),
@@ -64,8 +64,8 @@ def fwd_status(lib, ptrs=True, **kw):
     (dict(H=0, Hkv=0), _lib.S2ATTN_ERR_SHAPE),
     (dict(d=96), _lib.S2ATTN_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.S2ATTN_ERR_UNSUPPORTED),
-    (dict(G=64, N=512), _lib.S2ATTN_ERR_UNSUPPORTED),   # G not a multiple of 128
     (dict(H=6, Hkv=2, S=2, G=128, N=512), _lib.S2ATTN_ERR_UNSUPPORTED),  # mixed-shift KV head, G/2 % 128 != 0
+    (dict(H=6, Hkv=2, S=2, G=256, N=640), _lib.S2ATTN_ERR_UNSUPPORTED),  # mixed-shift KV head, G does not divide N
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd_status(lib, **kw) == code
@@ -100,6 +100,16 @@ def test_grid_size_limit(lib):
     assert fwd_status(lib, B=1 << 20, H=1 << 10, Hkv=1 << 10, S=0, N=256) == _lib.S2ATTN_ERR_UNSUPPORTED
 
 
+def test_unaligned_group_sizes_pass_validation(lib):
+    """G need not divide N, nor be a multiple of 128 (generic kernels): only the
+    pointers are left to reject (NULL here)."""
+    for kw in (dict(N=500), dict(G=129, N=129 * 4), dict(G=64, N=512), dict(G=1365, N=8192), dict(G=1, N=7),
+               dict(G=512, N=512)):
+        assert fwd_status(lib, ptrs=False, **kw) == _lib.S2ATTN_ERR_NULL, kw
+    # workspace of a short last group: still one fp32 row sum and one lse2 per row
+    assert lib.s2attn_bwd_workspace_bytes(1, 4, 4, 500, 64, 128, 2, 0) == 2 * ((4 * 500 * 4 + 255) // 256 * 256)
+
+
 def test_wrap_option_validation(lib):
     """The _ex calls take wrap in {ROLL, SPLIT}; anything else is unsupported,
     checked after the sizes and before the pointers."""
@@ -113,8 +123,14 @@ def test_wrap_option_validation(lib):
         assert lib.s2attn_bwd_dkdv_ex(*([None] * 7), need, *dims, wrap, 0, None) == code
         assert lib.s2attn_bwd_dq_ex(*([None] * 6), need, *dims, wrap, 0, None) == code
     bad = list(dims)
-    bad[3] = 500                                         # shape errors come first
+    bad[3] = 64                                          # shape errors come first (G > N)
     assert lib.s2attn_fwd_ex(None, None, None, None, None, *bad, 7, 0, None) == _lib.S2ATTN_ERR_SHAPE
+    unaligned = list(dims)
+    unaligned[3] = 500                                   # split needs whole groups of whole tiles
+    assert lib.s2attn_fwd_ex(None, None, None, None, None, *unaligned, _lib.S2ATTN_WRAP_SPLIT, 0, None) == \
+        _lib.S2ATTN_ERR_UNSUPPORTED
+    assert lib.s2attn_fwd_ex(None, None, None, None, None, *unaligned, _lib.S2ATTN_WRAP_ROLL, 0, None) == \
+        _lib.S2ATTN_ERR_NULL
     empty = list(dims)
     empty[0] = 0                                         # empty problem: validated, then a no-op
     assert lib.s2attn_fwd_ex(None, None, None, None, None, *empty, _lib.S2ATTN_WRAP_SPLIT, 0, None) == _lib.S2ATTN_OK
@@ -145,7 +161,7 @@ def test_bwd_workspace_checks(lib):
     bad[6] = None
     assert lib.s2attn_bwd(*bad, DUMMY, need, *dims) == _lib.S2ATTN_ERR_NULL
     dims_bad = list(dims)
-    dims_bad[3] = 500
+    dims_bad[3] = 64                   # G > N
     assert lib.s2attn_bwd(*args, DUMMY, need, *dims_bad) == _lib.S2ATTN_ERR_SHAPE
 
 
@@ -164,7 +180,7 @@ def test_bwd_stage_entry_points_validate(lib):
     need = lib.s2attn_bwd_workspace_bytes(p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"], 0)
     dims = [p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"], 0, None]
     bad_n = list(dims)
-    bad_n[3] = 500
+    bad_n[3] = 64                      # G > N
     # prep(o, lse, dO, ws, bytes, ...)
     assert lib.s2attn_bwd_prep(DUMMY, None, DUMMY, DUMMY, need, *dims) == _lib.S2ATTN_ERR_NULL
     assert lib.s2attn_bwd_prep(DUMMY, FDUMMY, DUMMY, DUMMY, need - 4, *dims) == _lib.S2ATTN_ERR_WORKSPACE

@@ -107,6 +107,26 @@ def test_small_parity_split(w):
     check_full(w, inp, out, wrap="split")
 
 
+# group sizes that do not divide the sequence, or are not whole 128-row tiles
+# (generic kernels): the last group is short, the shift floor(G/2)
+UNALIGNED = [
+    small_workload("bf16-short-last-group", B=1, H=4, Hkv=4, d=128, N=1000, G=256, shift_heads=2),
+    small_workload("bf16-g100-gqa", B=2, H=2, Hkv=1, d=64, N=777, G=100, shift_heads=2),
+    small_workload("bf16-table7-sixth", B=1, H=2, Hkv=2, d=128, N=8192, G=1365, shift_heads=1),
+    small_workload("bf16-g3", B=1, H=2, Hkv=2, d=64, N=100, G=3, shift_heads=1),
+    small_workload("f32-odd-g103", B=1, H=4, Hkv=2, d=64, N=515, G=103, shift_heads=2, dtype="f32"),
+    small_workload("f32-g-equals-n-300", B=1, H=2, Hkv=2, d=128, N=300, G=300, shift_heads=1, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("w", UNALIGNED, ids=[w.name for w in UNALIGNED])
+def test_small_parity_unaligned(w):
+    say(f"case {w}")
+    inp = make_inputs(w, seed=3)
+    out = run_gpu(w, to_gpu(inp))
+    check_full(w, inp, out)
+
+
 @pytest.mark.parametrize("seed", range(10))
 def test_tiny_f32_workload(seed):
     """B=1, H=4 (2 shifted), d=64, N=512, G=128, fp32; seeds 0-9."""
@@ -193,6 +213,21 @@ def test_full_size_workload(name):
     say("  kernels done; global checks")
     check_global(w, t, out)
     for c, g0 in SAMPLES[name]:
+        check_sampled(w, t, out, c, g0)
+
+
+def test_full_size_table7_sixth_group():
+    """Table 7's 1/6 group at the 7B 8k shape: G = 1365 (odd, does not divide
+    8192), shift 682.  Sampled: a shifted head's wrap group (rolled group 5)
+    and its 2-token last group, and an unshifted head's last group."""
+    w = WORKLOADS["llama2-7b-8k-g1365"]
+    say(f"case {w} (generating inputs on the GPU)")
+    t = make_inputs(w, seed=0, device="cuda")
+    out = run_gpu(w, t)
+    say("  kernels done")
+    for name, x in zip(("o", "lse", "dq", "dk", "dv"), out):
+        assert bool(torch.isfinite(x).all()), f"non-finite values in {name}"
+    for c, g0 in [(31, 5), (31, 6), (0, 6), (0, 0)]:
         check_sampled(w, t, out, c, g0)
 
 
@@ -305,4 +340,6 @@ def test_empty_inputs(B, N):
 def test_rejected_shape_raises():
     q = torch.zeros((1, 500, 2, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(S2AttnError):
-        s2attn_fwd(q, q, q, 128, 1)
+        s2attn_fwd(q, q, q, 1024, 1)            # group longer than the sequence
+    with pytest.raises(S2AttnError):
+        s2attn_fwd(q, q, q, 100, 1, wrap="split")   # split needs whole groups of whole tiles
