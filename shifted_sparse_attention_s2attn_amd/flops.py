@@ -15,14 +15,17 @@ MI355X_HBM_PEAK_GBS = 8000.0
 
 
 def allowed_pairs(B, H, N, G, shift_heads=0, wrap="roll"):
-    """B * H * (N/G) groups, each a causal G x G triangle with G(G+1)/2 pairs.
+    """B * H * (N/G) groups, each a causal G x G triangle with G(G+1)/2 pairs
+    (when G does not divide N, a last group of N mod G tokens).
 
     With the split wrap option each shifted head's wrap group loses the pairs of
-    its second-half queries with its first-half keys, (G/2)^2 of them.
+    the wrapped tokens (the last floor(G/2) of the group) with the tokens before
+    them, (G - floor(G/2)) floor(G/2) of them.
     """
-    pairs = B * H * (N // G) * G * (G + 1) // 2
+    rem = N % G
+    pairs = B * H * ((N // G) * G * (G + 1) // 2 + rem * (rem + 1) // 2)
     if wrap == "split":
-        pairs -= B * shift_heads * (G // 2) ** 2
+        pairs -= B * shift_heads * (G - G // 2) * (G // 2)
     return pairs
 
 

@@ -51,9 +51,12 @@ def test_table11_attention_flops():
 
 
 @pytest.mark.parametrize("wrap", ["roll", "split"])
-@pytest.mark.parametrize("N,G,H,S", [(16, 8, 2, 1), (24, 8, 3, 2), (32, 32, 2, 0), (12, 4, 4, 4), (16, 16, 2, 2)])
+@pytest.mark.parametrize("N,G,H,S", [(16, 8, 2, 1), (24, 8, 3, 2), (32, 32, 2, 0), (12, 4, 4, 4), (16, 16, 2, 2),
+                                     (30, 8, 2, 1), (23, 7, 3, 2), (9, 1, 2, 1), (21, 7, 2, 1)])
 def test_pair_count_matches_bruteforce_mask(N, G, H, S, wrap):
     """allowed_pairs counts exactly the entries the method lets attend."""
+    if wrap == "split" and N % G:
+        pytest.skip("the split option is defined on whole groups only")
     total = 0
     for h in range(H):
         total += int(pins.allowed_mask_original(N, G, h >= H - S, wrap == "split").sum())
