@@ -22,8 +22,9 @@
 //          on lanes), so dS feeds dQ^T = K^T dS^T straight from registers.
 // dS is kept without the softmax scale; dK and dQ take it at their stores.
 // Each stage has a generic kernel (any element type, register-staged LDS
-// tiles; used for fp32) and a bf16 kernel laid out for the bf16 matrix cores
-// (direct-to-LDS tile loads, transposing LDS reads).
+// tiles; used for fp32, and for groups that are not whole tiles) and a bf16
+// kernel laid out for the bf16 matrix cores (direct-to-LDS tile loads,
+// transposing LDS reads) for whole groups of whole tiles.
 #include "s2attn_common.h"
 
 #include <type_traits>
@@ -76,7 +77,9 @@ __device__ __forceinline__ void store_transposed(v8<T>* tile, const v8<T>* regs,
 }
 
 // ===========================================================================
-// dkdv, generic
+// dkdv, generic.  Also takes groups that are not whole tiles: key rows past
+// the group compute on a copy of its last row and are not stored; query rows of
+// the next group in the last query tile are masked; rows past N are clamped.
 // ===========================================================================
 template <typename T, int D>
 struct DkdvShape {
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
 }
 
 // ===========================================================================
-// dq, generic
+// dq, generic.  Groups that are not whole tiles as in the generic forward.
 // ===========================================================================
 template <typename T, int D>
 struct DqShape {

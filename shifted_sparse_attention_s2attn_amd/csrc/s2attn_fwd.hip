@@ -20,6 +20,10 @@
 //     its 32 keys split across lanes l and l ^ 32)
 //     O^T += V^T P^T     (P^T comes straight from the S^T registers)
 // Finally O = O^T / l is stored at the original rows with lse = m + ln l.
+// This kernel also takes groups that are not whole tiles (a short last group
+// when G does not divide N, or any G): query rows past the group compute on a
+// copy of its last row and are not stored, key rows past it (the next group, or
+// past N, clamped to a real row) follow every query of the group and are masked.
 #include "s2attn_common.h"
 
 #include <type_traits>
