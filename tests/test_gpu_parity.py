@@ -19,7 +19,8 @@ import pytest
 import torch
 
 from oracle import s2attn_oracle as orc
-from shifted_sparse_attention_s2attn_amd import S2AttnError, s2attn, s2attn_bwd, s2attn_fwd
+from shifted_sparse_attention_s2attn_amd import (S2AttnError, s2attn, s2attn_bwd, s2attn_bwd_workspace_bytes,
+                                                 s2attn_fwd)
 from shifted_sparse_attention_s2attn_amd.inputs import WORKLOADS, make_inputs, small_workload
 
 pytestmark = pytest.mark.gpu
@@ -319,6 +320,46 @@ def test_autograd_wrapper(wrap):
     assert torch.equal(o, ref[0])
     assert torch.equal(k.grad, ref[3]) and torch.equal(v.grad, ref[4])
     assert float((q.grad.float() - ref[2].float()).abs().max()) <= 1e-2
+
+
+@pytest.mark.parametrize("G,dtype", [(256, "bf16"), (100, "bf16"), (256, "f32")])
+def test_graph_capture_replays(G, dtype):
+    """The forward and backward calls launch kernels only (no allocation, copy,
+    memset or synchronisation), so they can be captured in a HIP graph: three
+    replays, with eager work and synchronisations between them, each equal to
+    the eager result bit for bit (fast and generic kernels)."""
+    w = small_workload("graph", B=1, H=4, Hkv=2, d=128, N=1024, G=G, shift_heads=2, dtype=dtype)
+    say(f"case {w}")
+    t = to_gpu(make_inputs(w, seed=5))
+    ref = run_gpu(w, t)
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o, lse = torch.empty_like(q), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws = torch.empty(s2attn_bwd_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.G, w.shift_heads, q.dtype),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        s2attn_fwd(q, k, v, w.G, w.shift_heads, out=o, lse=lse)
+        s2attn_bwd(q, k, v, o, lse, do, w.G, w.shift_heads, workspace=ws, grads=grads)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    outs = (o, lse) + grads
+    for rep in range(3):
+        for x in outs:
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, r in zip(("o", "lse", "dq", "dk", "dv"), outs, ref):
+            assert torch.equal(x, r), f"replay {rep}: {name} differs from the eager result"
 
 
 @pytest.mark.parametrize("B,N", [(0, 512), (2, 0)])
