@@ -3,8 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one forward (s2attn_fwd) and one backward (its three stages) over one
-batch of seeded synthetic inputs already resident in HBM.  W untimed steps,
+A step is one forward (s2attn_fwd) and one backward (its two launches, as
+s2attn_bwd runs them: prep fused into dQ, then dK/dV) over one batch of seeded
+synthetic inputs already resident in HBM.  W untimed steps,
 then K steps between two device synchronisations; the wall time of those K
 steps gives ``value`` (effective TFLOP/s: group-local causal pairs only, 4d
 FLOP per pair forward, 10d backward).  HIP events recorded on the launch
@@ -153,7 +154,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from shifted_sparse_attention_s2attn_amd import (s2attn_bwd_dkdv, s2attn_bwd_dq, s2attn_bwd_prep,
+    from shifted_sparse_attention_s2attn_amd import (s2attn_bwd_dkdv, s2attn_bwd_prep_dq,
                                                      s2attn_bwd_workspace_bytes, s2attn_fwd)
     from shifted_sparse_attention_s2attn_amd import flops as F
     from shifted_sparse_attention_s2attn_amd.inputs import WORKLOADS, make_inputs
@@ -169,7 +170,8 @@ def main():
     ws = torch.empty(s2attn_bwd_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.G, w.shift_heads, q.dtype),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    names = ["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
+    # the backward as the library's s2attn_bwd runs it: prep fused into dq, then dK/dV
+    names = ["fwd", "bwd_prep_dq", "bwd_dkdv"]
 
     def step(ev=None):
         if ev:
@@ -177,19 +179,16 @@ def main():
         s2attn_fwd(q, k, v, w.G, w.shift_heads, out=o, lse=lse, wrap=args.wrap)
         if ev:
             ev[1].record(stream)
-        s2attn_bwd_prep(q, k, o, lse, do, ws, w.G, w.shift_heads)
+        s2attn_bwd_prep_dq(q, k, v, o, lse, do, dq, ws, w.G, w.shift_heads, wrap=args.wrap)
         if ev:
             ev[2].record(stream)
         s2attn_bwd_dkdv(q, k, v, do, dk, dv, ws, w.G, w.shift_heads, wrap=args.wrap)
         if ev:
             ev[3].record(stream)
-        s2attn_bwd_dq(q, k, v, do, dq, ws, w.G, w.shift_heads, wrap=args.wrap)
-        if ev:
-            ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -202,12 +201,11 @@ def main():
     fwd_f = F.fwd_flops(w.B, w.H, w.N, w.G, w.d, w.shift_heads, args.wrap)
     bwd_f = F.bwd_flops(w.B, w.H, w.N, w.G, w.d, w.shift_heads, args.wrap)
     peak = F.MI355X_BF16_PEAK_TFLOPS if w.dtype == "bf16" else F.MI355X_F32_PEAK_TFLOPS
-    elt = 2 if w.dtype == "bf16" else 4
     # algorithmic FLOP per launch: the backward's five contractions are S, dP, dV, dK
     # (the dK/dV kernel, 8d per pair) and dQ (the dQ kernel, 2d per pair; that kernel
     # also recomputes S and dP, which are not counted again)
     pairs = F.allowed_pairs(w.B, w.H, w.N, w.G, w.shift_heads, args.wrap)
-    kern_flops = {"fwd": fwd_f, "bwd_dkdv": 8 * w.d * pairs, "bwd_dq": 2 * w.d * pairs}
+    kern_flops = {"fwd": fwd_f, "bwd_dkdv": 8 * w.d * pairs, "bwd_prep_dq": 2 * w.d * pairs}
     dominant = max(kern_ms, key=kern_ms.get)
     kernels = {}
     for n, ms in kern_ms.items():
@@ -215,18 +213,12 @@ def main():
         if n in kern_flops:
             kernels[n]["tflops"] = round(kern_flops[n] / ms / 1e9, 1)
             kernels[n]["frac_of_peak"] = round(kern_flops[n] / ms / 1e9 / peak, 4)
-    kernels["bwd_dq"]["executed_tflops"] = round(6 * w.d * pairs / kern_ms["bwd_dq"] / 1e9, 1)
+    kernels["bwd_prep_dq"]["executed_tflops"] = round(6 * w.d * pairs / kern_ms["bwd_prep_dq"] / 1e9, 1)
     fwd_ms = kern_ms["fwd"]
-    bwd_ms = kern_ms["bwd_prep"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
-    if dominant in kern_flops:
-        achieved = kern_flops[dominant] / kern_ms[dominant] / 1e9
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
-    else:
-        nbytes = 2 * elt * w.B * w.N * w.H * w.d + 12 * w.B * w.H * w.N   # bwd_prep
-        achieved = nbytes / kern_ms[dominant] / 1e6
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": F.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / F.MI355X_HBM_PEAK_GBS, 4)}
+    bwd_ms = kern_ms["bwd_prep_dq"] + kern_ms["bwd_dkdv"]
+    achieved = kern_flops[dominant] / kern_ms[dominant] / 1e9    # every launch is a contraction
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4)}
     roof["kernel"] = dominant
     roof["traffic"] = read_traffic(dominant, w.name)
 
@@ -265,8 +257,7 @@ def main():
     if w.dtype == "bf16" and not args.no_gemm_reference:
         ref = gemm_reference(torch, dev)
         ref["fwd_frac"] = round(fwd_f / fwd_ms / 1e9 / ref["tflops"], 4)
-        if dominant in kern_flops:
-            ref["roofline_kernel_frac"] = round(roof["achieved"] / ref["tflops"], 4)
+        ref["roofline_kernel_frac"] = round(roof["achieved"] / ref["tflops"], 4)
         result["gemm_reference"] = ref
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds, args.wrap)

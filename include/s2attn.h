@@ -125,9 +125,11 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
                int dtype, void* stream);
 
 /*
- * The backward as its three stages; s2attn_bwd is exactly prep, dkdv, dq in
- * this order on one stream.  Same checks and workspace as s2attn_bwd; dkdv
- * and dq both read what prep wrote and may run in either order after it.
+ * The backward as stages.  s2attn_bwd is exactly s2attn_bwd_prep_dq then
+ * s2attn_bwd_dkdv on one stream; s2attn_bwd_prep followed by s2attn_bwd_dq is
+ * the same as s2attn_bwd_prep_dq up to the rounding of Dvec.  Same checks and
+ * workspace as s2attn_bwd; dkdv and dq both read what prep (or prep_dq)
+ * wrote, and after prep they may run in either order.
  * The gradients are those of the causal softmax attention of "The shifting
  * mechanism" / Algorithm 1 (page section 3.4) in every group of every head's
  * rolled frame: P = exp(scale q k^T - lse), dS = P * (dO v^T - Dvec),
@@ -135,7 +137,11 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
  *          (fp32) into the workspace;
  *   dkdv : dv = P^T dO and dk = scale dS^T q, summed over the query heads
  *          that share a key/value head;
- *   dq   : dq = scale dS k (recomputes P and dS per query tile).
+ *   dq   : dq = scale dS k (recomputes P and dS per query tile);
+ *   prep_dq : prep and dq in one pass (one launch where the fast bf16 dq
+ *          kernel runs: every query row is handled by one workgroup, which
+ *          already holds its dO row); writes dq and the workspace.  It takes
+ *          the wrap option (an s2attn_wrap value) like the _ex calls below.
  */
 int s2attn_bwd_prep(const void* o, const float* lse, const void* dO, void* workspace, size_t workspace_bytes,
                     int B, int H, int Hkv, int N, int d, int G, int shift_heads,
@@ -148,6 +154,11 @@ int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                   void* dq, void* workspace, size_t workspace_bytes,
                   int B, int H, int Hkv, int N, int d, int G, int shift_heads,
                   int dtype, void* stream);
+int s2attn_bwd_prep_dq(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dO,
+                       void* dq, void* workspace, size_t workspace_bytes,
+                       int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                       int dtype, void* stream);
 
 /*
  * The forward, the backward and its dkdv and dq stages with a wrap option

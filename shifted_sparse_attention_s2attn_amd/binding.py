@@ -12,7 +12,7 @@ import torch
 from . import _lib
 
 __all__ = ["S2AttnError", "s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes",
-           "s2attn_bwd_prep", "s2attn_bwd_dkdv", "s2attn_bwd_dq",
+           "s2attn_bwd_prep", "s2attn_bwd_dkdv", "s2attn_bwd_dq", "s2attn_bwd_prep_dq",
            "s2attn_status_str", "S2Attn", "s2attn"]
 
 
@@ -152,6 +152,17 @@ def s2attn_bwd_dq(q, k, v, do, dq, workspace, G, shift_heads=None, stream=None, 
                                             B, H, Hkv, N, d, G, S, _wrap_code(wrap), _dtype_code(q),
                                             _stream(stream)),
                "s2attn_bwd_dq")
+
+
+def s2attn_bwd_prep_dq(q, k, v, o, lse, do, dq, workspace, G, shift_heads=None, stream=None, wrap="roll"):
+    """Stages 1 and 3 together: dq, and Dvec and lse * log2(e) into the workspace (dk, dv follow)."""
+    B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
+    with torch.cuda.device(q.device):
+        _check(_lib.load().s2attn_bwd_prep_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), _ptr(do), _ptr(dq),
+                                              _ptr(workspace), workspace.numel(),
+                                              B, H, Hkv, N, d, G, S, _wrap_code(wrap), _dtype_code(q),
+                                              _stream(stream)),
+               "s2attn_bwd_prep_dq")
 
 
 class S2Attn(torch.autograd.Function):

@@ -19,6 +19,9 @@ hipError_t launch_bwd_dkdv(const void*, const void*, const void*, const void*, c
 template <typename T, int D>
 hipError_t launch_bwd_dq(const void*, const void*, const void*, const void*, const float*, const float*, void*,
                          int, int, int, int, int, int, int, hipStream_t);
+template <typename T, int D>
+hipError_t launch_bwd_prep_dq(const void*, const void*, const void*, const void*, const float*, const void*,
+                              float*, float*, void*, int, int, int, int, int, int, int, hipStream_t);
 }  // namespace s2a
 
 namespace {
@@ -142,6 +145,15 @@ struct Dq {
   }
 };
 
+template <typename T, int D>
+struct PrepDq {
+  static hipError_t run(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dO, void* dq, Workspace ws, int B, int H, int Hkv, int N, int G, int S, int wrap,
+                        hipStream_t s) {
+    return s2a::launch_bwd_prep_dq<T, D>(q, k, v, o, lse, dO, ws.lse2, ws.dvec, dq, B, H, Hkv, N, G, S, wrap, s);
+  }
+};
+
 int status_of(hipError_t e) { return e == hipSuccess ? S2ATTN_OK : S2ATTN_ERR_HIP; }
 
 }  // namespace
@@ -206,6 +218,22 @@ int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, v
                           S2ATTN_WRAP_ROLL, dtype, stream);
 }
 
+int s2attn_bwd_prep_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dO, void* dq, void* workspace, size_t workspace_bytes,
+                       int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype,
+                       void* stream) {
+  int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st == S2ATTN_OK) st = check_wrap(wrap, N, G);
+  if (st != S2ATTN_OK) return st;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dO || !dq) return S2ATTN_ERR_NULL;
+  Workspace ws;
+  st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
+  if (st != S2ATTN_OK) return st;
+  return status_of(dispatch<PrepDq>(dtype, d, q, k, v, o, lse, dO, dq, ws, B, H, Hkv, N, G, shift_heads, wrap,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
 int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                   int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype, void* stream) {
@@ -218,10 +246,10 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, co
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = dispatch<Prep>(dtype, d, o, dO, lse, ws, B, H, N, s);
+  // prep fused into dq (it writes the workspace), then dK/dV
+  hipError_t e = dispatch<PrepDq>(dtype, d, q, k, v, o, lse, dO, dq, ws, B, H, Hkv, N, G, shift_heads, wrap, s);
   if (e == hipSuccess)
     e = dispatch<Dkdv>(dtype, d, q, k, v, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads, wrap, s);
-  if (e == hipSuccess) e = dispatch<Dq>(dtype, d, q, k, v, dO, dq, ws, B, H, Hkv, N, G, shift_heads, wrap, s);
   return status_of(e);
 }
 

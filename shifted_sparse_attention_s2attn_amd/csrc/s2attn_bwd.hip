@@ -726,6 +726,9 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
 // double-buffered in LDS.  Per tile: S^T = K Q^T and dP^T = V dO^T (queries
 // on lanes, so lse and Dvec are one value per lane), dS^T in registers, and
 // dQ^T += K^T dS^T with K^T read through transposing reads.
+// PREP: the prep stage fused in.  Every query row belongs to exactly one
+// workgroup, which already holds its dO row, so it computes Dvec = dO . O and
+// lse * log2(e) itself and writes both to the workspace for the dK/dV stage.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqB16Shape {
@@ -740,10 +743,11 @@ struct DqB16Shape {
   static constexpr int kDT = D / 32;
 };
 
-template <int D>
+template <int D, bool PREP>
 __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
+    const bf16* __restrict__ dO, const bf16* __restrict__ o, const float* __restrict__ lse,
+    float* __restrict__ lse2, float* __restrict__ dvec,
     bf16* __restrict__ dq, int N, int H, int Hkv, int G, int shift_heads, int split, float scale) {
   using S = DqB16Shape<D>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTile;
@@ -789,8 +793,28 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
       dof[cc] = *reinterpret_cast<const bf16x8*>(dorow + cc * 16 + hf * 8);
     }
   }
-  const float lse_q = lse2[((size_t)b * H + h) * N + tq];
-  const float dvec_q = dvec[((size_t)b * H + h) * N + tq];
+  const size_t rix = ((size_t)b * H + h) * N + tq;
+  float lse_q, dvec_q;
+  if constexpr (PREP) {
+    // Dvec = dO . O over this lane's half of the row, then the two halves
+    const bf16* orow = o + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+    float part = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < S::kDC; ++cc) {
+      const bf16x8 oc = *reinterpret_cast<const bf16x8*>(orow + cc * 16 + hf * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) part = fmaf((float)oc[i], (float)dof[cc][i], part);
+    }
+    dvec_q = sum_halves(part);
+    lse_q = lse[rix] * kLog2e;
+    if (hf == 0) {
+      dvec[rix] = dvec_q;
+      lse2[rix] = lse_q;
+    }
+  } else {
+    lse_q = lse2[rix];
+    dvec_q = dvec[rix];
+  }
 
   // K and V of this (batch, KV head) as buffers (32-bit byte offsets, which
   // the launcher checks); per-lane byte offsets of the chunks this lane moves
@@ -974,14 +998,21 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, split, scale, stream);
 }
 
+// o and lse non-NULL: prep fused in (writes lse2 and dvec); else reads them.
 template <int D>
-hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
-                          const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
-                          int split, float scale, hipStream_t stream) {
+hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO, const void* o,
+                          const float* lse, float* lse2, float* dvec, void* dq, int B, int H, int Hkv, int N, int G,
+                          int shift_heads, int split, float scale, hipStream_t stream) {
   using S = DqB16Shape<D>;
-  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D>), dim3(B * H * (N / S::kBR)), dim3(S::kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dq, N, H,
-                     Hkv, G, shift_heads, split, scale);
+  const dim3 grid(B * H * (N / S::kBR)), block(S::kThreads);
+  if (o)
+    hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, true>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dO, (const bf16*)o, lse, lse2, dvec, (bf16*)dq, N, H, Hkv, G,
+                       shift_heads, split, scale);
+  else
+    hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, false>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dO, (const bf16*)nullptr, (const float*)nullptr, lse2, dvec,
+                       (bf16*)dq, N, H, Hkv, G, shift_heads, split, scale);
   return hipGetLastError();
 }
 
@@ -1000,18 +1031,40 @@ hipError_t launch_dq_generic(const void* q, const void* k, const void* v, const 
   return hipGetLastError();
 }
 
+// the fast dq kernel takes whole 256-row tiles of whole groups, and addresses
+// one batch's K / V with 31-bit byte offsets
+template <typename T, int D>
+bool dq_fast(int N, int Hkv, int G) {
+  return sizeof(T) == 2 && G % DqB16Shape<D>::kBR == 0 && N % G == 0 &&
+         (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31);
+}
+
 template <typename T, int D>
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                          const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
                          int split, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
-    // the fast kernel takes whole 256-row tiles of whole groups, and addresses
-    // one batch's K / V with 31-bit byte offsets
-    if (G % DqB16Shape<D>::kBR == 0 && N % G == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
-      return launch_dq_bf16<D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split, scale, stream);
+    if (dq_fast<T, D>(N, Hkv, G))
+      return launch_dq_bf16<D>(q, k, v, dO, nullptr, nullptr, const_cast<float*>(lse2), const_cast<float*>(dvec),
+                               dq, B, H, Hkv, N, G, shift_heads, split, scale, stream);
   }
   return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split, scale, stream);
+}
+
+// prep and dq in one launch where the fast dq kernel runs, else one after the other
+template <typename T, int D>
+hipError_t launch_bwd_prep_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dO, float* lse2, float* dvec, void* dq, int B, int H, int Hkv, int N,
+                              int G, int shift_heads, int split, hipStream_t stream) {
+  if constexpr (sizeof(T) == 2) {
+    if (dq_fast<T, D>(N, Hkv, G))
+      return launch_dq_bf16<D>(q, k, v, dO, o, lse, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split,
+                               1.0f / sqrtf((float)D), stream);
+  }
+  const hipError_t e = launch_bwd_prep<T, D>(o, dO, lse, dvec, lse2, B, H, N, stream);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split, stream);
 }
 
 #define S2A_INST_BWD(T, D)                                                                                 \
@@ -1021,7 +1074,10 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                                             const float*, const float*, void*, void*, int, int, int, int,  \
                                             int, int, int, hipStream_t);                                   \
   template hipError_t launch_bwd_dq<T, D>(const void*, const void*, const void*, const void*, const float*, \
-                                          const float*, void*, int, int, int, int, int, int, int, hipStream_t);
+                                          const float*, void*, int, int, int, int, int, int, int, hipStream_t); \
+  template hipError_t launch_bwd_prep_dq<T, D>(const void*, const void*, const void*, const void*,           \
+                                               const float*, const void*, float*, float*, void*, int, int, int, \
+                                               int, int, int, int, hipStream_t);
 S2A_INST_BWD(bf16, 64)
 S2A_INST_BWD(bf16, 128)
 S2A_INST_BWD(float, 64)

@@ -88,6 +88,7 @@ def test_empty_problem_is_a_no_op(lib, kw):
     assert lib.s2attn_bwd_prep(None, None, None, None, 0, *dims) == _lib.S2ATTN_OK
     assert lib.s2attn_bwd_dkdv(*([None] * 7), 0, *dims) == _lib.S2ATTN_OK
     assert lib.s2attn_bwd_dq(*([None] * 6), 0, *dims) == _lib.S2ATTN_OK
+    assert lib.s2attn_bwd_prep_dq(*([None] * 8), 0, *dims[:7], 0, *dims[7:]) == _lib.S2ATTN_OK
     # the other sizes are still checked
     assert fwd_status(lib, ptrs=False, d=96, **kw) == _lib.S2ATTN_ERR_UNSUPPORTED
     assert fwd_status(lib, ptrs=False, S=9, **kw) == _lib.S2ATTN_ERR_SHAPE
@@ -194,3 +195,10 @@ def test_bwd_stage_entry_points_validate(lib):
     d96 = list(dims)
     d96[4] = 96
     assert lib.s2attn_bwd_dq(*([DUMMY] * 6), need, *d96) == _lib.S2ATTN_ERR_UNSUPPORTED
+    # prep_dq(q, k, v, o, lse, dO, dq, ws, bytes, ..., shift_heads, wrap, dtype, stream)
+    pd = [DUMMY, DUMMY, DUMMY, DUMMY, FDUMMY, DUMMY, DUMMY]
+    sz = dims[:7]
+    assert lib.s2attn_bwd_prep_dq(*pd[:4], None, *pd[5:], DUMMY, need, *sz, 0, 0, None) == _lib.S2ATTN_ERR_NULL
+    assert lib.s2attn_bwd_prep_dq(*pd, DUMMY, need - 4, *sz, 0, 0, None) == _lib.S2ATTN_ERR_WORKSPACE
+    assert lib.s2attn_bwd_prep_dq(*pd, DUMMY, need, *bad_n[:7], 0, 0, None) == _lib.S2ATTN_ERR_SHAPE
+    assert lib.s2attn_bwd_prep_dq(*pd, DUMMY, need, *sz, 3, 0, None) == _lib.S2ATTN_ERR_UNSUPPORTED

@@ -19,8 +19,8 @@ import pytest
 import torch
 
 from oracle import s2attn_oracle as orc
-from shifted_sparse_attention_s2attn_amd import (S2AttnError, s2attn, s2attn_bwd, s2attn_bwd_workspace_bytes,
-                                                 s2attn_fwd)
+from shifted_sparse_attention_s2attn_amd import (S2AttnError, s2attn, s2attn_bwd, s2attn_bwd_dq, s2attn_bwd_prep,
+                                                 s2attn_bwd_prep_dq, s2attn_bwd_workspace_bytes, s2attn_fwd)
 from shifted_sparse_attention_s2attn_amd.inputs import WORKLOADS, make_inputs, small_workload
 
 pytestmark = pytest.mark.gpu
@@ -360,6 +360,33 @@ def test_graph_capture_replays(G, dtype):
         torch.cuda.synchronize()
         for name, x, r in zip(("o", "lse", "dq", "dk", "dv"), outs, ref):
             assert torch.equal(x, r), f"replay {rep}: {name} differs from the eager result"
+
+
+@pytest.mark.parametrize("G,dtype", [(256, "bf16"), (256, "f32"), (100, "bf16")])
+def test_prep_fused_into_dq(G, dtype):
+    """s2attn_bwd_prep_dq (one launch on the fast bf16 path) against prep then dq:
+    lse * log2(e) bit-equal, Dvec and dq equal up to the rounding of Dvec."""
+    w = small_workload("prep-dq", B=2, H=4, Hkv=2, d=128, N=1024, G=G, shift_heads=2, dtype=dtype)
+    say(f"case {w}")
+    t = to_gpu(make_inputs(w, seed=6))
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o, lse = s2attn_fwd(q, k, v, w.G, w.shift_heads)
+    nbytes = s2attn_bwd_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.G, w.shift_heads, q.dtype)
+    ws_a = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    ws_b = torch.zeros_like(ws_a)
+    dq_a, dq_b = torch.empty_like(q), torch.empty_like(q)
+    s2attn_bwd_prep(q, k, o, lse, do, ws_a, w.G, w.shift_heads)
+    s2attn_bwd_dq(q, k, v, do, dq_a, ws_a, w.G, w.shift_heads)
+    s2attn_bwd_prep_dq(q, k, v, o, lse, do, dq_b, ws_b, w.G, w.shift_heads)
+    torch.cuda.synchronize()
+    n = w.B * w.H * w.N
+    half = nbytes // 2
+    dvec_a, dvec_b = ws_a[:4 * n].view(torch.float32), ws_b[:4 * n].view(torch.float32)
+    lse2_a, lse2_b = ws_a[half:half + 4 * n].view(torch.float32), ws_b[half:half + 4 * n].view(torch.float32)
+    assert torch.equal(lse2_a, lse2_b)
+    assert float((dvec_a - dvec_b).abs().max()) <= 1e-5 * max(1.0, float(dvec_a.abs().max()))
+    err = float((dq_a.float() - dq_b.float()).norm() / dq_a.float().norm())
+    assert err <= (1e-2 if dtype == "bf16" else 1e-5), err
 
 
 @pytest.mark.parametrize("B,N", [(0, 512), (2, 0)])
