@@ -128,6 +128,50 @@ def test_small_parity_unaligned(w):
     check_full(w, inp, out)
 
 
+def random_cases(n=24, seed=2024):
+    """Seeded random small problems over every option the ABI accepts: d, dtype,
+    B, GQA ratio, shifted-head count, aligned and unaligned G, both wrap modes.
+    Combinations the ABI rejects (split or a mixed-shift KV head on groups that
+    are not whole 128-row tiles, G/2 not whole tiles for a mixed KV head) are
+    redrawn."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["bf16", "bf16", "f32"]))
+        Hkv = int(rng.choice([1, 2]))
+        r = int(rng.choice([1, 2, 3]))
+        H = Hkv * r
+        S = int(rng.integers(0, H + 1))
+        G = int(rng.choice([128, 256, 384, 512, 100, 7, 250, 1000]))
+        N = int(rng.choice([G, 2 * G, 3 * G, G + int(rng.integers(1, G)) if G > 1 else G]))
+        N = min(N, 2048)
+        if G > N:
+            continue
+        B = int(rng.choice([1, 2]))
+        aligned = N % G == 0 and G % 128 == 0
+        wrap = str(rng.choice(["roll", "split"]))
+        if wrap == "split" and not aligned:
+            continue
+        if r > 1 and (H - S) % r != 0 and not (aligned and (G // 2) % 128 == 0):
+            continue
+        cases.append((small_workload(f"rand{len(cases)}", B=B, H=H, Hkv=Hkv, d=d, N=N, G=G, shift_heads=S,
+                                     dtype=dtype), wrap))
+    return cases
+
+
+RANDOM = random_cases()
+
+
+@pytest.mark.parametrize("w,wrap", RANDOM, ids=[f"{w.name}-{w.dtype}-d{w.d}-N{w.N}-G{w.G}-H{w.H}x{w.Hkv}-S{w.shift_heads}-{wrap}"
+                                                for w, wrap in RANDOM])
+def test_random_shapes(w, wrap):
+    say(f"case {w} wrap={wrap}")
+    inp = make_inputs(w, seed=7)
+    out = run_gpu(w, to_gpu(inp), wrap=wrap)
+    check_full(w, inp, out, wrap=wrap)
+
+
 @pytest.mark.parametrize("seed", range(10))
 def test_tiny_f32_workload(seed):
     """B=1, H=4 (2 shifted), d=64, N=512, G=128, fp32; seeds 0-9."""
