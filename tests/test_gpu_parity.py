@@ -276,6 +276,22 @@ def test_full_size_table7_sixth_group():
         check_sampled(w, t, out, c, g0)
 
 
+def test_slice_over_2gib():
+    """One batch's q / dO slice over 2 GiB (B=1, H=64, d=128, N=131072): the
+    dK/dV stage leaves its 32-bit-offset fast kernel for the generic one, the
+    forward and dQ keep theirs (their buffers are the smaller K / V).  Sampled
+    as the other full-size workloads: a shifted and an unshifted KV head."""
+    w = small_workload("gqa-131k", B=1, H=64, Hkv=8, d=128, N=131072, G=8192, shift_heads=32)
+    assert w.N * w.H * w.d * 2 >= 2 ** 31
+    say(f"case {w} (generating inputs on the GPU)")
+    t = make_inputs(w, seed=0, device="cuda")
+    out = run_gpu(w, t)
+    say("  kernels done; global checks")
+    check_global(w, t, out)
+    for c, g0 in [(7, 15), (0, 3)]:
+        check_sampled(w, t, out, c, g0)
+
+
 def test_full_size_split():
     """The split option at the 7B-32k size: the wrap group of a shifted head
     (its group 3, whose second half is tokens 0..G/2-1) and a plain group."""
