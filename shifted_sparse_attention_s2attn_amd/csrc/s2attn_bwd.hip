@@ -478,9 +478,12 @@ __device__ __forceinline__ f32x4 lds_f32x4(const char* base, int off) {
   return *reinterpret_cast<const f32x4*>(base + off);
 }
 
-// SPLIT: the split wrap option (compiled separately, so that the main method's
-// step loop carries no trace of it).
-template <int D, bool SPLIT>
+// SPLIT: the split wrap option; EDGE: groups that are not whole tiles (query
+// rows of the next group are masked, tiles that cross the wrap point or the
+// end of the sequence take per-row addresses, keys past the group are not
+// stored).  Each is compiled separately, so that the main method's step loop
+// carries no trace of either.
+template <int D, bool SPLIT, bool EDGE>
 __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
@@ -498,7 +501,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
   const int kg = wave & 3, qh = wave >> 2;
 
-  const int groups = N / G, tiles_per_group = G / BKV;
+  const int groups = EDGE ? num_groups(N, G) : N / G;
+  const int tiles_per_group = EDGE ? (G + BKV - 1) / BKV : G / BKV;
   const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
   const int pos = to.rank, grp = to.pair % groups;       // key tiles early in a group first
   const int c = (to.pair / groups) % Hkv, b = to.pair / (groups * Hkv);
@@ -506,6 +510,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   const int h0 = c * r;
   const int sig0 = (h0 >= H - shift_heads) ? G / 2 : 0;
   const int j0 = grp * G + pos * BKV;                 // key rows, rolled frame of head h0
+  const int ge0 = EDGE ? min(grp * G + G, N) : grp * G + G;   // end of their group
+  if (EDGE && j0 >= ge0) return;                      // a tile past the end of a short group
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
   const bf16* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
@@ -517,7 +523,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const int cb = (wave + S::kWaves * i) * 64;
     const int p = cb + lane;
     const int row = p / CPR, pc = p % CPR;
-    const size_t g = (size_t)orig_row(j0 + row, sig0, N) * kvstride + (pc ^ swz2<CPR>(row)) * 8;
+    const size_t g = (size_t)orig_row(EDGE ? min(j0 + row, N - 1) : j0 + row, sig0, N) * kvstride +
+                     (pc ^ swz2<CPR>(row)) * 8;
     load_lds16(kb + g, lds + S::kK + cb * 16);
     load_lds16(vb + g, lds + S::kV + cb * 16);
   }
@@ -561,17 +568,23 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   // shifted), so they are fixed here: first key row in the head's rolled frame,
   // the head's query tiles [qt_b, qt_e) meeting the tile's keys, and the end
   // row of the queries meeting this wave's keys.
-  int fr_jk0[2], fr_qb[2], fr_qe[2], fr_wqe[2];
+  // EDGE: the group end qge bounds every query (the last query tile may run
+  // into the next group), and keys past it belong to the next group.
+  int fr_jk0[2], fr_qb[2], fr_qe[2], fr_wqe[2], fr_qge[2];
 #pragma unroll
   for (int sh = 0; sh < 2; ++sh) {
     int jk = j0 + sig0 - sh * (G / 2);
     if (jk < 0) jk += N;
     if (jk >= N) jk -= N;
     const bool split_head = SPLIT && sh;
+    const int qge = query_end_row(jk, G, N, false);
     fr_jk0[sh] = jk;
     fr_qb[sh] = jk / BQ;
-    fr_qe[sh] = query_end_row(jk + BKV - 32, G, N, split_head) / BQ;
-    fr_wqe[sh] = query_end_row(jk + kg * 32, G, N, split_head);
+    fr_qe[sh] = EDGE ? (min(query_end_row(jk + BKV - 32, G, N, false), qge) + BQ - 1) / BQ
+                     : query_end_row(jk + BKV - 32, G, N, split_head) / BQ;
+    fr_wqe[sh] = EDGE ? min(query_end_row(jk + kg * 32, G, N, false), qge)
+                      : query_end_row(jk + kg * 32, G, N, split_head);
+    fr_qge[sh] = qge;
   }
   auto head_frame = [&](int hh, int& sig, int& jk0, int& qt_b, int& qt_e, int& wqe) {
     const int sh = h0 + hh >= H - shift_heads;
@@ -581,8 +594,29 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     qt_e = fr_qe[sh];
     wqe = fr_wqe[sh];
   };
+  // EDGE: the group end; one frame only (a KV head shared by shifted and
+  // unshifted query heads needs whole tiles)
+  const int qge = fr_qge[sig0 != 0];
   auto issue_step = [&](int hh, int qt, int sig, int stage) {
     const int h = h0 + hh;
+    // EDGE: a query tile that wraps from token N-1 to token 0, or runs past row
+    // N, takes each row's own address (rows past N read row N-1: masked)
+    if (EDGE && (qt * BQ + BQ > N || (sig != 0 && qt * BQ < N - sig && qt * BQ + BQ > N - sig))) {
+#pragma unroll
+      for (int i = 0; i < S::kQLoads; ++i) {
+        const int p = (wave + S::kWaves * i) * 64 + lane;
+        const int row = p / CPR, pc = p % CPR;
+        const int tok = orig_row(min(qt * BQ + row, N - 1), sig, N);
+        const int off = (tok * (int)qstride + h * D + (pc ^ swz2<CPR>(row)) * 8) * 2;
+        const int cb = (wave + S::kWaves * i) * 64 * 16;
+        buffer_load_lds16(qrs, off, 0, lds + S::kQ + stage * S::kQTileB + cb);
+        buffer_load_lds16(dors, off, 0, lds + S::kdO + stage * S::kQTileB + cb);
+      }
+      const int loff = (h * N + orig_row(min(qt * BQ + lane, N - 1), sig, N)) * 4;
+      if (wave == 0) buffer_load_lds4(lrs, loff, 0, lds + S::kF + stage * 2 * BQ * 4);
+      if (wave == 1) buffer_load_lds4(drs, loff, 0, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
+      return;
+    }
     const int t0 = orig_row(qt * BQ, sig, N);         // a 64-row tile is contiguous
     const int soff = (t0 * (int)qstride + h * D) * 2;
 #pragma unroll
@@ -604,7 +638,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   const float c2 = scale * kLog2e;
 
   // one query step for this wave: STG = LDS stage, MASK = causal mask needed
-  auto compute = [&](auto stg_c, auto mask_c, int jkey, int jq_first) {
+  auto compute = [&](auto stg_c, auto mask_c, int jkey, int jq_first) __attribute__((always_inline)) {
     constexpr int STG = decltype(stg_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
     const char* Qs = lds + S::kQ + STG * S::kQTileB;
@@ -630,7 +664,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
         const float lq = i < 4 ? l0[i] : l1[i - 4];
         const float dq = i < 4 ? d0[i] : d1[i - 4];
         float p = fast_exp2(fmaf(sacc[u * 8 + i], c2, -lq));
-        if (MASK && jkey > jq_first + u * 16 + i) p = 0.f;
+        if (MASK && (jkey > jq_first + u * 16 + i || (EDGE && jq_first + u * 16 + i >= qge))) p = 0.f;
         pv[i] = p;
         sv[i] = p * (pacc[u * 8 + i] - dq);
       }
@@ -650,9 +684,9 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const int jq0 = qt * BQ;
     const int key_lo = jk0 + kg * 32, q_lo = jq0 + qh * 32;
     if (key_lo > q_lo + 31) return;                   // every key follows every query: P = 0
-    if (SPLIT && q_lo >= wqe) return;                 // queries of another group than the wave's keys
+    if ((SPLIT || EDGE) && q_lo >= wqe) return;       // queries of another group than the wave's keys
     const int jkey = key_lo + l32, jq_first = q_lo + hf * 8;
-    if (key_lo + 31 > q_lo)
+    if (key_lo + 31 > q_lo || (EDGE && q_lo + 31 >= qge))
       compute(stg_c, std::integral_constant<bool, true>(), jkey, jq_first);
     else
       compute(stg_c, std::integral_constant<bool, false>(), jkey, jq_first);
@@ -709,6 +743,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
         dkacc[dt][i] += xs[((0 * S::kDT + dt) * 16 + i) * 64 + lane];
         dvacc[dt][i] += xs[((1 * S::kDT + dt) * 16 + i) * 64 + lane];
       }
+    if (EDGE && j0 + key_row >= ge0) return;          // a key of the next group
     const int tk = orig_row(j0 + key_row, sig0, N);
     bf16* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
     bf16* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
@@ -729,6 +764,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
 // PREP: the prep stage fused in.  Every query row belongs to exactly one
 // workgroup, which already holds its dO row, so it computes Dvec = dO . O and
 // lse * log2(e) itself and writes both to the workspace for the dK/dV stage.
+// EDGE: groups that are not whole tiles, as in the forward kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqB16Shape {
@@ -743,7 +779,7 @@ struct DqB16Shape {
   static constexpr int kDT = D / 32;
 };
 
-template <int D, bool PREP>
+template <int D, bool PREP, bool EDGE>
 __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const bf16* __restrict__ o, const float* __restrict__ lse,
@@ -763,7 +799,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   const int l32 = lane & 31, hf = lane >> 5;
   const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
 
-  const int groups = N / G, tiles_per_group = G / BR;
+  const int groups = EDGE ? num_groups(N, G) : N / G;
+  const int tiles_per_group = EDGE ? (G + BR - 1) / BR : G / BR;
   const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
   const int pos = tiles_per_group - 1 - to.rank;
   const int grp = to.pair % groups;
@@ -771,9 +808,11 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
   const bool split_head = split && sigma != 0;
+  const int ge = EDGE ? min(grp * G + G, N) : grp * G + G;   // end of the group
   const int j0 = grp * G + pos * BR;
+  if (EDGE && j0 >= ge) return;                      // a tile past the end of a short group
   const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
-  const int ntiles = (j0 + BR - kv_begin) / BC;
+  const int ntiles = EDGE ? (min(j0 + BR, ge) - kv_begin + BC - 1) / BC : (j0 + BR - kv_begin) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
   const bf16* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
@@ -781,7 +820,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
 
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
-  const int tq = orig_row(jq, sigma, N);
+  const bool q_ok = !EDGE || jq < ge;                // EDGE: rows past the group read its last row
+  const int tq = orig_row(q_ok ? jq : ge - 1, sigma, N);
   const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
   bf16x8 qf[S::kDC], dof[S::kDC];
   {
@@ -807,7 +847,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     }
     dvec_q = sum_halves(part);
     lse_q = lse[rix] * kLog2e;
-    if (hf == 0) {
+    if (hf == 0 && q_ok) {
       dvec[rix] = dvec_q;
       lse2[rix] = lse_q;
     }
@@ -829,9 +869,24 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     toff[i] = (row * (int)kvstride + (pc ^ swz2<CPR>(row)) * 8) * 2;
   }
   auto issue_tile = [&](int kt0, int stage) {
-    const int t0 = orig_row(kt0, sigma, N) * (int)kvstride * 2;   // whole tile is contiguous
     char* kd = kbuf(stage);
     char* vd = vbuf(stage);
+    // EDGE: a tile whose rows wrap from token N-1 to token 0, or run past row
+    // N, takes each row's own address (rows past N read row N-1: masked keys)
+    if (EDGE && (kt0 + BC > N || (sigma != 0 && kt0 < N - sigma && kt0 + BC > N - sigma))) {
+#pragma unroll
+      for (int i = 0; i < S::kLoads; ++i) {
+        const int p = (wave + S::kWaves * i) * 64 + lane;
+        const int row = p / CPR, pc = p % CPR;
+        const int tok = orig_row(min(kt0 + row, N - 1), sigma, N);
+        const int cb = (wave + S::kWaves * i) * 64 * 16;
+        const int off = (tok * (int)kvstride + (pc ^ swz2<CPR>(row)) * 8) * 2;
+        buffer_load_lds16(krs, off, 0, kd + cb);
+        buffer_load_lds16(vrs, off, 0, vd + cb);
+      }
+      return;
+    }
+    const int t0 = orig_row(kt0, sigma, N) * (int)kvstride * 2;   // whole tile is contiguous
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
@@ -908,6 +963,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     __syncthreads();
     if (it + 1 < ntiles) issue_tile(kt0 + BC, STG ^ 1);
     if (kt0 > jw + 31 || kt0 < kw0) return;      // tile after this wave's queries, or outside its group
+    if (EDGE && jw >= ge) return;                // every query of this wave is past the group
     if (kt0 + BC - 1 > jw)
       compute(stg_c, std::integral_constant<bool, true>(), kt0);
     else
@@ -922,6 +978,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     if (++it == ntiles) break;
   }
 
+  if (!q_ok) return;
   bf16* dqrow = dq + ((size_t)b * N + tq) * qstride + (size_t)h * D;
 #pragma unroll
   for (int dt = 0; dt < S::kDT; ++dt)
@@ -957,15 +1014,21 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
                             const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
                             int shift_heads, int split, float scale, hipStream_t stream) {
   using S = DkdvB16Shape<D>;
-  const dim3 grid(B * Hkv * (N / S::kBKV)), block(S::kThreads);
+  constexpr int BKV = S::kBKV;
+  const bool whole = N % G == 0 && G % BKV == 0;     // the split option implies whole tiles
+  const dim3 grid(whole ? B * Hkv * (N / BKV) : B * Hkv * ((N + G - 1) / G) * ((G + BKV - 1) / BKV));
+  const dim3 block(S::kThreads);
+#define S2A_DKDV_LAUNCH(SPLIT, EDGE)                                                                           \
+  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, SPLIT, EDGE>), grid, block, 0, stream, (const bf16*)q,           \
+                     (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk, (bf16*)dv, N, H, Hkv, \
+                     G, shift_heads, scale)
   if (split)
-    hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, true>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk, (bf16*)dv, N, H, Hkv, G, shift_heads,
-                       scale);
+    S2A_DKDV_LAUNCH(true, false);
+  else if (whole)
+    S2A_DKDV_LAUNCH(false, false);
   else
-    hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, false>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk, (bf16*)dv, N, H, Hkv, G, shift_heads,
-                       scale);
+    S2A_DKDV_LAUNCH(false, true);
+#undef S2A_DKDV_LAUNCH
   return hipGetLastError();
 }
 
@@ -990,9 +1053,8 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            int shift_heads, int split, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
-    // the fast kernel takes whole 128-key tiles of whole groups, and addresses
-    // one batch's Q / dO with 31-bit byte offsets
-    if (G % DkdvB16Shape<D>::kBKV == 0 && N % G == 0 && (size_t)N * H * D * sizeof(T) < (size_t(1) << 31))
+    // the fast kernel addresses one batch's Q / dO with 31-bit byte offsets
+    if ((size_t)N * H * D * sizeof(T) < (size_t(1) << 31))
       return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, split, scale, stream);
   }
   return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, split, scale, stream);
@@ -1004,15 +1066,20 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
                           const float* lse, float* lse2, float* dvec, void* dq, int B, int H, int Hkv, int N, int G,
                           int shift_heads, int split, float scale, hipStream_t stream) {
   using S = DqB16Shape<D>;
-  const dim3 grid(B * H * (N / S::kBR)), block(S::kThreads);
-  if (o)
-    hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, true>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dO, (const bf16*)o, lse, lse2, dvec, (bf16*)dq, N, H, Hkv, G,
-                       shift_heads, split, scale);
-  else
-    hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, false>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dO, (const bf16*)nullptr, (const float*)nullptr, lse2, dvec,
-                       (bf16*)dq, N, H, Hkv, G, shift_heads, split, scale);
+  constexpr int BR = S::kBR;
+  const bool whole = N % G == 0 && G % BR == 0;
+  const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR)), block(S::kThreads);
+  const bf16* ob = (const bf16*)o;
+#define S2A_DQ_LAUNCH(PREP, EDGE)                                                                             \
+  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, PREP, EDGE>), grid, block, 0, stream, (const bf16*)q,           \
+                     (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec, (bf16*)dq, N, H, Hkv, \
+                     G, shift_heads, split, scale)
+  if (o) {
+    if (whole) S2A_DQ_LAUNCH(true, false); else S2A_DQ_LAUNCH(true, true);
+  } else {
+    if (whole) S2A_DQ_LAUNCH(false, false); else S2A_DQ_LAUNCH(false, true);
+  }
+#undef S2A_DQ_LAUNCH
   return hipGetLastError();
 }
 
@@ -1031,12 +1098,11 @@ hipError_t launch_dq_generic(const void* q, const void* k, const void* v, const 
   return hipGetLastError();
 }
 
-// the fast dq kernel takes whole 256-row tiles of whole groups, and addresses
-// one batch's K / V with 31-bit byte offsets
+// the fast dq kernel addresses one batch's K / V with 31-bit byte offsets
 template <typename T, int D>
 bool dq_fast(int N, int Hkv, int G) {
-  return sizeof(T) == 2 && G % DqB16Shape<D>::kBR == 0 && N % G == 0 &&
-         (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31);
+  (void)G;
+  return sizeof(T) == 2 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31);
 }
 
 template <typename T, int D>

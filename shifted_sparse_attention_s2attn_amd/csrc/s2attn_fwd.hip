@@ -260,7 +260,12 @@ __device__ __forceinline__ int swz_v(int row) {
   return CPR == 16 ? ((4 * (row & 3)) ^ (2 * ((row >> 1) & 1))) : (2 * (row & 3));
 }
 
-template <int D>
+// EDGE: groups that are not whole tiles (a short last group, any G): query
+// rows past the group compute on a copy of its last row and are not stored,
+// key rows past it follow every query of the group and are masked, and a key
+// tile that crosses the roll's wrap point (or the end of the sequence) is
+// loaded with per-row addresses.  Compiled separately from the whole-tile case.
+template <int D, bool EDGE>
 __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse,
@@ -280,7 +285,8 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   const int l32 = lane & 31, hf = lane >> 5;
   const int g16 = lane >> 4, li = lane & 15, ts = li >> 2, tm = li & 3;
 
-  const int groups = N / G, tiles_per_group = G / BR;
+  const int groups = EDGE ? num_groups(N, G) : N / G;
+  const int tiles_per_group = EDGE ? (G + BR - 1) / BR : G / BR;
   const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
   const int pos = tiles_per_group - 1 - to.rank;     // heaviest query tiles first
   const int grp = to.pair % groups;
@@ -288,18 +294,21 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
   const bool split_head = split && sigma != 0;
+  const int ge = EDGE ? min(grp * G + G, N) : grp * G + G;   // end of the group
   const int j0 = grp * G + pos * BR;
+  if (EDGE && j0 >= ge) return;                      // a tile past the end of a short group
   const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
-  const int ntiles = (j0 + BR - kv_begin) / BC;
+  const int ntiles = EDGE ? (min(j0 + BR, ge) - kv_begin + BC - 1) / BC : (j0 + BR - kv_begin) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
   const bf16* kb = k + (size_t)b * N * kvstride + (size_t)c * D;
   const bf16* vb = v + (size_t)b * N * kvstride + (size_t)c * D;
 
-  // Q operand in registers
+  // Q operand in registers (EDGE: rows past the group read its last row)
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
-  const int tq = orig_row(jq, sigma, N);
+  const bool q_ok = !EDGE || jq < ge;
+  const int tq = orig_row(q_ok ? jq : ge - 1, sigma, N);
   const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
   bf16x8 qf[S::kDC];
   {
@@ -322,9 +331,23 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     voff[i] = (row * (int)kvstride + (pc ^ swz_v<CPR>(row)) * 8) * 2;
   }
   auto issue_tile = [&](int kt0, int stage) {
-    const int t0 = orig_row(kt0, sigma, N) * (int)kvstride * 2;   // whole tile is contiguous
     char* kd = kbuf(stage);
     char* vd = vbuf(stage);
+    // EDGE: a tile whose rows wrap from token N-1 to token 0, or run past row
+    // N, takes each row's own address (rows past N read row N-1: masked keys)
+    if (EDGE && (kt0 + BC > N || (sigma != 0 && kt0 < N - sigma && kt0 + BC > N - sigma))) {
+#pragma unroll
+      for (int i = 0; i < S::kLoads; ++i) {
+        const int p = (wave + S::kWaves * i) * 64 + lane;
+        const int row = p / CPR, pc = p % CPR;
+        const int tok = orig_row(min(kt0 + row, N - 1), sigma, N);
+        const int cb = (wave + S::kWaves * i) * 64 * 16;
+        buffer_load_lds16(krs, (tok * (int)kvstride + (pc ^ swz_k<CPR>(row)) * 8) * 2, 0, kd + cb);
+        buffer_load_lds16(vrs, (tok * (int)kvstride + (pc ^ swz_v<CPR>(row)) * 8) * 2, 0, vd + cb);
+      }
+      return;
+    }
+    const int t0 = orig_row(kt0, sigma, N) * (int)kvstride * 2;   // whole tile is contiguous
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
@@ -425,6 +448,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     __syncthreads();                             // ... and everyone's; the other stage is free
     if (it + 1 < ntiles) issue_tile(kt0 + BC, STG ^ 1);
     if (kt0 > jw + 31 || kt0 < kw0) return;      // tile after this wave's queries, or outside its group
+    if (EDGE && jw >= ge) return;                // every query of this wave is past the group
     if (kt0 + BC - 1 > jw)
       compute(stg_c, std::integral_constant<bool, true>(), kt0);
     else
@@ -440,6 +464,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   }
 
   const float l_tot = sum_halves(l_run);
+  if (!q_ok) return;
   const float inv = 1.f / l_tot;
   bf16* orow = o + ((size_t)b * N + tq) * qstride + (size_t)h * D;
 #pragma unroll
@@ -454,10 +479,16 @@ template <int D>
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Hkv, int N, int G, int shift_heads, int split, float scale,
                            hipStream_t stream) {
-  dim3 grid(B * H * (N / FwdB16Shape<D>::kBR));
-  hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D>), grid, dim3(FwdB16Shape<D>::kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads, split,
-                     scale);
+  constexpr int BR = FwdB16Shape<D>::kBR;
+  const dim3 block(FwdB16Shape<D>::kThreads);
+  if (N % G == 0 && G % BR == 0)
+    hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, false>), dim3(B * H * (N / BR)), block, 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads,
+                       split, scale);
+  else
+    hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, true>), dim3(B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR)),
+                       block, 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv,
+                       G, shift_heads, split, scale);
   return hipGetLastError();
 }
 
@@ -466,9 +497,8 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int B, int H, int Hkv, int N, int G, int shift_heads, int split, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
-    // the fast kernel takes whole 256-row tiles of whole groups, and addresses
-    // one batch's K / V with 31-bit byte offsets
-    if (G % FwdB16Shape<D>::kBR == 0 && N % G == 0 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
+    // the fast kernel addresses one batch's K / V with 31-bit byte offsets
+    if ((size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
       return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, split, scale, stream);
   }
   constexpr int BR = FwdShape<T, D>::kBR;
