@@ -22,9 +22,9 @@
 //          on lanes), so dS feeds dQ^T = K^T dS^T straight from registers.
 // dS is kept without the softmax scale; dK and dQ take it at their stores.
 // Each stage has a generic kernel (any element type, register-staged LDS
-// tiles; used for fp32, and for groups that are not whole tiles) and a bf16
-// kernel laid out for the bf16 matrix cores (direct-to-LDS tile loads,
-// transposing LDS reads) for whole groups of whole tiles.
+// tiles; used for fp32 and for bf16 batch slices over 2 GiB) and a bf16 kernel
+// laid out for the bf16 matrix cores (direct-to-LDS tile loads, transposing LDS
+// reads), with a separate instantiation for groups that are not whole tiles.
 #include "s2attn_common.h"
 
 #include <type_traits>

@@ -20,10 +20,11 @@
 //     its 32 keys split across lanes l and l ^ 32)
 //     O^T += V^T P^T     (P^T comes straight from the S^T registers)
 // Finally O = O^T / l is stored at the original rows with lse = m + ln l.
-// This kernel also takes groups that are not whole tiles (a short last group
-// when G does not divide N, or any G): query rows past the group compute on a
-// copy of its last row and are not stored, key rows past it (the next group, or
-// past N, clamped to a real row) follow every query of the group and are masked.
+// This kernel (fp32, and bf16 slices over 2 GiB) also takes groups that are not
+// whole tiles (a short last group when G does not divide N, or any G): query
+// rows past the group compute on a copy of its last row and are not stored, key
+// rows past it (the next group, or past N, clamped to a real row) follow every
+// query of the group and are masked.
 #include "s2attn_common.h"
 
 #include <type_traits>
@@ -222,7 +223,8 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// bf16 forward for groups holding a whole number of 256-row query tiles.
+// bf16 forward (any G: whole 256-row query tiles of whole groups, or the EDGE
+// instantiation below).
 //
 // 8 waves (two per SIMD, so one wave's matrix-core work overlaps another's
 // softmax) share each 64-row key/value tile; each wave owns 32 query rows.
