@@ -39,9 +39,10 @@
  *
  * Supported: d in {64, 128}; dtype bf16 (fp32 accumulation, P and dS rounded
  * to bf16 for the matrix cores) or fp32 (fp32 matrix cores throughout);
- * 1 <= G <= N.  Shapes whose groups are whole 128-row tiles (G a multiple of
- * 128, N a multiple of G) run the fast bf16 kernels; any other G runs the
- * generic kernels.  When a key/value head is shared by shifted and unshifted
+ * 1 <= G <= N.  bf16 runs kernels laid out for the bf16 matrix cores at any
+ * G (groups that are not whole 128-row tiles take slower instantiations that
+ * address rows one by one near group ends); fp32, and bf16 batch slices of
+ * 2 GiB or more, run generic kernels.  When a key/value head is shared by shifted and unshifted
  * query heads (H - shift_heads not a multiple of H / Hkv), and for the split
  * wrap option, the groups must be whole tiles (for the shared head, G a
  * multiple of 256).  Grids: B * H * ceil(N / G) * ceil(G / 128) < 2^31.

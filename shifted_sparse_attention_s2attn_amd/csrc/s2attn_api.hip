@@ -29,7 +29,9 @@ namespace {
 constexpr int kTileRows = 128;   // query rows per forward workgroup = key rows per backward workgroup
 
 // Whole groups of whole 128-row tiles.  Other shapes (G not dividing N, so the
-// last group is short, or G not a multiple of 128) run on the generic kernels.
+// last group is short, or G not a multiple of 128) take the kernels' EDGE
+// instantiations, which address tiles row by row where they cross a group end,
+// the wrap point or the sequence end.
 bool aligned(int N, int G) { return N % G == 0 && G % kTileRows == 0; }
 
 // Sizes only (no pointers).  B == 0 or N == 0 is a valid, empty problem.

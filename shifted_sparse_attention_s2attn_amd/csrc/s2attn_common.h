@@ -100,7 +100,7 @@ __device__ __forceinline__ int orig_row(int j, int sigma, int N) {
 
 // Groups of one head: N / G rounded up.  When G does not divide N the last
 // group holds the N mod G rows that remain (the reading taken for group sizes
-// like Table 7's 1/6 of the context); such shapes run on the generic kernels.
+// like Table 7's 1/6 of the context).
 __device__ __forceinline__ int num_groups(int N, int G) { return (N + G - 1) / G; }
 
 // Wrap option of the shifted heads (page section 5, "Ablation Studies and

@@ -50,7 +50,7 @@ WORKLOADS = {
     "llama2-7b-100k": Workload("llama2-7b-100k", 1, 32, 32, 128, 102400, 25600, 16, "bf16"),
     "llama2-70b-gqa-32k": Workload("llama2-70b-gqa-32k", 1, 64, 8, 128, 32768, 8192, 32, "bf16"),
     # Table 7's 1/6 group at context 8192: G = 1365 does not divide N (the last
-    # group holds 2 tokens) and is odd (shift 682); runs the generic kernels
+    # group holds 2 tokens) and is odd (shift 682); runs the kernels' EDGE instantiations
     "llama2-7b-8k-g1365": Workload("llama2-7b-8k-g1365", 1, 32, 32, 128, 8192, 1365, 16, "bf16", True),
     # full causal attention over the whole context (G = N, no shifted heads): what the
     # fine-tuned model runs at inference (section 3.2, "Inference")

@@ -202,3 +202,22 @@ def test_bwd_stage_entry_points_validate(lib):
     assert lib.s2attn_bwd_prep_dq(*pd, DUMMY, need - 4, *sz, 0, 0, None) == _lib.S2ATTN_ERR_WORKSPACE
     assert lib.s2attn_bwd_prep_dq(*pd, DUMMY, need, *bad_n[:7], 0, 0, None) == _lib.S2ATTN_ERR_SHAPE
     assert lib.s2attn_bwd_prep_dq(*pd, DUMMY, need, *sz, 3, 0, None) == _lib.S2ATTN_ERR_UNSUPPORTED
+
+
+def test_header_is_plain_c():
+    """include/s2attn.h compiles as C11 on its own (no C++ or HIP types)."""
+    import subprocess
+    r = subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_c_client_builds_and_links(lib, tmp_path):
+    """tests/c_abi_client.c builds with gcc against the header and links to
+    libs2attn.so; run without arguments it prints its usage and exits 1 before
+    any HIP call."""
+    import subprocess
+    from build_client import build_client
+    exe = build_client(str(tmp_path / "c_abi_client"))
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr, (r.returncode, r.stderr)

@@ -109,7 +109,8 @@ def test_small_parity_split(w):
 
 
 # group sizes that do not divide the sequence, or are not whole 128-row tiles
-# (generic kernels): the last group is short, the shift floor(G/2)
+# (EDGE instantiations of the bf16 kernels, generic kernels for fp32): the last
+# group is short, the shift floor(G/2)
 UNALIGNED = [
     small_workload("bf16-short-last-group", B=1, H=4, Hkv=4, d=128, N=1000, G=256, shift_heads=2),
     small_workload("bf16-g100-gqa", B=2, H=2, Hkv=1, d=64, N=777, G=100, shift_heads=2),
@@ -357,15 +358,15 @@ def test_full_size_full_attention():
 # ---------------------------------------------------------------------------
 
 def test_repeatability():
-    """Forward, dK and dV are bitwise repeatable; dQ differs only by fp32 atomic order."""
+    """Every output is bitwise repeatable: no kernel uses atomics, so the order of
+    every sum is fixed by the code."""
     w = small_workload("rep", B=1, H=8, Hkv=2, d=128, N=2048, G=512, shift_heads=4)
     say(f"case {w}")
     t = to_gpu(make_inputs(w, seed=3))
     a = run_gpu(w, t)
     b = run_gpu(w, t)
-    for i in (0, 1, 3, 4):
+    for i in range(5):
         assert torch.equal(a[i], b[i])
-    assert float((a[2].float() - b[2].float()).abs().max()) <= 1e-2
 
 
 @pytest.mark.parametrize("wrap", ["roll", "split"])
@@ -378,8 +379,7 @@ def test_autograd_wrapper(wrap):
     (o.float() * t["do"].float()).sum().backward()
     ref = run_gpu(w, t, wrap=wrap)
     assert torch.equal(o, ref[0])
-    assert torch.equal(k.grad, ref[3]) and torch.equal(v.grad, ref[4])
-    assert float((q.grad.float() - ref[2].float()).abs().max()) <= 1e-2
+    assert torch.equal(q.grad, ref[2]) and torch.equal(k.grad, ref[3]) and torch.equal(v.grad, ref[4])
 
 
 @pytest.mark.parametrize("G,dtype", [(256, "bf16"), (100, "bf16"), (256, "f32")])
