@@ -453,15 +453,16 @@ struct DkdvB16Shape {
   static constexpr int kRowB = D * 2;                     // bytes per tile row
   static constexpr int kQTileB = kBQ * kRowB;
   static constexpr int kKTileB = kBKV * kRowB;
-  // byte offsets: the per-step Q and dO stages first, so that every read of
-  // them is a per-lane offset plus a 16-bit immediate; the resident K and V
-  // tiles above them share one set of per-lane offsets (V = K + immediate)
-  static constexpr int kQ = 0;                            // [2 stages]
+  // byte offsets: the per-step stages (lse*log2(e) and Dvec, Q, dO) first, so
+  // that every read of them is a per-lane offset plus a 16-bit immediate; the
+  // resident K and V tiles above them share one set of per-lane addresses
+  // (V = K + immediate)
+  static constexpr int kF = 0;                            // floats [stage][lse2 | dvec][kBQ]
+  static constexpr int kQ = kF + 2 * 2 * kBQ * (int)sizeof(float);   // [2 stages]
   static constexpr int kdO = kQ + 2 * kQTileB;            // [2 stages]
   static constexpr int kK = kdO + 2 * kQTileB;
   static constexpr int kV = kK + kKTileB;
-  static constexpr int kF = kV + kKTileB;                 // floats [stage][lse2 | dvec][kBQ]
-  static constexpr size_t kLdsBytes = (size_t)kF + 2 * 2 * kBQ * sizeof(float);
+  static constexpr size_t kLdsBytes = (size_t)kV + kKTileB;
   static constexpr int kDC = D / 16;
   static constexpr int kDT = D / 32;
   static constexpr int kQLoads = kBQ * kCPR / kThreads;   // 16-byte chunks per thread per Q (or dO) tile
@@ -544,13 +545,17 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
 
   // ---- per-lane LDS byte offsets
   const int key_row = kg * 32 + l32;                  // B operand of S and dP: this lane's key
-  int offB[S::kDC];
+  int offB[S::kDC];                                   // LDS addresses of the K operand; V = K + kKTileB
   const int arow = qh * 32 + perm32(l32);             // A operand of S and dP: query rows
   int offA[S::kDC];
 #pragma unroll
   for (int cc = 0; cc < S::kDC; ++cc) {
-    offB[cc] = key_row * RB + (((2 * cc + hf) ^ swz2<CPR>(key_row)) << 4);
+    offB[cc] = S::kK + key_row * RB + (((2 * cc + hf) ^ swz2<CPR>(key_row)) << 4);
     offA[cc] = arow * RB + (((2 * cc + hf) ^ swz2<CPR>(arow)) << 4);
+    // hide the value from the optimiser, so that the V reads address it plus an
+    // immediate instead of taking registers of their own (K and V lie beyond
+    // the 16-bit immediate range)
+    asm volatile("" : "+v"(offB[cc]));
   }
   // transposing reads of dO^T / Q^T: rows (queries) qh*32 + 16u + 8hf + 4t + ts, head-dim columns of block dt
   int offT[S::kDT][2];
@@ -649,8 +654,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; pacc[i] = 0.f; }
 #pragma unroll
     for (int cc = 0; cc < S::kDC; ++cc) {
-      mma32(sacc, lds_b128(Qs, offA[cc]), lds_b128(lds + S::kK, offB[cc]));
-      mma32(pacc, lds_b128(dOs, offA[cc]), lds_b128(lds + S::kV, offB[cc]));
+      mma32(sacc, lds_b128(Qs, offA[cc]), lds_b128(lds, offB[cc]));
+      mma32(pacc, lds_b128(dOs, offA[cc]), lds_b128(lds, offB[cc] + S::kKTileB));
     }
     // P and dS of each 16-query half, then that half's dV / dK products, so the
     // second half's vector work can overlap the first half's matrix work
