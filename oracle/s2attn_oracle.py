@@ -32,6 +32,13 @@ Language Models", paper-graph-ui summary, section 3.4):
   to its start (the last one: the last G/2 tokens, then the first G/2) is cut
   at the wrap into two causal groups; every other group, and every unshifted
   head, is as in the main method (``wrap="roll"``).
+* Wrap-group option ``wrap="swap"`` (the same Table 8, Variant 3: the shifted
+  tokens swap places with the original front tokens).  Reading taken here: in
+  a shifted head the rolled group that wraps keeps its tokens, but the part the
+  roll carried from the front of the sequence (tokens 0, 1, ...) is placed
+  before the part from the end, so that inside every group causal order is the
+  original token order; every other group, and every unshifted head, is as in
+  the main method.
 * Group sizes that do not divide the sequence (section 5, "Ablation Studies
   and Robustness Checks", Table 7: a 1/6 group, 1365 tokens, at context 8192;
   Algorithm 1's reshape needs N to be a multiple of G there, and the pages do
@@ -62,15 +69,19 @@ of "The shifting mechanism"; ``row_attention`` against the brute-force
 attention row by row.  The split wrap option is pinned by the same
 brute-force mask with the split partition, by causal SDPA over each split group
 as a contiguous token range, by finite differences, and by its agreement with
-the main method wherever the two partitions coincide.
+the main method wherever the two partitions coincide.  The swap option is
+pinned by the brute-force mask of the same partition with original-order
+causality, by causal SDPA over each group gathered in token order, by finite
+differences, and by its agreement with the main method and the split option
+where they coincide.
 """
 
 import numpy as np
 
-WRAPS = ("roll", "split")
+WRAPS = ("roll", "split", "swap")
 
 __all__ = [
-    "WRAPS", "check_problem", "num_groups", "head_shift", "kv_head", "rolled_order", "group_parts",
+    "WRAPS", "check_problem", "num_groups", "head_shift", "kv_head", "rolled_order", "group_order", "group_parts",
     "group_forward", "group_backward",
     "forward", "backward",
     "head_group_forward", "head_group_backward", "row_attention",
@@ -82,7 +93,7 @@ def check_problem(B, N, H, Hkv, d, G, shift_heads, wrap="roll"):
 
     Grouping cuts the sequence into groups of G tokens (Algorithm 1's reshape to
     [B*N/G, G, ...]; a last, shorter group when G does not divide N), so G must
-    lie in [1, N].  ``wrap`` is "roll" (the main method) or "split".
+    lie in [1, N].  ``wrap`` is "roll" (the main method), "split" or "swap".
     """
     if wrap not in WRAPS:
         raise ValueError(f"wrap must be one of {WRAPS}, got {wrap!r}")
@@ -125,6 +136,27 @@ def rolled_order(N, sigma):
     return (np.arange(N) + sigma) % N
 
 
+def _wrap_cut(rows):
+    """Index in ``rows`` (a rolled group, original token indices) of the first
+    token after the wrap from the end of the sequence to its start, or None."""
+    wraps = np.nonzero(np.diff(rows) < 0)[0]
+    return int(wraps[0]) + 1 if len(wraps) else None
+
+
+def group_order(rows, sigma, wrap):
+    """The order in which the tokens of one rolled group attend causally.
+
+    Rolled order, except under ``wrap="swap"`` for the group of a shifted head
+    in which the rolled order wraps: there the tokens after the wrap (carried
+    from the front of the sequence) are moved before the tokens of the end.
+    """
+    if wrap == "swap" and sigma:
+        cut = _wrap_cut(rows)
+        if cut is not None:
+            return np.concatenate([rows[cut:], rows[:cut]])
+    return rows
+
+
 def group_parts(rows, sigma, wrap):
     """The causal groups that one rolled group (original rows ``rows``, in
     rolled order) is made of.
@@ -136,9 +168,8 @@ def group_parts(rows, sigma, wrap):
     of ``rows`` that cover it.
     """
     if wrap == "split" and sigma:
-        wraps = np.nonzero(np.diff(rows) < 0)[0]
-        if len(wraps):
-            cut = int(wraps[0]) + 1
+        cut = _wrap_cut(rows)
+        if cut is not None:
             return [slice(0, cut), slice(cut, len(rows))]
     return [slice(0, len(rows))]
 
@@ -200,11 +231,12 @@ def head_group_forward(q, k, v, G, shift_heads, b, h, g, wrap="roll"):
     """Forward of one (batch b, query head h, group g of h's rolled frame).
 
     Returns (rows, O, lse): ``rows`` are the original token indices of the group
-    in rolled order; O[i] and lse[i] belong to original token rows[i].
+    in the order its causal attention runs (rolled order; see ``group_order``);
+    O[i] and lse[i] belong to original token rows[i].
     """
     B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads, wrap)
     sigma = head_shift(h, H, shift_heads, G)
-    rows = rolled_order(N, sigma)[g * G:(g + 1) * G]
+    rows = group_order(rolled_order(N, sigma)[g * G:(g + 1) * G], sigma, wrap)
     c = kv_head(h, H, Hkv)
     O = np.empty((len(rows), d), dtype=np.float64)
     lse = np.empty(len(rows), dtype=np.float64)
@@ -226,7 +258,7 @@ def head_group_backward(q, k, v, do, G, shift_heads, b, h, g, wrap="roll"):
     """
     B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads, wrap)
     sigma = head_shift(h, H, shift_heads, G)
-    rows = rolled_order(N, sigma)[g * G:(g + 1) * G]
+    rows = group_order(rolled_order(N, sigma)[g * G:(g + 1) * G], sigma, wrap)
     c = kv_head(h, H, Hkv)
     scale = 1.0 / np.sqrt(d)
     dQ = np.empty((len(rows), d), dtype=np.float64)
@@ -247,7 +279,7 @@ def row_attention(q, k, v, do, G, shift_heads, b, h, t, wrap="roll"):
     """Everything about one query token t of head h, from its own row only.
 
     The keys token t attends to are the tokens of its causal group that come at
-    or before it in the group's rolled order.  Returns a dict: ``keys`` (their
+    or before it in the group's causal order (``group_order``).  Returns a dict: ``keys`` (their
     original indices, in that order), ``o`` and ``lse`` of token t, the row of
     attention weights ``p`` and of score gradients ``ds`` over ``keys`` (for L =
     sum(o * do)), and ``dq`` of token t.  Key/value gradients of key u are then
@@ -257,10 +289,9 @@ def row_attention(q, k, v, do, G, shift_heads, b, h, t, wrap="roll"):
     B, N, H, Hkv, d = _dims(q, k, v, G, shift_heads, wrap)
     sigma = head_shift(h, H, shift_heads, G)
     order = rolled_order(N, sigma)
-    j = int(np.nonzero(order == t)[0][0])   # rolled position of token t
-    g = j // G
-    rows = order[g * G:(g + 1) * G]
-    pos = j - g * G
+    g = int(np.nonzero(order == t)[0][0]) // G   # group of token t
+    rows = group_order(order[g * G:(g + 1) * G], sigma, wrap)
+    pos = int(np.nonzero(rows == t)[0][0])       # its place in the group's causal order
     part = next(pt for pt in group_parts(rows, sigma, wrap) if pt.start <= pos < pt.stop)
     keys = rows[part.start:pos + 1]
     c = kv_head(h, H, Hkv)

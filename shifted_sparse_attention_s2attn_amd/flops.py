@@ -20,7 +20,9 @@ def allowed_pairs(B, H, N, G, shift_heads=0, wrap="roll"):
 
     With the split wrap option each shifted head's wrap group loses the pairs of
     the wrapped tokens (the last floor(G/2) of the group) with the tokens before
-    them, (G - floor(G/2)) floor(G/2) of them.
+    them, (G - floor(G/2)) floor(G/2) of them.  The swap option only reorders
+    the wrap group, which stays one causal triangle: the count is the main
+    method's.
     """
     rem = N % G
     pairs = B * H * ((N // G) * G * (G + 1) // 2 + rem * (rem + 1) // 2)

@@ -49,7 +49,7 @@ def _close(a, b, tol, what):
 # P1: brute force in original coordinates
 # ---------------------------------------------------------------------------
 
-def allowed_mask_original(N, G, shifted, split=False):
+def allowed_mask_original(N, G, shifted, split=False, swap=False):
     """M[t, u] = token t may attend token u, written without any roll.
 
     Unshifted heads: groups are [kG, (k+1)G) and a token sees the earlier tokens
@@ -60,6 +60,9 @@ def allowed_mask_original(N, G, shifted, split=False):
     Variant 2): additionally both tokens must lie on the same side of the wrap
     (both among the first G/2 tokens, or both not), so for N a multiple of G the
     groups are [0, G/2), [G/2 + jG, G/2 + (j+1)G) and [N - G/2, N).
+    Shifted heads with ``swap`` (Variant 3): the groups of the main method, with
+    "earlier" meaning a smaller token index in every group (the first G/2
+    tokens come before the last G/2 in the group they share).
     When G does not divide N the groups are counted from the start of the
     (shifted) grid and the last one is short; the shift is floor(G/2).
     """
@@ -75,6 +78,9 @@ def allowed_mask_original(N, G, shifted, split=False):
                 ou = (u - half) % N
                 same = (ot // G) == (ou // G) and ((t < half) == (u < half))
                 before = ou <= ot
+            elif swap:
+                same = ((t - half) % N) // G == ((u - half) % N) // G
+                before = u <= t
             else:
                 # offset of each token from the start of the shifted grid
                 ot = (t - half) % N
@@ -85,7 +91,7 @@ def allowed_mask_original(N, G, shifted, split=False):
     return M
 
 
-def dense_masked_attention(q, k, v, G, S, grad_do=None, split=False):
+def dense_masked_attention(q, k, v, G, S, grad_do=None, split=False, swap=False):
     """Dense N x N masked softmax attention in torch float64 (autograd for grads)."""
     B, N, H, d = q.shape
     Hkv = k.shape[2]
@@ -94,7 +100,7 @@ def dense_masked_attention(q, k, v, G, S, grad_do=None, split=False):
     tk = torch.tensor(k, dtype=torch.float64, requires_grad=True)
     tv = torch.tensor(v, dtype=torch.float64, requires_grad=True)
     masks = {False: torch.tensor(allowed_mask_original(N, G, False)),
-             True: torch.tensor(allowed_mask_original(N, G, True, split))}
+             True: torch.tensor(allowed_mask_original(N, G, True, split, swap))}
     outs, lses = [], []
     for h in range(H):
         shifted = h >= H - S
@@ -520,6 +526,124 @@ def pin_split_finite_differences(orc):
 
 
 # ---------------------------------------------------------------------------
+# Swap wrap option (Table 8, Variant 3): inside the wrap group the tokens from
+# the front of the sequence come before those from its end
+# ---------------------------------------------------------------------------
+
+def pin_swap_bruteforce(orc):
+    """Oracle with wrap="swap" against the dense mask: the main method's groups,
+    causal in original token order."""
+    for i, (B, N, H, Hkv, d, G, S) in enumerate(SMALL_CASES):
+        q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=180 + i)
+        o, lse = orc.forward(q, k, v, G, S, "swap")
+        dq, dk, dv = orc.backward(q, k, v, do, G, S, "swap")
+        o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(q, k, v, G, S, grad_do=do, swap=True)
+        _close(o, o_ref, 1e-12, f"swap brute-force O case {i}")
+        _close(lse, lse_ref, 1e-12, f"swap brute-force lse case {i}")
+        _close(dq, dq_ref, 1e-11, f"swap brute-force dQ case {i}")
+        _close(dk, dk_ref, 1e-11, f"swap brute-force dK case {i}")
+        _close(dv, dv_ref, 1e-11, f"swap brute-force dV case {i}")
+
+
+def pin_swap_gathered_sdpa(orc, cases=((1, 32, 4, 2, 4, 8, 2), (2, 24, 2, 1, 3, 12, 1), (1, 16, 2, 2, 4, 16, 2))):
+    """Every swap group gathered in token order, then torch's causal SDPA.
+
+    Token t of a head shifted by s = floor(G/2) belongs to group ((t - s) mod N)
+    // G (the main method's partition, last group short when G does not divide
+    N); the tokens of each group are taken in increasing index, attended with
+    is_causal=True and scattered back; autograd for the gradients; K/V repeated
+    for grouped queries.
+    """
+    for i, (B, N, H, Hkv, d, G, S) in enumerate(cases):
+        q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=190 + i)
+        o, lse = orc.forward(q, k, v, G, S, "swap")
+        dq, dk, dv = orc.backward(q, k, v, do, G, S, "swap")
+        r = H // Hkv
+        tq = torch.tensor(q, requires_grad=True)
+        tk = torch.tensor(k, requires_grad=True)
+        tv = torch.tensor(v, requires_grad=True)
+        kk = torch.repeat_interleave(tk, r, dim=2)
+        vv = torch.repeat_interleave(tv, r, dim=2)
+        heads = []
+        for h in range(H):
+            sh = G // 2 if h >= H - S else 0
+            gid = ((np.arange(N) - sh) % N) // G
+            out = [None] * N
+            for g in np.unique(gid):
+                toks = torch.tensor(np.nonzero(gid == g)[0])      # increasing token index
+                og = F.scaled_dot_product_attention(tq[:, toks, h][:, None], kk[:, toks, h][:, None],
+                                                    vv[:, toks, h][:, None], is_causal=True)[:, 0]
+                for n, t in enumerate(toks.tolist()):
+                    out[t] = og[:, n]
+            heads.append(torch.stack(out, dim=1))
+        ref = torch.stack(heads, dim=2)
+        (ref * torch.tensor(do)).sum().backward()
+        _close(o, ref.detach().numpy(), 1e-12, f"swap SDPA O case {i}")
+        _close(dq, tq.grad.numpy(), 1e-11, f"swap SDPA dQ case {i}")
+        _close(dk, tk.grad.numpy(), 1e-11, f"swap SDPA dK case {i}")
+        _close(dv, tv.grad.numpy(), 1e-11, f"swap SDPA dV case {i}")
+
+
+def pin_swap_agrees_with_roll_and_split(orc):
+    """Where the options coincide.
+
+    S = 0: identical to the main method.  S > 0: unshifted heads, and in shifted
+    heads every token outside the wrap group ([G/2, N - G/2)), equal the main
+    method; the first G/2 tokens see exactly what they see under the split
+    option (the tokens before them), so they equal split; the first token
+    attends to itself only (O = V, lse = scale q.k); the last G/2 tokens differ
+    from both (they now also see the first G/2).
+    """
+    B, N, H, Hkv, d, G = 1, 32, 4, 2, 4, 8
+    q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=200)
+    for S in (0, 2):
+        o_r, lse_r = orc.forward(q, k, v, G, S)
+        o_w, lse_w = orc.forward(q, k, v, G, S, "swap")
+        if S == 0:
+            assert np.array_equal(o_r, o_w) and np.array_equal(lse_r, lse_w), "swap changed an unshifted problem"
+            for a, b, n in zip(orc.backward(q, k, v, do, G, S), orc.backward(q, k, v, do, G, S, "swap"),
+                               ("dQ", "dK", "dV")):
+                assert np.array_equal(a, b), f"swap changed {n} of an unshifted problem"
+            continue
+        o_s, lse_s = orc.forward(q, k, v, G, S, "split")
+        h2, half = H - S, G // 2
+        _close(o_w[:, :, :h2], o_r[:, :, :h2], 1e-14, "swap: unshifted heads O")
+        _close(o_w[:, half:N - half], o_r[:, half:N - half], 1e-13, "swap: tokens outside the wrap group")
+        _close(o_w[:, :half, h2:], o_s[:, :half, h2:], 1e-13, "swap: front tokens equal split")
+        _close(lse_w[:, h2:, :half], lse_s[:, h2:, :half], 1e-13, "swap: front tokens lse equal split")
+        assert np.max(np.abs(o_w[:, N - half:, h2:] - o_r[:, N - half:, h2:])) > 1e-3, \
+            "swap did not change the end tokens"
+        assert np.max(np.abs(o_w[:, N - half:, h2:] - o_s[:, N - half:, h2:])) > 1e-3, \
+            "swap equals split on the end tokens"
+        r = H // Hkv
+        for h in range(h2, H):
+            _close(o_w[0, 0, h], v[0, 0, h // r], 1e-14, f"swap: first token O head {h}")
+            _close(lse_w[0, h, 0], np.dot(q[0, 0, h], k[0, 0, h // r]) / np.sqrt(d), 1e-14,
+                   f"swap: first token lse head {h}")
+
+
+def pin_swap_finite_differences(orc):
+    B, N, H, Hkv, d, G, S = 1, 16, 2, 1, 3, 8, 1
+    q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=210)
+    grads = orc.backward(q, k, v, do, G, S, "swap")
+    eps = 1e-6
+    for pos, name in enumerate(("dQ", "dK", "dV")):
+        x = (q, k, v)[pos]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args_p, args_m = [q, k, v], [q, k, v]
+            args_p[pos] = x.copy()
+            args_p[pos][idx] += eps
+            args_m[pos] = x.copy()
+            args_m[pos][idx] -= eps
+            lp = float(np.sum(orc.forward(*args_p, G, S, "swap")[0] * do))
+            lm = float(np.sum(orc.forward(*args_m, G, S, "swap")[0] * do))
+            num[idx] = (lp - lm) / (2 * eps)
+        err = np.linalg.norm(num - grads[pos]) / np.linalg.norm(num)
+        assert err <= 1e-6, f"swap finite differences {name}: rel {err:.2e}"
+
+
+# ---------------------------------------------------------------------------
 # One token's row (used for sampled checks of long groups)
 # ---------------------------------------------------------------------------
 
@@ -527,11 +651,10 @@ def pin_row_attention(orc, cases=SMALL_CASES[:4] + [(1, 16, 2, 1, 3, 16, 0)]):
     """row_attention of every token against the brute-force dense attention:
     o, lse and dq per row; dk and dv assembled from the rows' p and ds."""
     for i, (B, N, H, Hkv, d, G, S) in enumerate(cases):
-        for split in (False, True):
+        for wrap in ("roll", "split", "swap"):
             q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=150 + i)
-            o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(q, k, v, G, S, grad_do=do,
-                                                                              split=split)
-            wrap = "split" if split else "roll"
+            o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(
+                q, k, v, G, S, grad_do=do, split=wrap == "split", swap=wrap == "swap")
             dk = np.zeros_like(k)
             dv = np.zeros_like(v)
             r = H // Hkv
@@ -566,13 +689,12 @@ UNALIGNED_CASES = [   # (B, N, H, Hkv, d, G, S)
 
 def pin_unaligned_bruteforce(orc):
     for i, (B, N, H, Hkv, d, G, S) in enumerate(UNALIGNED_CASES):
-        for split in (False, True):
+        for wrap in ("roll", "split", "swap"):
             q, k, v, do = rand_problem(B, N, H, Hkv, d, seed=160 + i)
-            wrap = "split" if split else "roll"
             o, lse = orc.forward(q, k, v, G, S, wrap)
             dq, dk, dv = orc.backward(q, k, v, do, G, S, wrap)
-            o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(q, k, v, G, S, grad_do=do,
-                                                                              split=split)
+            o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = dense_masked_attention(
+                q, k, v, G, S, grad_do=do, split=wrap == "split", swap=wrap == "swap")
             _close(o, o_ref, 1e-12, f"unaligned brute-force O case {i} {wrap}")
             _close(lse, lse_ref, 1e-12, f"unaligned brute-force lse case {i} {wrap}")
             _close(dq, dq_ref, 1e-11, f"unaligned brute-force dQ case {i} {wrap}")
@@ -582,6 +704,10 @@ def pin_unaligned_bruteforce(orc):
 
 def pin_unaligned_row_attention(orc):
     pin_row_attention(orc, cases=[(1, 23, 3, 3, 4, 7, 2), (1, 26, 4, 2, 3, 6, 2)])
+
+
+def pin_unaligned_swap_gathered_sdpa(orc):
+    pin_swap_gathered_sdpa(orc, cases=UNALIGNED_CASES)
 
 
 def pin_unaligned_cut_sdpa(orc):
@@ -625,5 +751,7 @@ ALL_PINS = [
     pin_direction_reversal, pin_head_swap, pin_closed_forms, pin_finite_differences,
     pin_gqa_repeat, pin_worked_example_index_map, pin_worked_example_reach,
     pin_split_bruteforce, pin_split_segments_sdpa, pin_split_agrees_with_roll, pin_split_finite_differences,
+    pin_swap_bruteforce, pin_swap_gathered_sdpa, pin_swap_agrees_with_roll_and_split, pin_swap_finite_differences,
     pin_row_attention, pin_unaligned_bruteforce, pin_unaligned_cut_sdpa, pin_unaligned_row_attention,
+    pin_unaligned_swap_gathered_sdpa,
 ]

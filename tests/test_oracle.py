@@ -34,7 +34,7 @@ def test_oracle_rejects_undefined_problems(bad):
 def test_oracle_rejects_unknown_wrap():
     q = np.zeros((1, 16, 2, 4))
     with pytest.raises(ValueError):
-        orc.forward(q, q, q, 8, 1, "swap")
+        orc.forward(q, q, q, 8, 1, "rotate")
 
 
 def test_table11_attention_flops():
@@ -50,7 +50,7 @@ def test_table11_attention_flops():
         16 * flops.dense_fwd_attention_flops(2048, 2048, 128, 32, 32)
 
 
-@pytest.mark.parametrize("wrap", ["roll", "split"])
+@pytest.mark.parametrize("wrap", ["roll", "split", "swap"])
 @pytest.mark.parametrize("N,G,H,S", [(16, 8, 2, 1), (24, 8, 3, 2), (32, 32, 2, 0), (12, 4, 4, 4), (16, 16, 2, 2),
                                      (30, 8, 2, 1), (23, 7, 3, 2), (9, 1, 2, 1), (21, 7, 2, 1)])
 def test_pair_count_matches_bruteforce_mask(N, G, H, S, wrap):
@@ -59,7 +59,7 @@ def test_pair_count_matches_bruteforce_mask(N, G, H, S, wrap):
         pytest.skip("the split option is defined on whole groups only")
     total = 0
     for h in range(H):
-        total += int(pins.allowed_mask_original(N, G, h >= H - S, wrap == "split").sum())
+        total += int(pins.allowed_mask_original(N, G, h >= H - S, wrap == "split", wrap == "swap").sum())
     assert flops.allowed_pairs(1, H, N, G, S, wrap) == total
 
 

@@ -44,9 +44,20 @@ MUTATIONS = [
     ("lse-of-rolled-row", "lse[b, h, rows] = lseg", "lse[b, h, g * G:(g + 1) * G] = lseg", 0),
     ("split-ignored", 'if wrap == "split" and sigma:', 'if wrap == "none" and sigma:', 0),
     ("split-in-roll-mode", 'if wrap == "split" and sigma:', 'if sigma:', 0),
-    ("split-at-quarter", "cut = int(wraps[0]) + 1", "cut = (int(wraps[0]) + 1) // 2", 0),
-    ("split-every-group", "        if len(wraps):\n            cut = int(wraps[0]) + 1",
-     "        if True:\n            cut = len(rows) // 2", 0),
+    ("split-at-quarter", "return [slice(0, cut), slice(cut, len(rows))]",
+     "return [slice(0, cut // 2), slice(cut // 2, len(rows))]", 0),
+    ("split-every-group", "        cut = _wrap_cut(rows)\n        if cut is not None:\n            return [slice",
+     "        cut = len(rows) // 2\n        if cut is not None:\n            return [slice", 0),
+    ("wrap-cut-off-by-one", "return int(wraps[0]) + 1 if len(wraps) else None",
+     "return int(wraps[0]) if len(wraps) else None", 0),
+    ("swap-ignored", 'if wrap == "swap" and sigma:', 'if wrap == "none" and sigma:', 0),
+    ("swap-in-roll-mode", 'if wrap == "swap" and sigma:', 'if sigma:', 0),
+    ("swap-keeps-rolled-order", "return np.concatenate([rows[cut:], rows[:cut]])",
+     "return np.concatenate([rows[:cut], rows[cut:]])", 0),
+    ("swap-every-group", "        cut = _wrap_cut(rows)\n        if cut is not None:\n            return np.concatenate",
+     "        cut = len(rows) // 2\n        if cut is not None:\n            return np.concatenate", 0),
+    ("swap-front-reversed", "return np.concatenate([rows[cut:], rows[:cut]])",
+     "return np.concatenate([rows[cut:][::-1], rows[:cut]])", 0),
     ("row-drops-own-key", "keys = rows[part.start:pos + 1]", "keys = rows[part.start:pos]", 0),
     ("row-group-start", "keys = rows[part.start:pos + 1]", "keys = rows[0:pos + 1]", 0),
     ("row-drops-dvec", "ds = p * (dp - np.dot(dot, o))", "ds = p * dp", 0),
@@ -92,7 +103,8 @@ def test_direction_reversal_is_not_a_mistake():
     """
     mod = _mutant(*NEUTRAL)
     direction_sensitive = (pins.pin_worked_example_index_map, pins.pin_unaligned_bruteforce,
-                           pins.pin_unaligned_cut_sdpa, pins.pin_unaligned_row_attention)
+                           pins.pin_unaligned_cut_sdpa, pins.pin_unaligned_row_attention,
+                           pins.pin_unaligned_swap_gathered_sdpa)
     for pin in pins.ALL_PINS:
         if pin in direction_sensitive:
             with pytest.raises(AssertionError):
