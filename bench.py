@@ -138,8 +138,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama2-7b-32k")
-    ap.add_argument("--wrap", default="roll", choices=["roll", "split"],
-                    help="wrap handling of the shifted heads (split: Table 8's Variant 2)")
+    ap.add_argument("--wrap", default="roll", choices=["roll", "split", "swap"],
+                    help="wrap handling of the shifted heads (split, swap: Table 8's Variants 2, 3)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-reference", action="store_true")

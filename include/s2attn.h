@@ -44,8 +44,8 @@
  * address rows one by one near group ends); fp32, and bf16 batch slices of
  * 2 GiB or more, run generic kernels.  When a key/value head is shared by shifted and unshifted
  * query heads (H - shift_heads not a multiple of H / Hkv), and for the split
- * wrap option, the groups must be whole tiles (for the shared head, G a
- * multiple of 256).  Grids: B * H * ceil(N / G) * ceil(G / 128) < 2^31.
+ * and swap wrap options, the groups must be whole tiles (for the shared head,
+ * G a multiple of 256).  Grids: B * H * ceil(N / G) * ceil(G / 128) < 2^31.
  * B == 0 or N == 0 is an empty problem: every call validates the other sizes,
  * then returns S2ATTN_OK without reading any pointer or touching the GPU.
  */
@@ -69,7 +69,7 @@ typedef enum {
     S2ATTN_ERR_SHAPE = 2,        /* B or N < 0, H, Hkv, d or G <= 0, G > N (N > 0),
                                     shift_heads outside [0, H], H % Hkv != 0 */
     S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype or wrap option, the mixed-shift or
-                                    split rule above, or the grid size limit */
+                                    split / swap rule above, or the grid size limit */
     S2ATTN_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError) */
     S2ATTN_ERR_WORKSPACE = 5     /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
 } s2attn_status;
@@ -86,10 +86,18 @@ typedef enum {
  *                       so that last rolled group is cut at G/2 into two causal
  *                       groups, tokens [N-G/2, N) and tokens [0, G/2).  Every
  *                       other group, and every unshifted head, is unchanged.
+ *   S2ATTN_WRAP_SWAP  : Variant 3 of the same table (the shifted tokens swap
+ *                       places with the original front tokens), read as: that
+ *                       last rolled group keeps its tokens but takes tokens
+ *                       0..G/2-1 first and N-G/2..N-1 after them, so every
+ *                       group is causal in token order (the end tokens see the
+ *                       front ones, not the reverse).  Every other group, and
+ *                       every unshifted head, is unchanged.
  */
 typedef enum {
     S2ATTN_WRAP_ROLL = 0,
-    S2ATTN_WRAP_SPLIT = 1
+    S2ATTN_WRAP_SPLIT = 1,
+    S2ATTN_WRAP_SWAP = 2
 } s2attn_wrap;
 
 /*

@@ -20,7 +20,8 @@ S2ATTN_BF16 = 0
 S2ATTN_F32 = 1
 S2ATTN_WRAP_ROLL = 0
 S2ATTN_WRAP_SPLIT = 1
-WRAPS = {"roll": S2ATTN_WRAP_ROLL, "split": S2ATTN_WRAP_SPLIT}
+S2ATTN_WRAP_SWAP = 2
+WRAPS = {"roll": S2ATTN_WRAP_ROLL, "split": S2ATTN_WRAP_SPLIT, "swap": S2ATTN_WRAP_SWAP}
 
 EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes", "s2attn_bwd_prep", "s2attn_bwd_dkdv",
            "s2attn_bwd_dq", "s2attn_bwd_prep_dq", "s2attn_fwd_ex", "s2attn_bwd_ex", "s2attn_bwd_dkdv_ex",

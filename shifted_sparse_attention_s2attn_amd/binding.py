@@ -55,7 +55,8 @@ def _check_tensors(q, k, v, extra=()):
 
 
 def _wrap_code(wrap):
-    """Wrap handling of the shifted heads: "roll" (the method) or "split" (Table 8, Variant 2)."""
+    """Wrap handling of the shifted heads: "roll" (the method), "split" or "swap"
+    (Table 8, Variants 2 and 3)."""
     if wrap not in _lib.WRAPS:
         raise ValueError(f"wrap must be one of {sorted(_lib.WRAPS)}, got {wrap!r}")
     return _lib.WRAPS[wrap]
@@ -186,6 +187,7 @@ def s2attn(q, k, v, G, shift_heads=None, wrap="roll"):
     """Differentiable S2-Attn on [B, N, H, d] tensors (shift_heads defaults to H // 2).
 
     ``wrap="split"`` selects Variant 2 of Table 8: the tokens the roll carries
-    from the front of the sequence form their own group.
+    from the front of the sequence form their own group; ``wrap="swap"``
+    Variant 3: they stay in the last group but come before its end tokens.
     """
     return S2Attn.apply(q, k, v, G, q.shape[2] // 2 if shift_heads is None else shift_heads, wrap)

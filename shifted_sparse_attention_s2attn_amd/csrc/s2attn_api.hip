@@ -56,10 +56,12 @@ int check_problem(int B, int H, int Hkv, int N, int d, int G, int shift_heads, i
 
 bool empty_problem(int B, int N) { return B == 0 || N == 0; }
 
-// The split option cuts the last group at G/2; it needs aligned shapes.
+// The split option cuts the last group at G/2 and the swap option reorders
+// its halves; both need aligned shapes.
 int check_wrap(int wrap, int N, int G) {
   if (wrap == S2ATTN_WRAP_ROLL) return S2ATTN_OK;
-  if (wrap == S2ATTN_WRAP_SPLIT) return (N == 0 || aligned(N, G)) ? S2ATTN_OK : S2ATTN_ERR_UNSUPPORTED;
+  if (wrap == S2ATTN_WRAP_SPLIT || wrap == S2ATTN_WRAP_SWAP)
+    return (N == 0 || aligned(N, G)) ? S2ATTN_OK : S2ATTN_ERR_UNSUPPORTED;
   return S2ATTN_ERR_UNSUPPORTED;
 }
 
@@ -266,7 +268,7 @@ const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_OK: return "ok";
     case S2ATTN_ERR_NULL: return "a required pointer is NULL";
     case S2ATTN_ERR_SHAPE: return "invalid shape (a size < 0, H, Hkv, d or G <= 0, G > N, shift_heads outside [0,H], or H % Hkv != 0)";
-    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, or grid too large)";
+    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split, swap or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, or grid too large)";
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     default: return "unknown status";

@@ -104,7 +104,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
-    T* __restrict__ dk, T* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, int split,
+    T* __restrict__ dk, T* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, int wrap,
     float scale) {
   using S = DkdvShape<T, D>;
   constexpr int BKV = S::kBKV, BQ = S::kBQ, NQS = S::kNQS;
@@ -130,6 +130,8 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   const int r = H / Hkv;
   const int h0 = c * r;
   const int sig0 = (h0 >= H - shift_heads) ? G / 2 : 0;
+  const bool swap = wrap == kWrapSwap;
+  auto tok = [&](int j, int sig) { return swap ? token_of_row<true>(j, sig, N, G) : orig_row(j, sig, N); };
   const int ge0 = min(grp * G + G, N);          // end of the group (a last group may be short)
   const int j0 = grp * G + pos * BKV;           // first key row, rolled frame of head h0
   if (j0 >= ge0) return;                        // a tile past the end of a short group
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   // keys past the group compute on a copy of its last row and are not stored
   const int key_local = wave * 32 + l32;
   const bool k_ok = j0 + key_local < ge0;
-  const int tk = orig_row(k_ok ? j0 + key_local : ge0 - 1, sig0, N);
+  const int tk = tok(k_ok ? j0 + key_local : ge0 - 1, sig0);
   v8<T> kf[S::kDC], vf[S::kDC];
 #pragma unroll
   for (int cc = 0; cc < S::kDC; ++cc) {
@@ -162,10 +164,9 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   for (int hh = 0; hh < r; ++hh) {
     const int h = h0 + hh;
     const int sig = (h >= H - shift_heads) ? G / 2 : 0;
-    int jk0 = j0 + sig0 - sig;                  // same key rows in head h's rolled frame
-    if (jk0 < 0) jk0 += N;
-    if (jk0 >= N) jk0 -= N;
-    const bool split_head = split && sig != 0;
+    // same key rows in head h's rolled frame
+    const int jk0 = swap ? frame_row<true>(j0, sig0, sig, N, G) : frame_row<false>(j0, sig0, sig, N, G);
+    const bool split_head = wrap == kWrapSplit && sig != 0;
     // query tiles meeting the workgroup's keys, and the end of this wave's queries
     // (queries from the next group in the last tile are masked)
     const int q_end_g = query_end_row(jk0, G, N, false);
@@ -183,12 +184,12 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     auto load_q = [&](int jq0) {
 #pragma unroll
       for (int i = 0; i < QRPT; ++i) {
-        const int t = orig_row(min(jq0 + q_qg * QRPT + i, N - 1), sig, N);   // rows past N are masked
+        const int t = tok(min(jq0 + q_qg * QRPT + i, N - 1), sig);   // rows past N are masked
         qr[i] = *reinterpret_cast<const v8<T>*>(qb + (size_t)t * qstride + q_dc * 8);
         dr[i] = *reinterpret_cast<const v8<T>*>(dob + (size_t)t * qstride + q_dc * 8);
       }
       if (tid < BQ) {
-        const int t = orig_row(min(jq0 + tid, N - 1), sig, N);
+        const int t = tok(min(jq0 + tid, N - 1), sig);
         lse_r = lse_h[t];
         dvec_r = dvec_h[t];
       }
@@ -288,7 +289,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void s2attn_bwd_dq(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ dvec, T* __restrict__ dq,
-    int N, int H, int Hkv, int G, int shift_heads, int split, float scale) {
+    int N, int H, int Hkv, int G, int shift_heads, int wrap, float scale) {
   using S = DqShape<T, D>;
   constexpr int BR = S::kBR, BC = S::kBC, KCPR = S::kKCPR, TCPR = S::kTCPR, KRPT = S::kKRowsPerThread;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -308,7 +309,9 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   const int h = (to.pair / groups) % H, b = to.pair / (groups * H);
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
-  const bool split_head = split && sigma != 0;
+  const bool split_head = wrap == kWrapSplit && sigma != 0;
+  const bool swap_head = wrap == kWrapSwap && sigma != 0;
+  auto tok = [&](int j) { return swap_head ? token_of_row<true>(j, sigma, N, G) : orig_row(j, sigma, N); };
   const int ge = min(grp * G + G, N);           // end of the group (a last group may be short)
   const int j0 = grp * G + pos * BR;
   if (j0 >= ge) return;                         // a tile past the end of a short group
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
   const bool q_ok = jq < ge;
-  const int tq = orig_row(q_ok ? jq : ge - 1, sigma, N);
+  const int tq = tok(q_ok ? jq : ge - 1);
   const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
   v8<T> qf[S::kDC], dof[S::kDC];
   {
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   auto load_tile = [&](int kt0) {
 #pragma unroll
     for (int i = 0; i < KRPT; ++i) {
-      const int t = orig_row(min(kt0 + k_kg * KRPT + i, N - 1), sigma, N);   // rows past N are masked keys
+      const int t = tok(min(kt0 + k_kg * KRPT + i, N - 1));   // rows past N are masked keys
       kr[i] = *reinterpret_cast<const v8<T>*>(kb + (size_t)t * kvstride + k_dc * 8);
       vr[i] = *reinterpret_cast<const v8<T>*>(vb + (size_t)t * kvstride + k_dc * 8);
     }
@@ -482,9 +485,10 @@ __device__ __forceinline__ f32x4 lds_f32x4(const char* base, int off) {
 // SPLIT: the split wrap option; EDGE: groups that are not whole tiles (query
 // rows of the next group are masked, tiles that cross the wrap point or the
 // end of the sequence take per-row addresses, keys past the group are not
-// stored).  Each is compiled separately, so that the main method's step loop
-// carries no trace of either.
-template <int D, bool SPLIT, bool EDGE>
+// stored); SWAP: the swap wrap option's row map (token_of_row).  Each is
+// compiled separately, so that the main method's step loop carries no trace
+// of any of them.
+template <int D, bool SPLIT, bool EDGE, bool SWAP>
 __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const int cb = (wave + S::kWaves * i) * 64;
     const int p = cb + lane;
     const int row = p / CPR, pc = p % CPR;
-    const size_t g = (size_t)orig_row(EDGE ? min(j0 + row, N - 1) : j0 + row, sig0, N) * kvstride +
+    const size_t g = (size_t)token_of_row<SWAP>(EDGE ? min(j0 + row, N - 1) : j0 + row, sig0, N, G) * kvstride +
                      (pc ^ swz2<CPR>(row)) * 8;
     load_lds16(kb + g, lds + S::kK + cb * 16);
     load_lds16(vb + g, lds + S::kV + cb * 16);
@@ -578,9 +582,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   int fr_jk0[2], fr_qb[2], fr_qe[2], fr_wqe[2], fr_qge[2];
 #pragma unroll
   for (int sh = 0; sh < 2; ++sh) {
-    int jk = j0 + sig0 - sh * (G / 2);
-    if (jk < 0) jk += N;
-    if (jk >= N) jk -= N;
+    const int jk = frame_row<SWAP>(j0, sig0, sh * (G / 2), N, G);
     const bool split_head = SPLIT && sh;
     const int qge = query_end_row(jk, G, N, false);
     fr_jk0[sh] = jk;
@@ -611,18 +613,18 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
       for (int i = 0; i < S::kQLoads; ++i) {
         const int p = (wave + S::kWaves * i) * 64 + lane;
         const int row = p / CPR, pc = p % CPR;
-        const int tok = orig_row(min(qt * BQ + row, N - 1), sig, N);
+        const int tok = token_of_row<SWAP>(min(qt * BQ + row, N - 1), sig, N, G);
         const int off = (tok * (int)qstride + h * D + (pc ^ swz2<CPR>(row)) * 8) * 2;
         const int cb = (wave + S::kWaves * i) * 64 * 16;
         buffer_load_lds16(qrs, off, 0, lds + S::kQ + stage * S::kQTileB + cb);
         buffer_load_lds16(dors, off, 0, lds + S::kdO + stage * S::kQTileB + cb);
       }
-      const int loff = (h * N + orig_row(min(qt * BQ + lane, N - 1), sig, N)) * 4;
+      const int loff = (h * N + token_of_row<SWAP>(min(qt * BQ + lane, N - 1), sig, N, G)) * 4;
       if (wave == 0) buffer_load_lds4(lrs, loff, 0, lds + S::kF + stage * 2 * BQ * 4);
       if (wave == 1) buffer_load_lds4(drs, loff, 0, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
       return;
     }
-    const int t0 = orig_row(qt * BQ, sig, N);         // a 64-row tile is contiguous
+    const int t0 = token_of_row<SWAP>(qt * BQ, sig, N, G);   // a 64-row tile is contiguous
     const int soff = (t0 * (int)qstride + h * D) * 2;
 #pragma unroll
     for (int i = 0; i < S::kQLoads; ++i) {
@@ -749,7 +751,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
         dvacc[dt][i] += xs[((1 * S::kDT + dt) * 16 + i) * 64 + lane];
       }
     if (EDGE && j0 + key_row >= ge0) return;          // a key of the next group
-    const int tk = orig_row(j0 + key_row, sig0, N);
+    const int tk = token_of_row<SWAP>(j0 + key_row, sig0, N, G);
     bf16* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
     bf16* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
 #pragma unroll
@@ -784,7 +786,7 @@ struct DqB16Shape {
   static constexpr int kDT = D / 32;
 };
 
-template <int D, bool PREP, bool EDGE>
+template <int D, bool PREP, bool EDGE, bool SWAP>
 __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const bf16* __restrict__ o, const float* __restrict__ lse,
@@ -826,7 +828,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
   const bool q_ok = !EDGE || jq < ge;                // EDGE: rows past the group read its last row
-  const int tq = orig_row(q_ok ? jq : ge - 1, sigma, N);
+  const int tq = token_of_row<SWAP>(q_ok ? jq : ge - 1, sigma, N, G);
   const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
   bf16x8 qf[S::kDC], dof[S::kDC];
   {
@@ -883,7 +885,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
       for (int i = 0; i < S::kLoads; ++i) {
         const int p = (wave + S::kWaves * i) * 64 + lane;
         const int row = p / CPR, pc = p % CPR;
-        const int tok = orig_row(min(kt0 + row, N - 1), sigma, N);
+        const int tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, G);
         const int cb = (wave + S::kWaves * i) * 64 * 16;
         const int off = (tok * (int)kvstride + (pc ^ swz2<CPR>(row)) * 8) * 2;
         buffer_load_lds16(krs, off, 0, kd + cb);
@@ -891,7 +893,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
       }
       return;
     }
-    const int t0 = orig_row(kt0, sigma, N) * (int)kvstride * 2;   // whole tile is contiguous
+    const int t0 = token_of_row<SWAP>(kt0, sigma, N, G) * (int)kvstride * 2;   // whole tile is contiguous
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
@@ -1017,22 +1019,24 @@ hipError_t launch_bwd_prep(const void* o, const void* dO, const float* lse, floa
 template <int D>
 hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                             const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                            int shift_heads, int split, float scale, hipStream_t stream) {
+                            int shift_heads, int wrap, float scale, hipStream_t stream) {
   using S = DkdvB16Shape<D>;
   constexpr int BKV = S::kBKV;
-  const bool whole = N % G == 0 && G % BKV == 0;     // the split option implies whole tiles
+  const bool whole = N % G == 0 && G % BKV == 0;     // the split and swap options imply whole tiles
   const dim3 grid(whole ? B * Hkv * (N / BKV) : B * Hkv * ((N + G - 1) / G) * ((G + BKV - 1) / BKV));
   const dim3 block(S::kThreads);
-#define S2A_DKDV_LAUNCH(SPLIT, EDGE)                                                                           \
-  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, SPLIT, EDGE>), grid, block, 0, stream, (const bf16*)q,           \
+#define S2A_DKDV_LAUNCH(SPLIT, EDGE, SWAP)                                                                     \
+  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, SPLIT, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,     \
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk, (bf16*)dv, N, H, Hkv, \
                      G, shift_heads, scale)
-  if (split)
-    S2A_DKDV_LAUNCH(true, false);
+  if (wrap == kWrapSplit)
+    S2A_DKDV_LAUNCH(true, false, false);
+  else if (wrap == kWrapSwap)
+    S2A_DKDV_LAUNCH(false, false, true);   // the swap option implies whole tiles too
   else if (whole)
-    S2A_DKDV_LAUNCH(false, false);
+    S2A_DKDV_LAUNCH(false, false, false);
   else
-    S2A_DKDV_LAUNCH(false, true);
+    S2A_DKDV_LAUNCH(false, true, false);
 #undef S2A_DKDV_LAUNCH
   return hipGetLastError();
 }
@@ -1040,7 +1044,7 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
 template <typename T, int D>
 hipError_t launch_dkdv_generic(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                                const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                               int shift_heads, int split, float scale, hipStream_t stream) {
+                               int shift_heads, int wrap, float scale, hipStream_t stream) {
   using S = DkdvShape<T, D>;
   static bool attr = false;
   hipError_t e = raise_lds_limit(&s2attn_bwd_dkdv<T, D>, S::kLdsBytes, attr);
@@ -1048,41 +1052,47 @@ hipError_t launch_dkdv_generic(const void* q, const void* k, const void* v, cons
   const dim3 grid(B * Hkv * ((N + G - 1) / G) * ((G + S::kBKV - 1) / S::kBKV));
   hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), grid, dim3(S::kThreads), S::kLdsBytes,
                      stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dk, (T*)dv, N,
-                     H, Hkv, G, shift_heads, split, scale);
+                     H, Hkv, G, shift_heads, wrap, scale);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                            const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                           int shift_heads, int split, hipStream_t stream) {
+                           int shift_heads, int wrap, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
     // the fast kernel addresses one batch's Q / dO with 31-bit byte offsets
     if ((size_t)N * H * D * sizeof(T) < (size_t(1) << 31))
-      return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, split, scale, stream);
+      return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
   }
-  return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, split, scale, stream);
+  return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
 }
 
 // o and lse non-NULL: prep fused in (writes lse2 and dvec); else reads them.
 template <int D>
 hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO, const void* o,
                           const float* lse, float* lse2, float* dvec, void* dq, int B, int H, int Hkv, int N, int G,
-                          int shift_heads, int split, float scale, hipStream_t stream) {
+                          int shift_heads, int wrap, float scale, hipStream_t stream) {
   using S = DqB16Shape<D>;
   constexpr int BR = S::kBR;
   const bool whole = N % G == 0 && G % BR == 0;
   const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR)), block(S::kThreads);
   const bf16* ob = (const bf16*)o;
-#define S2A_DQ_LAUNCH(PREP, EDGE)                                                                             \
-  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, PREP, EDGE>), grid, block, 0, stream, (const bf16*)q,           \
+#define S2A_DQ_LAUNCH(PREP, EDGE, SWAP)                                                                       \
+  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, PREP, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,     \
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec, (bf16*)dq, N, H, Hkv, \
-                     G, shift_heads, split, scale)
-  if (o) {
-    if (whole) S2A_DQ_LAUNCH(true, false); else S2A_DQ_LAUNCH(true, true);
+                     G, shift_heads, (int)(wrap == kWrapSplit), scale)
+  if (wrap == kWrapSwap) {
+    if (o) {
+      if (whole) S2A_DQ_LAUNCH(true, false, true); else S2A_DQ_LAUNCH(true, true, true);
+    } else {
+      if (whole) S2A_DQ_LAUNCH(false, false, true); else S2A_DQ_LAUNCH(false, true, true);
+    }
+  } else if (o) {
+    if (whole) S2A_DQ_LAUNCH(true, false, false); else S2A_DQ_LAUNCH(true, true, false);
   } else {
-    if (whole) S2A_DQ_LAUNCH(false, false); else S2A_DQ_LAUNCH(false, true);
+    if (whole) S2A_DQ_LAUNCH(false, false, false); else S2A_DQ_LAUNCH(false, true, false);
   }
 #undef S2A_DQ_LAUNCH
   return hipGetLastError();
@@ -1091,7 +1101,7 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
 template <typename T, int D>
 hipError_t launch_dq_generic(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                              const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
-                             int split, float scale, hipStream_t stream) {
+                             int wrap, float scale, hipStream_t stream) {
   using S = DqShape<T, D>;
   static bool attr = false;
   hipError_t e = raise_lds_limit(&s2attn_bwd_dq<T, D>, S::kLdsBytes, attr);
@@ -1099,7 +1109,7 @@ hipError_t launch_dq_generic(const void* q, const void* k, const void* v, const 
   const dim3 grid(B * H * ((N + G - 1) / G) * ((G + S::kBR - 1) / S::kBR));
   hipLaunchKernelGGL((s2attn_bwd_dq<T, D>), grid, dim3(S::kThreads), S::kLdsBytes, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dq, N, H, Hkv, G,
-                     shift_heads, split, scale);
+                     shift_heads, wrap, scale);
   return hipGetLastError();
 }
 
@@ -1113,29 +1123,29 @@ bool dq_fast(int N, int Hkv, int G) {
 template <typename T, int D>
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                          const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
-                         int split, hipStream_t stream) {
+                         int wrap, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
     if (dq_fast<T, D>(N, Hkv, G))
       return launch_dq_bf16<D>(q, k, v, dO, nullptr, nullptr, const_cast<float*>(lse2), const_cast<float*>(dvec),
-                               dq, B, H, Hkv, N, G, shift_heads, split, scale, stream);
+                               dq, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
   }
-  return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split, scale, stream);
+  return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
 }
 
 // prep and dq in one launch where the fast dq kernel runs, else one after the other
 template <typename T, int D>
 hipError_t launch_bwd_prep_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
                               const void* dO, float* lse2, float* dvec, void* dq, int B, int H, int Hkv, int N,
-                              int G, int shift_heads, int split, hipStream_t stream) {
+                              int G, int shift_heads, int wrap, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
     if (dq_fast<T, D>(N, Hkv, G))
-      return launch_dq_bf16<D>(q, k, v, dO, o, lse, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split,
+      return launch_dq_bf16<D>(q, k, v, dO, o, lse, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap,
                                1.0f / sqrtf((float)D), stream);
   }
   const hipError_t e = launch_bwd_prep<T, D>(o, dO, lse, dvec, lse2, B, H, N, stream);
   if (e != hipSuccess) return e;
-  return launch_bwd_dq<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, split, stream);
+  return launch_bwd_dq<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap, stream);
 }
 
 #define S2A_INST_BWD(T, D)                                                                                 \

@@ -122,6 +122,43 @@ __device__ __forceinline__ int query_end_row(int j, int G, int N, bool split_hea
   return (split_head && gs == N - G && j - gs < G / 2) ? gs + G / 2 : min(gs + G, N);
 }
 
+// Wrap options as the kernels take them (the values of s2attn_wrap).
+constexpr int kWrapRoll = 0, kWrapSplit = 1, kWrapSwap = 2;
+
+// Swap wrap option (Table 8 / Figure 6, Variant 3): in a shifted head the last
+// rolled group (rows N-G .. N-1) keeps its tokens, but the G/2 tokens the roll
+// carried from the front of the sequence come first, so that causal order in
+// that group is token order: rows N-G .. N-G/2-1 hold tokens 0 .. G/2-1 and
+// rows N-G/2 .. N-1 hold tokens N-G/2 .. N-1.  Whole groups only (G divides N,
+// G/2 a multiple of 64, so no 64-row tile straddles a break of the map).
+// Token held at rolled row j of a head rolled by sigma:
+template <bool SWAP>
+__device__ __forceinline__ int token_of_row(int j, int sigma, int N, int G) {
+  if (SWAP && sigma != 0 && j >= N - G) return j < N - G / 2 ? j - (N - G) : j;
+  return orig_row(j, sigma, N);
+}
+// ... and its inverse, the row of token t:
+template <bool SWAP>
+__device__ __forceinline__ int row_of_token(int t, int sigma, int N, int G) {
+  if (SWAP && sigma != 0) {
+    if (t < G / 2) return N - G + t;
+    if (t >= N - G / 2) return t;
+  }
+  const int j = t - sigma;
+  return j < 0 ? j + N : j;
+}
+
+// The row that rolled row j of a head rolled by sig_from has in the frame of a
+// head rolled by sig_to (the same token).
+template <bool SWAP>
+__device__ __forceinline__ int frame_row(int j, int sig_from, int sig_to, int N, int G) {
+  if (SWAP) return row_of_token<true>(token_of_row<true>(j, sig_from, N, G), sig_to, N, G);
+  int r = j + sig_from - sig_to;
+  if (r < 0) r += N;
+  if (r >= N) r -= N;
+  return r;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));

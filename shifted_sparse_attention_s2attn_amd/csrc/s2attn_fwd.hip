@@ -7,8 +7,10 @@
 // independent causal attention over G tokens; heads h >= H - shift_heads read
 // their tokens rolled by G/2, so rolled row j is original token (j + G/2) mod N,
 // and write their outputs back at the original rows (the roll-back).
-// With `split` (Table 8 / Figure 6, Variant 2) the shifted heads' last rolled
-// group is cut at G/2: its second-half queries start at key G/2 of the group.
+// Wrap options of the shifted heads' last rolled group (Table 8 / Figure 6):
+// split (Variant 2) cuts it at G/2, so its second-half queries start at key G/2
+// of the group; swap (Variant 3) puts the tokens carried from the front first
+// (a different row -> token map for that group, token_of_row).
 //
 // One workgroup = 4 waves = 128 consecutive query rows (rolled frame) of one
 // (batch, head).  Each wave owns 32 query rows; its Q operand stays in
@@ -52,7 +54,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     T* __restrict__ o, float* __restrict__ lse,
-    int N, int H, int Hkv, int G, int shift_heads, int split, float scale) {
+    int N, int H, int Hkv, int G, int shift_heads, int wrap, float scale) {
   using S = FwdShape<T, D>;
   constexpr int BR = S::kBR, BC = S::kBC, KCPR = S::kKCPR, VCPR = S::kVCPR;
   constexpr int KPT = S::kKChunksPerThread, VKPT = S::kVKeysPerThread;
@@ -72,7 +74,9 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
 
-  const bool split_head = split && sigma != 0;
+  const bool split_head = wrap == kWrapSplit && sigma != 0;
+  const bool swap_head = wrap == kWrapSwap && sigma != 0;
+  auto tok = [&](int j) { return swap_head ? token_of_row<true>(j, sigma, N, G) : orig_row(j, sigma, N); };
   const int ge = min(grp * G + G, N);           // end of the group (a last group may be short)
   const int j0 = grp * G + pos * BR;            // first query row (rolled)
   if (j0 >= ge) return;                         // a tile past the end of a short group
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
   const int jw = j0 + wave * 32;                // wave's first query (rolled)
   const int jq = jw + l32;                      // this lane's query (rolled)
   const bool q_ok = jq < ge;                    // rows past the group compute on a copy, are not stored
-  const int tq = orig_row(q_ok ? jq : ge - 1, sigma, N);
+  const int tq = tok(q_ok ? jq : ge - 1);
   const int kw0 = first_key_row(jw, G, N, split_head);        // ... and this wave's first key
   v8<T> qf[S::kDC];
 #pragma unroll
@@ -106,12 +110,12 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
     for (int i = 0; i < KPT; ++i) {
       const int ci = tid + i * 256;
       const int row = ci / KCPR, cc = ci % KCPR;
-      const int t = orig_row(min(kt0 + row, N - 1), sigma, N);   // rows past N are masked keys
+      const int t = tok(min(kt0 + row, N - 1));   // rows past N are masked keys
       kreg[i] = *reinterpret_cast<const v8<T>*>(kb + (size_t)t * kvstride + cc * 8);
     }
 #pragma unroll
     for (int i = 0; i < VKPT; ++i) {
-      const int t = orig_row(min(kt0 + v_kg * VKPT + i, N - 1), sigma, N);
+      const int t = tok(min(kt0 + v_kg * VKPT + i, N - 1));
       vreg[i] = *reinterpret_cast<const v8<T>*>(vb + (size_t)t * kvstride + v_dc * 8);
     }
   };
@@ -267,7 +271,9 @@ __device__ __forceinline__ int swz_v(int row) {
 // key rows past it follow every query of the group and are masked, and a key
 // tile that crosses the roll's wrap point (or the end of the sequence) is
 // loaded with per-row addresses.  Compiled separately from the whole-tile case.
-template <int D, bool EDGE>
+// SWAP: the swap wrap option's row map (token_of_row); `split` is 1 for the
+// split option.
+template <int D, bool EDGE, bool SWAP>
 __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse,
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
   const bool q_ok = !EDGE || jq < ge;
-  const int tq = orig_row(q_ok ? jq : ge - 1, sigma, N);
+  const int tq = token_of_row<SWAP>(q_ok ? jq : ge - 1, sigma, N, G);
   const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
   bf16x8 qf[S::kDC];
   {
@@ -342,14 +348,14 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
       for (int i = 0; i < S::kLoads; ++i) {
         const int p = (wave + S::kWaves * i) * 64 + lane;
         const int row = p / CPR, pc = p % CPR;
-        const int tok = orig_row(min(kt0 + row, N - 1), sigma, N);
+        const int tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, G);
         const int cb = (wave + S::kWaves * i) * 64 * 16;
         buffer_load_lds16(krs, (tok * (int)kvstride + (pc ^ swz_k<CPR>(row)) * 8) * 2, 0, kd + cb);
         buffer_load_lds16(vrs, (tok * (int)kvstride + (pc ^ swz_v<CPR>(row)) * 8) * 2, 0, vd + cb);
       }
       return;
     }
-    const int t0 = orig_row(kt0, sigma, N) * (int)kvstride * 2;   // whole tile is contiguous
+    const int t0 = token_of_row<SWAP>(kt0, sigma, N, G) * (int)kvstride * 2;   // whole tile is contiguous
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
@@ -479,34 +485,40 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
 
 template <int D>
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int H, int Hkv, int N, int G, int shift_heads, int split, float scale,
+                           int B, int H, int Hkv, int N, int G, int shift_heads, int wrap, float scale,
                            hipStream_t stream) {
   constexpr int BR = FwdB16Shape<D>::kBR;
   const dim3 block(FwdB16Shape<D>::kThreads);
-  if (N % G == 0 && G % BR == 0)
-    hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, false>), dim3(B * H * (N / BR)), block, 0, stream,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads,
-                       split, scale);
-  else
-    hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, true>), dim3(B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR)),
-                       block, 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv,
-                       G, shift_heads, split, scale);
+  const bool whole = N % G == 0 && G % BR == 0;
+  const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
+#define S2A_FWD_LAUNCH(EDGE, SWAP)                                                                              \
+  hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,          \
+                     (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads,                \
+                     (int)(wrap == kWrapSplit), scale)
+  if (wrap == kWrapSwap) {
+    if (whole) S2A_FWD_LAUNCH(false, true);
+    else S2A_FWD_LAUNCH(true, true);
+  } else {
+    if (whole) S2A_FWD_LAUNCH(false, false);
+    else S2A_FWD_LAUNCH(true, false);
+  }
+#undef S2A_FWD_LAUNCH
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int H, int Hkv, int N, int G, int shift_heads, int split, hipStream_t stream) {
+                      int B, int H, int Hkv, int N, int G, int shift_heads, int wrap, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
     // the fast kernel addresses one batch's K / V with 31-bit byte offsets
     if ((size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
-      return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, split, scale, stream);
+      return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
   }
   constexpr int BR = FwdShape<T, D>::kBR;
   dim3 grid(B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
   hipLaunchKernelGGL((s2attn_fwd_kernel<T, D>), grid, dim3(256), 0, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, split, scale);
+                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, wrap, scale);
   return hipGetLastError();
 }
 

@@ -112,13 +112,14 @@ def test_unaligned_group_sizes_pass_validation(lib):
 
 
 def test_wrap_option_validation(lib):
-    """The _ex calls take wrap in {ROLL, SPLIT}; anything else is unsupported,
-    checked after the sizes and before the pointers."""
+    """The _ex calls take wrap in {ROLL, SPLIT, SWAP}; anything else is
+    unsupported, checked after the sizes and before the pointers."""
     p = dict(GOOD)
     dims = [p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"]]
     need = lib.s2attn_bwd_workspace_bytes(*dims, 0)
-    for wrap, code in ((2, _lib.S2ATTN_ERR_UNSUPPORTED), (-1, _lib.S2ATTN_ERR_UNSUPPORTED),
-                       (_lib.S2ATTN_WRAP_SPLIT, _lib.S2ATTN_ERR_NULL), (_lib.S2ATTN_WRAP_ROLL, _lib.S2ATTN_ERR_NULL)):
+    for wrap, code in ((3, _lib.S2ATTN_ERR_UNSUPPORTED), (-1, _lib.S2ATTN_ERR_UNSUPPORTED),
+                       (_lib.S2ATTN_WRAP_SPLIT, _lib.S2ATTN_ERR_NULL), (_lib.S2ATTN_WRAP_SWAP, _lib.S2ATTN_ERR_NULL),
+                       (_lib.S2ATTN_WRAP_ROLL, _lib.S2ATTN_ERR_NULL)):
         assert lib.s2attn_fwd_ex(None, None, None, None, None, *dims, wrap, 0, None) == code
         assert lib.s2attn_bwd_ex(*([None] * 10), need, *dims, wrap, 0, None) == code
         assert lib.s2attn_bwd_dkdv_ex(*([None] * 7), need, *dims, wrap, 0, None) == code
@@ -127,9 +128,11 @@ def test_wrap_option_validation(lib):
     bad[3] = 64                                          # shape errors come first (G > N)
     assert lib.s2attn_fwd_ex(None, None, None, None, None, *bad, 7, 0, None) == _lib.S2ATTN_ERR_SHAPE
     unaligned = list(dims)
-    unaligned[3] = 500                                   # split needs whole groups of whole tiles
-    assert lib.s2attn_fwd_ex(None, None, None, None, None, *unaligned, _lib.S2ATTN_WRAP_SPLIT, 0, None) == \
-        _lib.S2ATTN_ERR_UNSUPPORTED
+    unaligned[3] = 500                                   # split and swap need whole groups of whole tiles
+    for wrap in (_lib.S2ATTN_WRAP_SPLIT, _lib.S2ATTN_WRAP_SWAP):
+        assert lib.s2attn_fwd_ex(None, None, None, None, None, *unaligned, wrap, 0, None) == \
+            _lib.S2ATTN_ERR_UNSUPPORTED
+        assert lib.s2attn_bwd_ex(*([None] * 10), need, *unaligned, wrap, 0, None) == _lib.S2ATTN_ERR_UNSUPPORTED
     assert lib.s2attn_fwd_ex(None, None, None, None, None, *unaligned, _lib.S2ATTN_WRAP_ROLL, 0, None) == \
         _lib.S2ATTN_ERR_NULL
     empty = list(dims)

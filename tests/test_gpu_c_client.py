@@ -19,11 +19,12 @@ from shifted_sparse_attention_s2attn_amd.inputs import make_inputs, small_worklo
 pytestmark = pytest.mark.gpu
 
 CLIENT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_bin", "c_abi_client")
-WRAP_CODE = {"roll": 0, "split": 1}
+WRAP_CODE = {"roll": 0, "split": 1, "swap": 2}
 
 CASES = [
     (small_workload("c-gqa2-roll", B=2, H=4, Hkv=2, d=128, N=1024, G=256, shift_heads=2), "roll"),
     (small_workload("c-gqa2-split", B=1, H=4, Hkv=2, d=64, N=1024, G=512, shift_heads=2), "split"),
+    (small_workload("c-gqa2-swap", B=1, H=4, Hkv=2, d=128, N=1024, G=256, shift_heads=2), "swap"),
     (small_workload("c-short-last-group", B=1, H=4, Hkv=2, d=128, N=1000, G=300, shift_heads=2), "roll"),
 ]
 

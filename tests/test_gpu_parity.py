@@ -108,6 +108,16 @@ def test_small_parity_split(w):
     check_full(w, inp, out, wrap="split")
 
 
+# the swap option (Table 8, Variant 3) on the same shapes: its row map breaks at
+# N - G and N - G/2, tile boundaries of every kernel for these G
+@pytest.mark.parametrize("w", SPLIT, ids=[w.name for w in SPLIT])
+def test_small_parity_swap(w):
+    say(f"case {w} wrap=swap")
+    inp = make_inputs(w, seed=8)
+    out = run_gpu(w, to_gpu(inp), wrap="swap")
+    check_full(w, inp, out, wrap="swap")
+
+
 # group sizes that do not divide the sequence, or are not whole 128-row tiles
 # (EDGE instantiations of the bf16 kernels, generic kernels for fp32): the last
 # group is short, the shift floor(G/2)
@@ -131,10 +141,10 @@ def test_small_parity_unaligned(w):
 
 def random_cases(n=24, seed=2024):
     """Seeded random small problems over every option the ABI accepts: d, dtype,
-    B, GQA ratio, shifted-head count, aligned and unaligned G, both wrap modes.
-    Combinations the ABI rejects (split or a mixed-shift KV head on groups that
-    are not whole 128-row tiles, G/2 not whole tiles for a mixed KV head) are
-    redrawn."""
+    B, GQA ratio, shifted-head count, aligned and unaligned G, every wrap mode.
+    Combinations the ABI rejects (split, swap or a mixed-shift KV head on groups
+    that are not whole 128-row tiles, G/2 not whole tiles for a mixed KV head)
+    are redrawn."""
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
@@ -151,8 +161,8 @@ def random_cases(n=24, seed=2024):
             continue
         B = int(rng.choice([1, 2]))
         aligned = N % G == 0 and G % 128 == 0
-        wrap = str(rng.choice(["roll", "split"]))
-        if wrap == "split" and not aligned:
+        wrap = str(rng.choice(["roll", "split", "swap"]))
+        if wrap != "roll" and not aligned:
             continue
         if r > 1 and (H - S) % r != 0 and not (aligned and (G // 2) % 128 == 0):
             continue
@@ -310,6 +320,23 @@ def test_full_size_split():
         check_sampled(w, t, out, c, g0, wrap="split")
 
 
+def test_full_size_swap():
+    """The swap option at the 7B-32k size: the wrap group of a shifted head
+    (tokens 0..G/2-1 first, then N-G/2..N-1) and a plain group."""
+    w = WORKLOADS["llama2-7b-32k"]
+    say(f"case {w} wrap=swap (generating inputs on the GPU)")
+    t = make_inputs(w, seed=0, device="cuda")
+    out = run_gpu(w, t, wrap="swap")
+    say("  kernels done")
+    for name, x in zip(("o", "lse", "dq", "dk", "dv"), out):
+        assert bool(torch.isfinite(x).all()), f"non-finite values in {name}"
+    # token 0 now opens the wrap group of a shifted head: it attends to itself only
+    h = w.H - 1
+    assert torch.equal(out[0][:, 0, h], t["v"][:, 0, h // (w.H // w.Hkv)])
+    for c, g0 in [(31, 3), (0, 3)]:
+        check_sampled(w, t, out, c, g0, wrap="swap")
+
+
 def test_full_size_full_attention():
     """G = N = 102400, no shift: full causal attention at the 7B 100k shape.
 
@@ -369,7 +396,7 @@ def test_repeatability():
         assert torch.equal(a[i], b[i])
 
 
-@pytest.mark.parametrize("wrap", ["roll", "split"])
+@pytest.mark.parametrize("wrap", ["roll", "split", "swap"])
 def test_autograd_wrapper(wrap):
     w = small_workload("autograd", B=1, H=4, Hkv=4, d=64, N=512, G=256, shift_heads=2)
     say(f"case {w} wrap={wrap}")
