@@ -43,15 +43,34 @@ def _fptr(t):
 
 
 def _check_tensors(q, k, v, extra=()):
-    for name, t in (("q", q), ("k", k), ("v", v)) + tuple(extra):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+    """q [B,N,H,d], k and v [B,N,Hkv,d] of one dtype, plus the named tensors of
+    ``extra`` as (name, tensor, shape, dtype); shape None = q's, dtype None =
+    q's.  Every tensor must be contiguous and on q's GPU: the library takes raw
+    pointers, so a mismatch here would become an out-of-bounds access there."""
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
         raise ValueError(f"bad shapes q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
+    for name, t, shape, dtype in (("q", q, None, None), ("k", k, k.shape, None), ("v", v, v.shape, None)) + tuple(extra):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a GPU tensor on {q.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        want = tuple(q.shape if shape is None else shape)
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+        if t.dtype != (q.dtype if dtype is None else dtype):
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype if dtype is None else dtype}")
+
+
+def _lse_shape(q):
+    B, N, H, _ = q.shape
+    return (B, H, N)
+
+
+def _check_workspace(q, ws):
+    if not ws.is_cuda or ws.device != q.device or not ws.is_contiguous() or ws.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {q.device}")
 
 
 def _wrap_code(wrap):
@@ -76,6 +95,7 @@ def s2attn_fwd(q, k, v, G, shift_heads=None, out=None, lse=None, stream=None, wr
         shift_heads = H // 2
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensors(q, k, v, (("out", o, None, None), ("lse", lse_t, (B, H, N), torch.float32)))
     with torch.cuda.device(q.device):
         st = _lib.load().s2attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse_t),
                                        B, H, Hkv, N, d, G, shift_heads, _wrap_code(wrap), _dtype_code(q),
@@ -92,7 +112,8 @@ def s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype):
 
 def s2attn_bwd(q, k, v, o, lse, do, G, shift_heads=None, workspace=None, stream=None, grads=None, wrap="roll"):
     """S2-Attn backward of sum(o * do).  Returns (dq, dk, dv)."""
-    _check_tensors(q, k, v, (("o", o), ("lse", lse), ("do", do)))
+    _check_tensors(q, k, v, (("o", o, None, None), ("lse", lse, _lse_shape(q), torch.float32),
+                             ("do", do, None, None)))
     B, N, H, d = q.shape
     Hkv = k.shape[2]
     if shift_heads is None:
@@ -104,6 +125,8 @@ def s2attn_bwd(q, k, v, o, lse, do, G, shift_heads=None, workspace=None, stream=
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = grads
+        _check_tensors(q, k, v, (("dq", dq, None, None), ("dk", dk, k.shape, None), ("dv", dv, k.shape, None)))
+    _check_workspace(q, workspace)
     with torch.cuda.device(q.device):
         st = _lib.load().s2attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), _ptr(do),
                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
@@ -126,6 +149,9 @@ def _check(st, where):
 
 def s2attn_bwd_prep(q, k, o, lse, do, workspace, G, shift_heads=None, stream=None):
     """Stage 1 of the backward: Dvec = rowsum(dO * o) and lse * log2(e) into the workspace."""
+    _check_tensors(q, k, k, (("o", o, None, None), ("lse", lse, _lse_shape(q), torch.float32),
+                             ("do", do, None, None)))
+    _check_workspace(q, workspace)
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
         _check(_lib.load().s2attn_bwd_prep(_ptr(o), _fptr(lse), _ptr(do), _ptr(workspace), workspace.numel(),
@@ -135,6 +161,8 @@ def s2attn_bwd_prep(q, k, o, lse, do, workspace, G, shift_heads=None, stream=Non
 
 def s2attn_bwd_dkdv(q, k, v, do, dk, dv, workspace, G, shift_heads=None, stream=None, wrap="roll"):
     """Stage 2 of the backward: dk, dv (needs prep's workspace)."""
+    _check_tensors(q, k, v, (("do", do, None, None), ("dk", dk, k.shape, None), ("dv", dv, k.shape, None)))
+    _check_workspace(q, workspace)
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
         _check(_lib.load().s2attn_bwd_dkdv_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
@@ -146,6 +174,8 @@ def s2attn_bwd_dkdv(q, k, v, do, dk, dv, workspace, G, shift_heads=None, stream=
 
 def s2attn_bwd_dq(q, k, v, do, dq, workspace, G, shift_heads=None, stream=None, wrap="roll"):
     """Stage 3 of the backward: dq (needs prep's workspace)."""
+    _check_tensors(q, k, v, (("do", do, None, None), ("dq", dq, None, None)))
+    _check_workspace(q, workspace)
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
         _check(_lib.load().s2attn_bwd_dq_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
@@ -157,6 +187,9 @@ def s2attn_bwd_dq(q, k, v, do, dq, workspace, G, shift_heads=None, stream=None, 
 
 def s2attn_bwd_prep_dq(q, k, v, o, lse, do, dq, workspace, G, shift_heads=None, stream=None, wrap="roll"):
     """Stages 1 and 3 together: dq, and Dvec and lse * log2(e) into the workspace (dk, dv follow)."""
+    _check_tensors(q, k, v, (("o", o, None, None), ("lse", lse, _lse_shape(q), torch.float32),
+                             ("do", do, None, None), ("dq", dq, None, None)))
+    _check_workspace(q, workspace)
     B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
     with torch.cuda.device(q.device):
         _check(_lib.load().s2attn_bwd_prep_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), _ptr(do), _ptr(dq),

@@ -224,3 +224,20 @@ def test_c_client_builds_and_links(lib, tmp_path):
     exe = build_client(str(tmp_path / "c_abi_client"))
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "usage" in r.stderr, (r.returncode, r.stderr)
+
+
+def test_binding_validates_tensors_before_any_call():
+    """The binding passes raw pointers, so it checks shapes, dtypes, devices and
+    contiguity first (CPU tensors are rejected before the library is used)."""
+    import torch
+    from shifted_sparse_attention_s2attn_amd import s2attn_bwd, s2attn_fwd
+    q = torch.zeros(1, 256, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 256, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        s2attn_fwd(q, k, k, 128, 2)
+    with pytest.raises(ValueError, match="bad shapes"):
+        s2attn_fwd(q, torch.zeros(1, 128, 2, 64, dtype=torch.bfloat16), k, 128, 2)
+    with pytest.raises(TypeError):
+        s2attn_fwd(q, k.float(), k, 128, 2)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        s2attn_bwd(q, k, k, q, torch.zeros(1, 4, 256), q, 128, 2)

@@ -492,6 +492,28 @@ def test_empty_inputs(B, N):
     torch.cuda.synchronize()
 
 
+def test_binding_rejects_mismatched_tensors():
+    """Wrong shapes, dtypes or workspaces raise in the binding, before any launch."""
+    w = small_workload("mismatch", B=1, H=4, Hkv=2, d=64, N=512, G=128, shift_heads=2)
+    t = to_gpu(make_inputs(w, seed=9))
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o, lse = s2attn_fwd(q, k, v, w.G, w.shift_heads)
+    with pytest.raises(ValueError, match="lse"):
+        s2attn_fwd(q, k, v, w.G, w.shift_heads, lse=torch.empty(1, 4, 256, device="cuda"))
+    with pytest.raises(TypeError, match="lse"):
+        s2attn_bwd(q, k, v, o, lse.double(), do, w.G, w.shift_heads)
+    with pytest.raises(ValueError, match="do"):
+        s2attn_bwd(q, k, v, o, lse, do[:, :256].contiguous(), w.G, w.shift_heads)
+    with pytest.raises(ValueError, match="dk"):
+        s2attn_bwd(q, k, v, o, lse, do, w.G, w.shift_heads, grads=(torch.empty_like(q), torch.empty_like(q),
+                                                                      torch.empty_like(k)))
+    with pytest.raises(ValueError, match="workspace"):
+        s2attn_bwd(q, k, v, o, lse, do, w.G, w.shift_heads, workspace=torch.empty(1 << 20, device="cuda"))
+    with pytest.raises(ValueError, match="contiguous"):
+        s2attn_fwd(q.transpose(1, 2).contiguous().transpose(1, 2), k, v, w.G, w.shift_heads)
+    torch.cuda.synchronize()
+
+
 def test_rejected_shape_raises():
     q = torch.zeros((1, 500, 2, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(S2AttnError):
