@@ -112,6 +112,27 @@ def cpu_baseline(w, t, seconds, wrap="roll"):
     }
 
 
+def device_peak():
+    """The bf16 dense matrix-core peak recomputed from what rocminfo reports for
+    the GPU agent (compute units x max engine clock x 4096 FLOP per CU-clock),
+    next to the nominal figure; None where rocminfo is not available."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for block in out.split("Agent ")[1:]:
+        if not re.search(r"Name:\s+gfx9", block):
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", block)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", block)
+        if cu and mhz:
+            n, f = int(cu.group(1)), int(mhz.group(1))
+            return {"compute_units": n, "max_clock_mhz": f, "bf16_peak_tflops": round(n * f * 1e6 * 4096 / 1e12, 1)}
+    return None
+
+
 def gemm_reference(torch, dev, n=16384, reps=5):
     """A vendor bf16 GEMM (torch.matmul, i.e. hipBLASLt) of n x n x n on seeded
     standard-normal operands: the rate a tuned dense contraction sustains on this
@@ -201,7 +222,8 @@ def main():
     el = time.perf_counter() - t0
     ms_step = el * 1e3 / args.steps
 
-    kern_ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
+    kern_all = {n: sorted(ev[j].elapsed_time(ev[j + 1]) for ev in events) for j, n in enumerate(names)}
+    kern_ms = {n: sum(v) / len(v) for n, v in kern_all.items()}
     fwd_f = F.fwd_flops(w.B, w.H, w.N, w.G, w.d, w.shift_heads, args.wrap)
     bwd_f = F.bwd_flops(w.B, w.H, w.N, w.G, w.d, w.shift_heads, args.wrap)
     peak = F.MI355X_BF16_PEAK_TFLOPS if w.dtype == "bf16" else F.MI355X_F32_PEAK_TFLOPS
@@ -213,7 +235,9 @@ def main():
     dominant = max(kern_ms, key=kern_ms.get)
     kernels = {}
     for n, ms in kern_ms.items():
-        kernels[n] = {"ms": round(ms, 4)}
+        v = kern_all[n]
+        kernels[n] = {"ms": round(ms, 4), "ms_min": round(v[0], 4), "ms_median": round(v[len(v) // 2], 4),
+                      "ms_max": round(v[-1], 4)}
         if n in kern_flops:
             kernels[n]["tflops"] = round(kern_flops[n] / ms / 1e9, 1)
             kernels[n]["frac_of_peak"] = round(kern_flops[n] / ms / 1e9 / peak, 4)
@@ -259,6 +283,7 @@ def main():
         torch.cuda.synchronize()
         result["hbm_copy_bytes"] = src.numel() * 4
         del src, dst
+    result["device_peak"] = device_peak()
     if w.dtype == "bf16" and not args.no_gemm_reference:
         ref = gemm_reference(torch, dev)
         ref["fwd_frac"] = round(fwd_f / fwd_ms / 1e9 / ref["tflops"], 4)
