@@ -139,27 +139,28 @@ def test_small_parity_unaligned(w):
     check_full(w, inp, out)
 
 
-def random_cases(n=24, seed=2024):
+def random_cases(n=24, seed=2024, wide=False):
     """Seeded random small problems over every option the ABI accepts: d, dtype,
     B, GQA ratio, shifted-head count, aligned and unaligned G, every wrap mode.
     Combinations the ABI rejects (split, swap or a mixed-shift KV head on groups
     that are not whole 128-row tiles, G/2 not whole tiles for a mixed KV head)
-    are redrawn."""
+    are redrawn.  ``wide``: larger batches, GQA ratios and groups (bf16 only,
+    N up to 4096)."""
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
         d = int(rng.choice([64, 128]))
-        dtype = str(rng.choice(["bf16", "bf16", "f32"]))
-        Hkv = int(rng.choice([1, 2]))
-        r = int(rng.choice([1, 2, 3]))
+        dtype = "bf16" if wide else str(rng.choice(["bf16", "bf16", "f32"]))
+        Hkv = int(rng.choice([1, 2, 3] if wide else [1, 2]))
+        r = int(rng.choice([1, 2, 4] if wide else [1, 2, 3]))
         H = Hkv * r
         S = int(rng.integers(0, H + 1))
-        G = int(rng.choice([128, 256, 384, 512, 100, 7, 250, 1000]))
+        G = int(rng.choice([768, 1024, 1536, 640, 1200, 333] if wide else [128, 256, 384, 512, 100, 7, 250, 1000]))
         N = int(rng.choice([G, 2 * G, 3 * G, G + int(rng.integers(1, G)) if G > 1 else G]))
-        N = min(N, 2048)
+        N = min(N, 4096 if wide else 2048)
         if G > N:
             continue
-        B = int(rng.choice([1, 2]))
+        B = int(rng.choice([1, 2, 3] if wide else [1, 2]))
         aligned = N % G == 0 and G % 128 == 0
         wrap = str(rng.choice(["roll", "split", "swap"]))
         if wrap != "roll" and not aligned:
@@ -179,6 +180,18 @@ RANDOM = random_cases()
 def test_random_shapes(w, wrap):
     say(f"case {w} wrap={wrap}")
     inp = make_inputs(w, seed=7)
+    out = run_gpu(w, to_gpu(inp), wrap=wrap)
+    check_full(w, inp, out, wrap=wrap)
+
+
+RANDOM_WIDE = random_cases(n=12, seed=77, wide=True)
+
+
+@pytest.mark.parametrize("w,wrap", RANDOM_WIDE, ids=[f"{w.name}-d{w.d}-B{w.B}-N{w.N}-G{w.G}-H{w.H}x{w.Hkv}-S{w.shift_heads}-{wrap}"
+                                                     for w, wrap in RANDOM_WIDE])
+def test_random_wide_shapes(w, wrap):
+    say(f"case {w} wrap={wrap}")
+    inp = make_inputs(w, seed=8)
     out = run_gpu(w, to_gpu(inp), wrap=wrap)
     check_full(w, inp, out, wrap=wrap)
 
