@@ -84,7 +84,7 @@ __all__ = [
     "WRAPS", "check_problem", "num_groups", "head_shift", "kv_head", "rolled_order", "group_order", "group_parts",
     "group_forward", "group_backward",
     "forward", "backward",
-    "head_group_forward", "head_group_backward", "row_attention",
+    "head_group_forward", "head_group_backward", "row_attention", "rope",
 ]
 
 
@@ -349,3 +349,40 @@ def backward(q, k, v, do, G, shift_heads, wrap="roll"):
                 dk[b, rows, c] += dKg
                 dv[b, rows, c] += dVg
     return dq, dk, dv
+
+
+def rope(x, pos_scale=1.0, base=10000.0, inverse=False):
+    """Rotary position embedding with Position Interpolation, on q or k.
+
+    The step before the attention on the pages' fine-tuning path (page
+    "LongLoRA: Efficient Fine-tuning of Long-Context Large Language Models",
+    section 3.2 Phase 1 item 2, and "Training Procedure, Hyperparameters, and
+    Dataset Configuration", "Model setup"): the rotary position embeddings of
+    the pre-trained model are rescaled by Position Interpolation so that the
+    extended context maps into the original position range.  The pages give
+    neither formula; the readings taken here are the published definitions:
+    rotary embedding (RoFormer) in the rotate-half pairing of Llama models,
+    dimension i paired with i + d/2, frequencies base^(-2i/d) with base 10000;
+    Position Interpolation multiplies every position by pos_scale = original
+    context / target context (4096 / 32768 for the 7B model at 32k).
+
+    x [B, N, heads, d] (any float dtype; computed in float64), token n at
+    position n.  With angle t = n * pos_scale * base^(-2i/d):
+        y_i       = x_i cos t - x_{i+d/2} sin t
+        y_{i+d/2} = x_{i+d/2} cos t + x_i sin t
+    ``inverse`` rotates by -t: the transpose, which maps gradients of the
+    rotated tensor back to gradients of x.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, N, Hx, d = x.shape
+    if d % 2:
+        raise ValueError(f"the head dimension must be even, got {d}")
+    half = d // 2
+    inv_freq = base ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    t = (np.arange(N, dtype=np.float64) * pos_scale)[:, None] * inv_freq[None, :]   # [N, d/2]
+    c = np.cos(t)[None, :, None, :]
+    s = np.sin(t)[None, :, None, :]
+    if inverse:
+        s = -s
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)

@@ -746,6 +746,63 @@ def pin_unaligned_cut_sdpa(orc):
             _close(dv, tv.grad.numpy(), 1e-11, f"cut/SDPA dV case {i} {wrap}")
 
 
+# ---------------------------------------------------------------------------
+# Rotary position embedding with Position Interpolation (the step before the
+# attention on the fine-tuning path)
+# ---------------------------------------------------------------------------
+
+def pin_rope_complex(orc):
+    """Each pair (i, i + d/2) is the complex number x_i + j x_{i+d/2} multiplied
+    by exp(j t), t = n * scale * base^(-2i/d): numpy complex arithmetic."""
+    rng = np.random.default_rng(300)
+    for (B, N, Hx, d, scale, base) in [(1, 9, 2, 8, 1.0, 10000.0), (2, 17, 3, 16, 0.125, 10000.0),
+                                       (1, 5, 1, 4, 0.5, 500.0)]:
+        x = rng.standard_normal((B, N, Hx, d))
+        half = d // 2
+        z = x[..., :half] + 1j * x[..., half:]
+        freq = np.array([base ** (-2.0 * i / d) for i in range(half)])
+        pos = np.arange(N) * scale
+        rot = np.exp(1j * pos[:, None] * freq[None, :])[None, :, None, :]
+        w = z * rot
+        ref = np.concatenate([w.real, w.imag], axis=-1)
+        _close(orc.rope(x, scale, base), ref, 1e-13, f"rope complex d={d}")
+        winv = z * np.conj(rot)
+        _close(orc.rope(x, scale, base, inverse=True), np.concatenate([winv.real, winv.imag], axis=-1), 1e-13,
+               f"rope inverse complex d={d}")
+
+
+def pin_rope_relative_position(orc):
+    """A rotated query and key meet with a score that depends on their positions
+    only through the difference (the defining property of rotary embeddings)."""
+    rng = np.random.default_rng(301)
+    d, N = 16, 64
+    qv, kv = rng.standard_normal(d), rng.standard_normal(d)
+    X = np.broadcast_to(qv, (1, N, 1, d)).copy()
+    Y = np.broadcast_to(kv, (1, N, 1, d)).copy()
+    for scale in (1.0, 0.125):
+        rq, rk = orc.rope(X, scale)[0, :, 0], orc.rope(Y, scale)[0, :, 0]
+        for m, n, t in [(5, 2, 11), (40, 40, 7), (3, 30, 20), (0, 9, 50)]:
+            a, b = float(rq[m] @ rk[n]), float(rq[m + t] @ rk[n + t])
+            assert abs(a - b) <= 1e-12 * max(1.0, abs(a)), f"rope score moved with the positions ({m},{n})+{t}"
+        assert abs(float(rq[7] @ rk[7]) - float(qv @ kv)) <= 1e-12 * max(1.0, abs(float(qv @ kv))), \
+            "equal positions must give the unrotated score"
+
+
+def pin_rope_orthogonal(orc):
+    """Position 0 (and scale 0) is the identity; norms are preserved; the inverse
+    undoes the rotation and is its transpose: <rope(x), y> = <x, rope_inv(y)>."""
+    rng = np.random.default_rng(302)
+    x = rng.standard_normal((2, 33, 3, 8))
+    y = rng.standard_normal((2, 33, 3, 8))
+    r = orc.rope(x, 0.25)
+    _close(r[:, 0], x[:, 0], 0.0, "rope at position 0")
+    _close(orc.rope(x, 0.0), x, 0.0, "rope with scale 0")
+    _close(np.linalg.norm(r, axis=-1), np.linalg.norm(x, axis=-1), 1e-14, "rope norm")
+    _close(orc.rope(r, 0.25, inverse=True), x, 1e-14, "rope inverse")
+    assert abs(float(np.sum(r * y)) - float(np.sum(x * orc.rope(y, 0.25, inverse=True)))) <= 1e-11, \
+        "the inverse is not the transpose"
+
+
 ALL_PINS = [
     pin_bruteforce_forward, pin_bruteforce_backward, pin_roll_regroup, pin_full_causal,
     pin_direction_reversal, pin_head_swap, pin_closed_forms, pin_finite_differences,
@@ -753,5 +810,5 @@ ALL_PINS = [
     pin_split_bruteforce, pin_split_segments_sdpa, pin_split_agrees_with_roll, pin_split_finite_differences,
     pin_swap_bruteforce, pin_swap_gathered_sdpa, pin_swap_agrees_with_roll_and_split, pin_swap_finite_differences,
     pin_row_attention, pin_unaligned_bruteforce, pin_unaligned_cut_sdpa, pin_unaligned_row_attention,
-    pin_unaligned_swap_gathered_sdpa,
+    pin_unaligned_swap_gathered_sdpa, pin_rope_complex, pin_rope_relative_position, pin_rope_orthogonal,
 ]

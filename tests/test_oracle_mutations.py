@@ -58,6 +58,14 @@ MUTATIONS = [
      "        cut = len(rows) // 2\n        if cut is not None:\n            return np.concatenate", 0),
     ("swap-front-reversed", "return np.concatenate([rows[cut:], rows[:cut]])",
      "return np.concatenate([rows[cut:][::-1], rows[:cut]])", 0),
+    ("rope-interleaved-pairs", "x1, x2 = x[..., :half], x[..., half:]", "x1, x2 = x[..., 0::2], x[..., 1::2]", 0),
+    ("rope-sign", "return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)",
+     "return np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=-1)", 0),
+    ("rope-frequency-exponent", "inv_freq = base ** (-2.0 * np.arange(half, dtype=np.float64) / d)",
+     "inv_freq = base ** (-1.0 * np.arange(half, dtype=np.float64) / d)", 0),
+    ("rope-scale-ignored", "t = (np.arange(N, dtype=np.float64) * pos_scale)", "t = (np.arange(N, dtype=np.float64) * 1.0)", 0),
+    ("rope-position-offset", "t = (np.arange(N, dtype=np.float64) * pos_scale)", "t = (np.arange(1, N + 1, dtype=np.float64) * pos_scale)", 0),
+    ("rope-inverse-ignored", "    if inverse:\n        s = -s\n", "", 0),
     ("row-drops-own-key", "keys = rows[part.start:pos + 1]", "keys = rows[part.start:pos]", 0),
     ("row-group-start", "keys = rows[part.start:pos + 1]", "keys = rows[0:pos + 1]", 0),
     ("row-drops-dvec", "ds = p * (dp - np.dot(dot, o))", "ds = p * dp", 0),
