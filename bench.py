@@ -165,6 +165,9 @@ def main():
     ap.add_argument("--workload", default="llama2-7b-32k")
     ap.add_argument("--wrap", default="roll", choices=["roll", "split", "swap"],
                     help="wrap handling of the shifted heads (split, swap: Table 8's Variants 2, 3)")
+    ap.add_argument("--rope", action="store_true",
+                    help="also time the rotary embedding with Position Interpolation on q and k (and its inverse "
+                         "on dq and dk), the step before the attention; reported apart from the step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-reference", action="store_true")
@@ -283,6 +286,29 @@ def main():
         torch.cuda.synchronize()
         result["hbm_copy_bytes"] = src.numel() * 4
         del src, dst
+    if args.rope:
+        from shifted_sparse_attention_s2attn_amd import s2attn_rope
+        pi = 4096 / w.N                          # Position Interpolation from a 4k model to this context
+        qr, kr = torch.empty_like(q), torch.empty_like(k)
+
+        def rope_step():
+            s2attn_rope(q, pi, out=qr)
+            s2attn_rope(k, pi, out=kr)
+            s2attn_rope(dq, pi, inverse=True, out=qr)
+            s2attn_rope(dk, pi, inverse=True, out=kr)
+
+        for _ in range(3):
+            rope_step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            rope_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        nbytes = 2 * 2 * (q.numel() + k.numel()) * q.element_size()   # read + write, forward and inverse
+        result["rope"] = {"ms": round(ms, 4), "gbps": round(nbytes / ms / 1e6, 1), "bytes": nbytes,
+                          "pos_scale": pi, "bound": "hbm", "frac_of_8tbs": round(nbytes / ms / 1e6 / 8000, 4)}
     result["device_peak"] = device_peak()
     if w.dtype == "bf16" and not args.no_gemm_reference:
         ref = gemm_reference(torch, dev)

@@ -195,6 +195,33 @@ int s2attn_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO
                      int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
                      int dtype, void* stream);
 
+/*
+ * Rotary position embedding with Position Interpolation, the step before the
+ * attention on the pages' fine-tuning path (page "LongLoRA: Efficient
+ * Fine-tuning of Long-Context Large Language Models", section 3.2 Phase 1
+ * item 2, and "Training Procedure, Hyperparameters, and Dataset
+ * Configuration", "Model setup": the pre-trained rotary embeddings are
+ * rescaled by Position Interpolation).  The pages give no formula; this is
+ * the published rotary embedding in the rotate-half pairing.  For x and y of
+ * shape [B, N, Hx, d] (q with Hx = H, or k with Hx = Hkv), token n and
+ * i < d/2, with t = n * pos_scale * base^(-2i/d):
+ *   y[.., i]       = x[.., i] cos t - x[.., i + d/2] sin t
+ *   y[.., i + d/2] = x[.., i + d/2] cos t + x[.., i] sin t
+ * pos_scale is Position Interpolation's original / target context (1 = plain
+ * rotary embedding; 4096 / 32768 for a 4k model extended to 32k); base is the
+ * rotary base (10000 for Llama2).  inverse = 1 turns by -t instead: the
+ * transpose, which maps the gradient of y to the gradient of x, so a backward
+ * applies it to dq and dk.  y may equal x (in place); otherwise the two must
+ * not overlap.  Asynchronous on `stream`; computed in fp32 from angles formed
+ * and reduced in fp64, outputs rounded to the dtype.
+ * Errors (before any HIP call): S2ATTN_ERR_SHAPE for B or N < 0, Hx <= 0 or
+ * d <= 0; S2ATTN_ERR_UNSUPPORTED for d not in {64, 128}, an unknown dtype,
+ * pos_scale negative or not finite, base not finite or <= 1, or inverse not 0
+ * or 1; S2ATTN_ERR_NULL for a NULL x or y.  B == 0 or N == 0 is a no-op.
+ */
+int s2attn_rope(const void* x, void* y, int B, int N, int Hx, int d, double pos_scale, double base,
+                int inverse, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* s2attn_status_str(int status);
 

@@ -25,7 +25,7 @@ WRAPS = {"roll": S2ATTN_WRAP_ROLL, "split": S2ATTN_WRAP_SPLIT, "swap": S2ATTN_WR
 
 EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes", "s2attn_bwd_prep", "s2attn_bwd_dkdv",
            "s2attn_bwd_dq", "s2attn_bwd_prep_dq", "s2attn_fwd_ex", "s2attn_bwd_ex", "s2attn_bwd_dkdv_ex",
-           "s2attn_bwd_dq_ex", "s2attn_status_str")
+           "s2attn_bwd_dq_ex", "s2attn_rope", "s2attn_status_str")
 
 _lib = None
 
@@ -64,6 +64,9 @@ def load():
     lib.s2attn_bwd_dq_ex.restype = i
     lib.s2attn_bwd_prep_dq.argtypes = [vp, vp, vp, vp, fp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, i, vp]
     lib.s2attn_bwd_prep_dq.restype = i
+    dbl = ctypes.c_double
+    lib.s2attn_rope.argtypes = [vp, vp, i, i, i, i, dbl, dbl, i, i, vp]
+    lib.s2attn_rope.restype = i
     lib.s2attn_status_str.argtypes = [i]
     lib.s2attn_status_str.restype = ctypes.c_char_p
     _lib = lib

@@ -13,7 +13,7 @@ from . import _lib
 
 __all__ = ["S2AttnError", "s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes",
            "s2attn_bwd_prep", "s2attn_bwd_dkdv", "s2attn_bwd_dq", "s2attn_bwd_prep_dq",
-           "s2attn_status_str", "S2Attn", "s2attn"]
+           "s2attn_status_str", "S2Attn", "s2attn", "s2attn_rope", "RoPE", "rope"]
 
 
 class S2AttnError(RuntimeError):
@@ -224,3 +224,42 @@ def s2attn(q, k, v, G, shift_heads=None, wrap="roll"):
     Variant 3: they stay in the last group but come before its end tokens.
     """
     return S2Attn.apply(q, k, v, G, q.shape[2] // 2 if shift_heads is None else shift_heads, wrap)
+
+
+def s2attn_rope(x, pos_scale=1.0, base=10000.0, inverse=False, out=None, stream=None):
+    """Rotary position embedding with Position Interpolation on x [B, N, heads, d]
+    (q or k): pair (i, i + d/2) of token n turned by n * pos_scale * base^(-2i/d)
+    (by minus that with ``inverse``).  ``out`` may be ``x`` (in place)."""
+    if x.dim() != 4:
+        raise ValueError(f"x must be [B, N, heads, d], got {tuple(x.shape)}")
+    y = torch.empty_like(x) if out is None else out
+    for name, t in (("x", x), ("out", y)):
+        if not t.is_cuda or t.device != x.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor on {x.device}")
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError(f"out {tuple(y.shape)} {y.dtype} does not match x {tuple(x.shape)} {x.dtype}")
+    B, N, Hx, d = x.shape
+    with torch.cuda.device(x.device):
+        st = _lib.load().s2attn_rope(_ptr(x), _ptr(y), B, N, Hx, d, float(pos_scale), float(base), int(bool(inverse)),
+                                     _dtype_code(x), _stream(stream))
+    if st != _lib.S2ATTN_OK:
+        raise S2AttnError(st, "s2attn_rope")
+    return y
+
+
+class RoPE(torch.autograd.Function):
+    """autograd wrapper: the backward is the inverse rotation (its transpose)."""
+
+    @staticmethod
+    def forward(ctx, x, pos_scale, base):
+        ctx.pos_scale, ctx.base = pos_scale, base
+        return s2attn_rope(x.contiguous(), pos_scale, base)
+
+    @staticmethod
+    def backward(ctx, g):
+        return s2attn_rope(g.contiguous(), ctx.pos_scale, ctx.base, inverse=True), None, None
+
+
+def rope(x, pos_scale=1.0, base=10000.0):
+    """Differentiable rotary embedding with Position Interpolation (see s2attn_rope)."""
+    return RoPE.apply(x, pos_scale, base)

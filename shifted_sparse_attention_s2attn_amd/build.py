@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libs2attn.so")
-SOURCES = ["s2attn_api.hip", "s2attn_fwd.hip", "s2attn_bwd.hip"]
+SOURCES = ["s2attn_api.hip", "s2attn_fwd.hip", "s2attn_bwd.hip", "s2attn_rope.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -4,10 +4,13 @@
 // instantiation recording that its LDS limit was raised.
 #include "s2attn.h"
 
+#include <math.h>
 #include <stdint.h>
 #include "s2attn_common.h"
 
 namespace s2a {
+template <typename T, int D>
+hipError_t launch_rope(const void*, void*, int, int, int, double, double, int, hipStream_t);
 template <typename T, int D>
 hipError_t launch_fwd(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, int,
                       hipStream_t);
@@ -264,11 +267,31 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
                        shift_heads, S2ATTN_WRAP_ROLL, dtype, stream);
 }
 
+int s2attn_rope(const void* x, void* y, int B, int N, int Hx, int d, double pos_scale, double base,
+                int inverse, int dtype, void* stream) {
+  if (B < 0 || N < 0 || Hx <= 0 || d <= 0) return S2ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return S2ATTN_ERR_UNSUPPORTED;
+  if (dtype != S2ATTN_BF16 && dtype != S2ATTN_F32) return S2ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(pos_scale) || pos_scale < 0 || !isfinite(base) || !(base > 1) || (inverse != 0 && inverse != 1))
+    return S2ATTN_ERR_UNSUPPORTED;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!x || !y) return S2ATTN_ERR_NULL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == S2ATTN_BF16)
+    e = d == 64 ? s2a::launch_rope<s2a::bf16, 64>(x, y, B, N, Hx, pos_scale, base, inverse, s)
+                : s2a::launch_rope<s2a::bf16, 128>(x, y, B, N, Hx, pos_scale, base, inverse, s);
+  else
+    e = d == 64 ? s2a::launch_rope<float, 64>(x, y, B, N, Hx, pos_scale, base, inverse, s)
+                : s2a::launch_rope<float, 128>(x, y, B, N, Hx, pos_scale, base, inverse, s);
+  return e == hipSuccess ? S2ATTN_OK : S2ATTN_ERR_HIP;
+}
+
 const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_OK: return "ok";
     case S2ATTN_ERR_NULL: return "a required pointer is NULL";
     case S2ATTN_ERR_SHAPE: return "invalid shape (a size < 0, H, Hkv, d or G <= 0, G > N, shift_heads outside [0,H], or H % Hkv != 0)";
-    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split, swap or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, or grid too large)";
+    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split, swap or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, grid too large, or a rotary scale, base or direction out of range)";
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     default: return "unknown status";

@@ -1,0 +1,92 @@
+// Rotary position embedding with Position Interpolation on q or k (gfx950).
+//
+// The step before the attention on the pages' fine-tuning path (page
+// "LongLoRA: Efficient Fine-tuning of Long-Context Large Language Models",
+// section 3.2 Phase 1 item 2, and "Training Procedure, Hyperparameters, and
+// Dataset Configuration", "Model setup"): the pre-trained model's rotary
+// position embeddings are rescaled by Position Interpolation, every position
+// multiplied by original context / target context.  The rotation itself is
+// the published rotary embedding in the rotate-half pairing: dimension i is
+// paired with i + d/2 and turned by t = n * pos_scale * base^(-2i/d) at token n.
+//
+// An elementwise pass bound by HBM bandwidth (one read and one write of the
+// tensor).  It is not fused into the attention kernels' tile loads: those are
+// bound by the matrix cores and their issue slots, and rotating every Q and K
+// operand there would cost more than this pass.
+//
+// One thread owns 8 consecutive pairs (dimensions 8c .. 8c+7 and their
+// partners d/2 + 8c ..) and strides over rows, so its 8 frequencies are
+// computed once, in float64.  Angles are formed in float64, in revolutions,
+// and reduced to [-1/2, 1/2] before the float32 sine and cosine: at positions
+// near 10^5 a float32 angle would be off by ~10^-2 radians.  bf16 outputs take
+// the hardware sine and cosine of revolutions (error far below the output's
+// rounding); fp32 outputs take sincosf.
+#include "s2attn_common.h"
+
+namespace s2a {
+
+// sine and cosine of x revolutions (x * 2 pi radians), |x| <= 1/2
+__device__ __forceinline__ float hw_sin_rev(float x) { return __builtin_amdgcn_sinf(x); }
+__device__ __forceinline__ float hw_cos_rev(float x) { return __builtin_amdgcn_cosf(x); }
+
+// I: the row index type (32-bit while the row count allows it: cheaper division)
+template <typename T, int D, typename I>
+__global__ __launch_bounds__(256) void s2attn_rope_kernel(const T* x, T* y, I rows, int N, int Hx,
+                                                          double pos_scale, double log2_base, int inverse) {
+  constexpr int TPR = D / 16;                 // threads per row, 8 pairs each
+  constexpr int RPB = 256 / TPR;              // rows per block per pass
+  const int c = threadIdx.x % TPR;
+  double g[8];                                // revolutions per position of each pair
+#pragma unroll
+  for (int e = 0; e < 8; ++e) g[e] = exp2(-(2.0 * (8 * c + e) / D) * log2_base) * 0.15915494309189533577;
+  for (I r = (I)blockIdx.x * RPB + threadIdx.x / TPR; r < rows; r += (I)gridDim.x * RPB) {
+    const int n = (int)((r / (I)Hx) % (I)N);  // rows are (batch, token, head), token-major
+    const double pos = (double)n * pos_scale;
+    const T* xr = x + r * D;
+    T* yr = y + r * D;
+    const v8<T> a = *reinterpret_cast<const v8<T>*>(xr + 8 * c);
+    const v8<T> b = *reinterpret_cast<const v8<T>*>(xr + D / 2 + 8 * c);
+    v8<T> ya, yb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double u = pos * g[e];
+      const float fr = (float)(u - rint(u));    // the angle in revolutions, in [-1/2, 1/2]
+      float sn, cs;
+      if constexpr (sizeof(T) == 2) {
+        sn = hw_sin_rev(fr);
+        cs = hw_cos_rev(fr);
+      } else {
+        sincosf(fr * 6.28318530717958647692f, &sn, &cs);
+      }
+      if (inverse) sn = -sn;
+      const float xa = (float)a[e], xb = (float)b[e];
+      ya[e] = (T)(xa * cs - xb * sn);
+      yb[e] = (T)(xb * cs + xa * sn);
+    }
+    *reinterpret_cast<v8<T>*>(yr + 8 * c) = ya;
+    *reinterpret_cast<v8<T>*>(yr + D / 2 + 8 * c) = yb;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_rope(const void* x, void* y, int B, int N, int Hx, double pos_scale, double base, int inverse,
+                       hipStream_t stream) {
+  const long long rows = (long long)B * N * Hx;
+  constexpr int RPB = 256 / (D / 16);
+  const long long blocks = (rows + RPB - 1) / RPB;
+  const unsigned grid = (unsigned)(blocks < 16384 ? blocks : 16384);   // grid-stride beyond 16384 blocks
+  if (rows + (long long)grid * RPB < (1ll << 32))
+    hipLaunchKernelGGL((s2attn_rope_kernel<T, D, unsigned>), dim3(grid), dim3(256), 0, stream, (const T*)x, (T*)y,
+                       (unsigned)rows, N, Hx, pos_scale, log2(base), inverse);
+  else
+    hipLaunchKernelGGL((s2attn_rope_kernel<T, D, long long>), dim3(grid), dim3(256), 0, stream, (const T*)x, (T*)y,
+                       rows, N, Hx, pos_scale, log2(base), inverse);
+  return hipGetLastError();
+}
+
+template hipError_t launch_rope<bf16, 64>(const void*, void*, int, int, int, double, double, int, hipStream_t);
+template hipError_t launch_rope<bf16, 128>(const void*, void*, int, int, int, double, double, int, hipStream_t);
+template hipError_t launch_rope<float, 64>(const void*, void*, int, int, int, double, double, int, hipStream_t);
+template hipError_t launch_rope<float, 128>(const void*, void*, int, int, int, double, double, int, hipStream_t);
+
+}  // namespace s2a

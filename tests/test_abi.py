@@ -241,3 +241,21 @@ def test_binding_validates_tensors_before_any_call():
         s2attn_fwd(q, k.float(), k, 128, 2)
     with pytest.raises(ValueError, match="GPU tensor"):
         s2attn_bwd(q, k, k, q, torch.zeros(1, 4, 256), q, 128, 2)
+
+
+def test_rope_validation(lib):
+    """s2attn_rope checks sizes, then options, then pointers, before any HIP call."""
+    E = _lib
+    args = dict(B=1, N=64, Hx=2, d=128, scale=0.125, base=10000.0, inv=0, dtype=0)
+
+    def call(x=None, y=None, **kw):
+        a = dict(args, **kw)
+        return lib.s2attn_rope(x, y, a["B"], a["N"], a["Hx"], a["d"], a["scale"], a["base"], a["inv"], a["dtype"], None)
+
+    assert call() == E.S2ATTN_ERR_NULL
+    assert call(B=-1) == E.S2ATTN_ERR_SHAPE and call(Hx=0) == E.S2ATTN_ERR_SHAPE and call(d=0) == E.S2ATTN_ERR_SHAPE
+    assert call(d=96) == E.S2ATTN_ERR_UNSUPPORTED and call(dtype=7) == E.S2ATTN_ERR_UNSUPPORTED
+    for bad in (dict(scale=-1.0), dict(scale=float("nan")), dict(base=1.0), dict(base=float("inf")), dict(inv=2)):
+        assert call(**bad) == E.S2ATTN_ERR_UNSUPPORTED, bad
+    assert call(B=0) == E.S2ATTN_OK and call(N=0) == E.S2ATTN_OK    # empty: a no-op
+    assert call(scale=0.0, inv=1) == E.S2ATTN_ERR_NULL                  # valid options, NULL pointers
