@@ -49,7 +49,7 @@ int main(int argc, char** argv) {
 
   /* host images of the inputs and outputs */
   char* host = malloc(2 * nq + 2 * nkv);
-  char* out = malloc(2 * nq + 2 * nkv + nlse);
+  char* out = malloc(3 * nq + 2 * nkv + nlse);
   if (!host || !out) return 1;
   FILE* fi = fopen(argv[1], "rb");
   if (!fi || !read_exact(fi, host, 2 * nq + 2 * nkv)) {
@@ -58,7 +58,7 @@ int main(int argc, char** argv) {
   }
   fclose(fi);
 
-  void *q, *k, *v, *dO, *o, *dq, *dk, *dv, *ws = NULL;
+  void *q, *k, *v, *dO, *o, *dq, *dk, *dv, *qr, *ws = NULL;
   float* lse;
   HIP_CHECK(hipMalloc(&q, nq));
   HIP_CHECK(hipMalloc(&k, nkv));
@@ -69,6 +69,7 @@ int main(int argc, char** argv) {
   HIP_CHECK(hipMalloc(&dq, nq));
   HIP_CHECK(hipMalloc(&dk, nkv));
   HIP_CHECK(hipMalloc(&dv, nkv));
+  HIP_CHECK(hipMalloc(&qr, nq));
   const size_t wsb = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, S, S2ATTN_BF16);
   if (wsb == 0) {
     fprintf(stderr, "s2attn_bwd_workspace_bytes rejected the problem\n");
@@ -85,6 +86,8 @@ int main(int argc, char** argv) {
   S2_CHECK(s2attn_fwd_ex(q, k, v, o, lse, B, H, Hkv, N, d, G, S, wrap, S2ATTN_BF16, stream));
   S2_CHECK(s2attn_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, ws, wsb, B, H, Hkv, N, d, G, S, wrap, S2ATTN_BF16,
                          stream));
+  /* rotary embedding of q with Position Interpolation by 1/4, base 10000 */
+  S2_CHECK(s2attn_rope(q, qr, B, N, H, d, 0.25, 10000.0, 0, S2ATTN_BF16, stream));
   HIP_CHECK(hipStreamSynchronize(stream));
 
   char* p = out;
@@ -97,15 +100,17 @@ int main(int argc, char** argv) {
   HIP_CHECK(hipMemcpy(p, dk, nkv, hipMemcpyDeviceToHost));
   p += nkv;
   HIP_CHECK(hipMemcpy(p, dv, nkv, hipMemcpyDeviceToHost));
+  p += nkv;
+  HIP_CHECK(hipMemcpy(p, qr, nq, hipMemcpyDeviceToHost));
   FILE* fo = fopen(argv[2], "wb");
-  if (!fo || !write_exact(fo, out, 2 * nq + 2 * nkv + nlse)) {
+  if (!fo || !write_exact(fo, out, 3 * nq + 2 * nkv + nlse)) {
     fprintf(stderr, "cannot write %s\n", argv[2]);
     return 1;
   }
   fclose(fo);
 
   HIP_CHECK(hipStreamDestroy(stream));
-  void* bufs[] = {q, k, v, dO, o, lse, dq, dk, dv, ws};
+  void* bufs[] = {q, k, v, dO, o, lse, dq, dk, dv, qr, ws};
   for (size_t i = 0; i < sizeof(bufs) / sizeof(bufs[0]); ++i) HIP_CHECK(hipFree(bufs[i]));
   free(host);
   free(out);

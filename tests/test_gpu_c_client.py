@@ -1,6 +1,7 @@
 """The library from plain C: tests/_bin/c_abi_client (tests/c_abi_client.c)
-allocates device memory with the HIP runtime, calls s2attn_fwd_ex and
-s2attn_bwd_ex through include/s2attn.h, and writes the outputs to a file.  They
+allocates device memory with the HIP runtime, calls s2attn_fwd_ex,
+s2attn_bwd_ex and s2attn_rope (q, Position Interpolation by 1/4) through
+include/s2attn.h, and writes the outputs to a file.  They
 must meet the float64 oracle's bars and equal, bit for bit, what the Python
 binding gets from the same library on the same inputs (every kernel is
 deterministic)."""
@@ -13,7 +14,7 @@ import pytest
 import torch
 
 from oracle import s2attn_oracle as orc
-from shifted_sparse_attention_s2attn_amd import s2attn_bwd, s2attn_fwd
+from shifted_sparse_attention_s2attn_amd import s2attn_bwd, s2attn_fwd, s2attn_rope
 from shifted_sparse_attention_s2attn_amd.inputs import make_inputs, small_workload
 
 pytestmark = pytest.mark.gpu
@@ -46,7 +47,7 @@ def test_c_client_matches_oracle_and_binding(w, wrap, tmp_path):
 
     raw = dst.read_bytes()
     nq, nkv, nl = w.B * w.N * w.H * w.d, w.B * w.N * w.Hkv * w.d, w.B * w.H * w.N
-    assert len(raw) == 2 * (2 * nq + 2 * nkv) + 4 * nl
+    assert len(raw) == 2 * (3 * nq + 2 * nkv) + 4 * nl
     pos = 0
 
     def take(n, dtype, shape):
@@ -62,13 +63,17 @@ def test_c_client_matches_oracle_and_binding(w, wrap, tmp_path):
     dq = take(nq, np.int16, qs).view(torch.bfloat16)
     dk = take(nkv, np.int16, ks).view(torch.bfloat16)
     dv = take(nkv, np.int16, ks).view(torch.bfloat16)
+    qr = take(nq, np.int16, qs).view(torch.bfloat16)
 
     # the same library through the Python binding
     t = {k: v.cuda() for k, v in inp.items()}
     o_b, lse_b = s2attn_fwd(t["q"], t["k"], t["v"], w.G, w.shift_heads, wrap=wrap)
     g_b = s2attn_bwd(t["q"], t["k"], t["v"], o_b, lse_b, t["do"], w.G, w.shift_heads, wrap=wrap)
     torch.cuda.synchronize()
-    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), (o, lse, dq, dk, dv), (o_b, lse_b) + tuple(g_b)):
+    qr_b = s2attn_rope(t["q"], 0.25)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv", "rope(q)"), (o, lse, dq, dk, dv, qr),
+                          (o_b, lse_b) + tuple(g_b) + (qr_b,)):
         assert torch.equal(a, b.cpu()), f"{name}: C client and Python binding differ"
 
     # against the oracle (bars of the bf16 parity tests)
@@ -81,3 +86,8 @@ def test_c_client_matches_oracle_and_binding(w, wrap, tmp_path):
     for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
         e = float(np.linalg.norm(f(a) - b) / np.linalg.norm(b))
         assert e <= 3e-2, (name, e)
+    # rotary embedding: the per-element bar of the rotary parity tests
+    half = w.d // 2
+    mag = np.abs(q[..., :half]) + np.abs(q[..., half:])
+    bound = 2.0 ** -8 * np.concatenate([mag, mag], axis=-1) + 1e-30
+    assert float(np.max(np.abs(f(qr) - orc.rope(q, 0.25, 10000.0, False)) / bound)) <= 1.0
