@@ -71,7 +71,8 @@ typedef enum {
     S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype or wrap option, the mixed-shift or
                                     split / swap rule above, or the grid size limit */
     S2ATTN_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError) */
-    S2ATTN_ERR_WORKSPACE = 5     /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
+    S2ATTN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
+    S2ATTN_ERR_ALIGN = 6         /* an element tensor pointer not 16-byte aligned, or lse not 4-byte */
 } s2attn_status;
 
 /*
@@ -217,7 +218,8 @@ int s2attn_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO
  * Errors (before any HIP call): S2ATTN_ERR_SHAPE for B or N < 0, Hx <= 0 or
  * d <= 0; S2ATTN_ERR_UNSUPPORTED for d not in {64, 128}, an unknown dtype,
  * pos_scale negative or not finite, base not finite or <= 1, or inverse not 0
- * or 1; S2ATTN_ERR_NULL for a NULL x or y.  B == 0 or N == 0 is a no-op.
+ * or 1; S2ATTN_ERR_NULL for a NULL x or y, S2ATTN_ERR_ALIGN for an x or y not
+ * 16-byte aligned.  B == 0 or N == 0 is a no-op.
  */
 int s2attn_rope(const void* x, void* y, int B, int N, int Hx, int d, double pos_scale, double base,
                 int inverse, int dtype, void* stream);

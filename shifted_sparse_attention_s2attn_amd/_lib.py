@@ -16,6 +16,7 @@ S2ATTN_ERR_SHAPE = 2
 S2ATTN_ERR_UNSUPPORTED = 3
 S2ATTN_ERR_HIP = 4
 S2ATTN_ERR_WORKSPACE = 5
+S2ATTN_ERR_ALIGN = 6
 S2ATTN_BF16 = 0
 S2ATTN_F32 = 1
 S2ATTN_WRAP_ROLL = 0

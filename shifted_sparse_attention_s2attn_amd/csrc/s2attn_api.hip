@@ -5,6 +5,7 @@
 #include "s2attn.h"
 
 #include <math.h>
+#include <initializer_list>
 #include <stdint.h>
 #include "s2attn_common.h"
 
@@ -59,6 +60,15 @@ int check_problem(int B, int H, int Hkv, int N, int d, int G, int shift_heads, i
 
 bool empty_problem(int B, int N) { return B == 0 || N == 0; }
 
+// Element tensors are read and written in 16-byte vectors; lse takes 4-byte
+// scalars.  Checked after the NULL checks, before any HIP call.
+bool misaligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return true;
+  return false;
+}
+bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) != 0; }
+
 // The split option cuts the last group at G/2 and the swap option reorders
 // its halves; both need aligned shapes.
 int check_wrap(int wrap, int N, int G) {
@@ -81,6 +91,7 @@ int s2attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* l
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !o || !lse) return S2ATTN_ERR_NULL;
+  if (misaligned16({q, k, v, o}) || misaligned4(lse)) return S2ATTN_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == S2ATTN_BF16) {
@@ -173,6 +184,7 @@ int s2attn_bwd_prep(const void* o, const float* lse, const void* dO, void* works
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!o || !lse || !dO) return S2ATTN_ERR_NULL;
+  if (misaligned16({o, dO}) || misaligned4(lse)) return S2ATTN_ERR_ALIGN;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
@@ -188,6 +200,7 @@ int s2attn_bwd_dkdv_ex(const void* q, const void* k, const void* v, const void* 
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !dO || !dk || !dv) return S2ATTN_ERR_NULL;
+  if (misaligned16({q, k, v, dO, dk, dv})) return S2ATTN_ERR_ALIGN;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
@@ -211,6 +224,7 @@ int s2attn_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !dO || !dq) return S2ATTN_ERR_NULL;
+  if (misaligned16({q, k, v, dO, dq})) return S2ATTN_ERR_ALIGN;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
@@ -234,6 +248,7 @@ int s2attn_bwd_prep_dq(const void* q, const void* k, const void* v, const void* 
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dO || !dq) return S2ATTN_ERR_NULL;
+  if (misaligned16({q, k, v, o, dO, dq}) || misaligned4(lse)) return S2ATTN_ERR_ALIGN;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
@@ -249,6 +264,7 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, co
   if (st != S2ATTN_OK) return st;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
+  if (misaligned16({q, k, v, o, dO, dq, dk, dv}) || misaligned4(lse)) return S2ATTN_ERR_ALIGN;
   Workspace ws;
   st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
@@ -276,6 +292,7 @@ int s2attn_rope(const void* x, void* y, int B, int N, int Hx, int d, double pos_
     return S2ATTN_ERR_UNSUPPORTED;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!x || !y) return S2ATTN_ERR_NULL;
+  if (misaligned16({x, y})) return S2ATTN_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == S2ATTN_BF16)
@@ -294,6 +311,7 @@ const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split, swap or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, grid too large, or a rotary scale, base or direction out of range)";
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
+    case S2ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (element tensors need 16 bytes, lse 4)";
     default: return "unknown status";
   }
 }

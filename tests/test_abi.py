@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert lib.s2attn_status_str(code)
     assert lib.s2attn_status_str(99) == b"unknown status"
 
@@ -205,6 +205,31 @@ def test_bwd_stage_entry_points_validate(lib):
     assert lib.s2attn_bwd_prep_dq(*pd, DUMMY, need - 4, *sz, 0, 0, None) == _lib.S2ATTN_ERR_WORKSPACE
     assert lib.s2attn_bwd_prep_dq(*pd, DUMMY, need, *bad_n[:7], 0, 0, None) == _lib.S2ATTN_ERR_SHAPE
     assert lib.s2attn_bwd_prep_dq(*pd, DUMMY, need, *sz, 3, 0, None) == _lib.S2ATTN_ERR_UNSUPPORTED
+
+
+def test_misaligned_pointers_rejected(lib):
+    """Element tensors need 16-byte alignment (16-byte vector accesses), lse 4:
+    every entry point returns S2ATTN_ERR_ALIGN before any HIP call."""
+    E = _lib
+    odd = ctypes.c_void_p(0x1008)
+    fodd = ctypes.cast(ctypes.c_void_p(0x1002), ctypes.POINTER(ctypes.c_float))
+    p = GOOD
+    sz = [p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"]]
+    dims = sz + [0, None]
+    need = lib.s2attn_bwd_workspace_bytes(*sz, 0)
+    assert lib.s2attn_fwd(odd, DUMMY, DUMMY, DUMMY, FDUMMY, *dims) == E.S2ATTN_ERR_ALIGN
+    assert lib.s2attn_fwd(DUMMY, DUMMY, DUMMY, odd, FDUMMY, *dims) == E.S2ATTN_ERR_ALIGN
+    assert lib.s2attn_fwd(DUMMY, DUMMY, DUMMY, DUMMY, fodd, *dims) == E.S2ATTN_ERR_ALIGN
+    for i in range(9):      # q, k, v, o, lse, dO, dq, dk, dv in turn
+        ptrs = [DUMMY, DUMMY, DUMMY, DUMMY, FDUMMY, DUMMY, DUMMY, DUMMY, DUMMY]
+        ptrs[i] = fodd if i == 4 else odd
+        assert lib.s2attn_bwd(*ptrs, DUMMY, need, *dims) == E.S2ATTN_ERR_ALIGN, i
+    assert lib.s2attn_bwd_prep(odd, FDUMMY, DUMMY, DUMMY, need, *dims) == E.S2ATTN_ERR_ALIGN
+    assert lib.s2attn_bwd_dkdv(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, odd, DUMMY, need, *dims) == E.S2ATTN_ERR_ALIGN
+    assert lib.s2attn_bwd_dq(DUMMY, odd, DUMMY, DUMMY, DUMMY, DUMMY, need, *dims) == E.S2ATTN_ERR_ALIGN
+    assert lib.s2attn_bwd_prep_dq(DUMMY, DUMMY, DUMMY, DUMMY, fodd, DUMMY, DUMMY, DUMMY, need, *sz, 0, 0,
+                                  None) == E.S2ATTN_ERR_ALIGN
+    assert lib.s2attn_rope(DUMMY, odd, 1, 64, 2, 128, 0.125, 10000.0, 0, 0, None) == E.S2ATTN_ERR_ALIGN
 
 
 def test_header_is_plain_c():
