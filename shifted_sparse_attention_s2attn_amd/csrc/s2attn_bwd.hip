@@ -12,7 +12,8 @@
 // with dK, dV summed over the query heads that share a key/value head.
 //
 // Three stages on one stream, no atomics:
-//   prep : Dvec[b,h,t] = sum_d dO*O and lse*log2(e), fp32, into the workspace.
+//   prep : -Dvec[b,h,t] = -sum_d dO*O and lse*log2(e), fp32, into the workspace
+//          (Dvec negated, so that the bf16 dK/dV kernel starts its dP sums there).
 //   dkdv : one workgroup per 128 key rows of one (batch, KV head); it walks
 //          every query head sharing the KV head and, in that head's rolled
 //          frame, every query tile of the group from the diagonal to the group
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_pre(
     const long long h = row % H;
     const long long bt = row / H;
     const long long t = bt % N, b = bt / N;
-    dvec[(b * H + h) * N + t] = s;
+    dvec[(b * H + h) * N + t] = -s;               // stored negated (see the dK/dV kernel)
     lse2[(b * H + h) * N + t] = lse[(b * H + h) * N + t] * kLog2e;
   }
 }
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
       if (tid < BQ) {
         const int t = tok(min(jq0 + tid, N - 1), sig);
         lse_r = lse_h[t];
-        dvec_r = dvec_h[t];
+        dvec_r = -dvec_h[t];
       }
     };
 
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
     }
   }
   const float lse_q = lse2[((size_t)b * H + h) * N + tq];
-  const float dvec_q = dvec[((size_t)b * H + h) * N + tq];
+  const float dvec_q = -dvec[((size_t)b * H + h) * N + tq];
 
   const int k_dc = tid % (D / 8), k_kg = tid / (D / 8);
   v8<T> kr[KRPT], vr[KRPT];
@@ -651,9 +652,16 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const char* Qs = lds + S::kQ + STG * S::kQTileB;
     const char* dOs = lds + S::kdO + STG * S::kQTileB;
     const char* Fs = lds + S::kF + STG * 2 * BQ * 4;
+    // dP accumulates onto -Dvec (stored negated), so it ends as dP - Dvec
     f32x16 sacc, pacc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; pacc[i] = 0.f; }
+    for (int u = 0; u < 2; ++u) {
+      const f32x4 n0 = lds_f32x4(Fs, BQ * 4 + offL + u * 64), n1 = lds_f32x4(Fs, BQ * 4 + offL + u * 64 + 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { pacc[u * 8 + i] = n0[i]; pacc[u * 8 + 4 + i] = n1[i]; }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
     for (int cc = 0; cc < S::kDC; ++cc) {
       mma32(sacc, lds_b128(Qs, offA[cc]), lds_b128(lds, offB[cc]));
@@ -664,16 +672,14 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const f32x4 l0 = lds_f32x4(Fs, offL + u * 64), l1 = lds_f32x4(Fs, offL + u * 64 + 16);
-      const f32x4 d0 = lds_f32x4(Fs, BQ * 4 + offL + u * 64), d1 = lds_f32x4(Fs, BQ * 4 + offL + u * 64 + 16);
       f32x8 pv, sv;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float lq = i < 4 ? l0[i] : l1[i - 4];
-        const float dq = i < 4 ? d0[i] : d1[i - 4];
         float p = fast_exp2(fmaf(sacc[u * 8 + i], c2, -lq));
         if (MASK && (jkey > jq_first + u * 16 + i || (EDGE && jq_first + u * 16 + i >= qge))) p = 0.f;
         pv[i] = p;
-        sv[i] = p * (pacc[u * 8 + i] - dq);
+        sv[i] = p * pacc[u * 8 + i];
       }
       const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
       const bf16x8 sf = __builtin_convertvector(sv, bf16x8);
@@ -855,12 +861,12 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     dvec_q = sum_halves(part);
     lse_q = lse[rix] * kLog2e;
     if (hf == 0 && q_ok) {
-      dvec[rix] = dvec_q;
+      dvec[rix] = -dvec_q;
       lse2[rix] = lse_q;
     }
   } else {
     lse_q = lse2[rix];
-    dvec_q = dvec[rix];
+    dvec_q = -dvec[rix];
   }
 
   // K and V of this (batch, KV head) as buffers (32-bit byte offsets, which
