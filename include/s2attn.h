@@ -113,7 +113,7 @@ int s2attn_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace s2attn_bwd needs: the fp32 row sums
- * Dvec = rowsum(dO * o) [B,H,N] and lse * log2(e) [B,H,N].
+ * -Dvec = -rowsum(dO * o) [B,H,N] (stored negated) and lse * log2(e) [B,H,N].
  * Returns 0 when the arguments would be rejected by s2attn_bwd, and for an
  * empty problem (B == 0 or N == 0), which needs no workspace.
  */
@@ -143,7 +143,7 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * The gradients are those of the causal softmax attention of "The shifting
  * mechanism" / Algorithm 1 (page section 3.4) in every group of every head's
  * rolled frame: P = exp(scale q k^T - lse), dS = P * (dO v^T - Dvec),
- *   prep : Dvec[b,h,t] = sum_c dO[b,t,h,c] * o[b,t,h,c] and lse * log2(e)
+ *   prep : -Dvec[b,h,t] = -sum_c dO[b,t,h,c] * o[b,t,h,c] and lse * log2(e)
  *          (fp32) into the workspace;
  *   dkdv : dv = P^T dO and dk = scale dS^T q, summed over the query heads
  *          that share a key/value head;
