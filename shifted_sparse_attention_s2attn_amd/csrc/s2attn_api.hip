@@ -1,7 +1,6 @@
 // C ABI of libs2attn: host-side validation, workspace sizing and launch.
 // Every check runs on the host before any HIP call, so a rejected call
-// launches nothing.  The library keeps no state besides one flag per kernel
-// instantiation recording that its LDS limit was raised.
+// launches nothing.  The library keeps no state.
 #include "s2attn.h"
 
 #include <math.h>
@@ -47,6 +46,9 @@ int check_problem(int B, int H, int Hkv, int N, int d, int G, int shift_heads, i
   // one-dimensional grids of (batch, head, group, 128-row tile) blocks
   const size_t blocks = (size_t)B * H * (size_t)((N + G - 1) / G) * (size_t)((G + kTileRows - 1) / kTileRows);
   if (blocks > (size_t)INT32_MAX) return S2ATTN_ERR_UNSUPPORTED;
+  // the bf16 kernels address a 64-row tile with 32-bit byte offsets from its
+  // first row: 64 rows of q (H * d elements each, the widest tensor) < 2^31 bytes
+  if ((size_t)H * (size_t)d >= ((size_t)1 << 24)) return S2ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return S2ATTN_ERR_UNSUPPORTED;
   if (dtype != S2ATTN_BF16 && dtype != S2ATTN_F32) return S2ATTN_ERR_UNSUPPORTED;
   const int r = H / Hkv;
@@ -308,7 +310,7 @@ const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_OK: return "ok";
     case S2ATTN_ERR_NULL: return "a required pointer is NULL";
     case S2ATTN_ERR_SHAPE: return "invalid shape (a size < 0, H, Hkv, d or G <= 0, G > N, shift_heads outside [0,H], or H % Hkv != 0)";
-    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split, swap or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, grid too large, or a rotary scale, base or direction out of range)";
+    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split, swap or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, grid too large, H * d >= 2^24, or a rotary scale, base or direction out of range)";
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     case S2ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (element tensors need 16 bytes, lse 4)";

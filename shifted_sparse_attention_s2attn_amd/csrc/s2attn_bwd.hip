@@ -22,10 +22,10 @@
 //          tiles of the group up to the diagonal, recomputing S and dP (queries
 //          on lanes), so dS feeds dQ^T = K^T dS^T straight from registers.
 // dS is kept without the softmax scale; dK and dQ take it at their stores.
-// Each stage has a generic kernel (any element type, register-staged LDS
-// tiles; used for fp32 and for bf16 batch slices over 2 GiB) and a bf16 kernel
-// laid out for the bf16 matrix cores (direct-to-LDS tile loads, transposing LDS
-// reads), with a separate instantiation for groups that are not whole tiles.
+// Each stage has an fp32 kernel (register-staged LDS tiles, fp32 matrix cores)
+// and a bf16 kernel laid out for the bf16 matrix cores (direct-to-LDS tile
+// loads, transposing LDS reads), which serves bf16 inputs of every size, with
+// a separate instantiation for groups that are not whole tiles.
 #include "s2attn_common.h"
 
 #include <type_traits>
@@ -78,7 +78,8 @@ __device__ __forceinline__ void store_transposed(v8<T>* tile, const v8<T>* regs,
 }
 
 // ===========================================================================
-// dkdv, generic.  Also takes groups that are not whole tiles: key rows past
+// dkdv, fp32 ("generic": written for any element type, instantiated for
+// fp32 only).  Also takes groups that are not whole tiles: key rows past
 // the group compute on a copy of its last row and are not stored; query rows of
 // the next group in the last query tile are masked; rows past N are clamped.
 // ===========================================================================
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   using S = DkdvShape<T, D>;
   constexpr int BKV = S::kBKV, BQ = S::kBQ, NQS = S::kNQS;
   constexpr int QCPR = S::kQCPR, TCPR = S::kTCPR, QRPT = S::kQRowsPerThread;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ __align__(16) unsigned char smem_raw[S::kLdsBytes];
   v8<T>* smem = reinterpret_cast<v8<T>*>(smem_raw);
   v8<T>* Qs = smem + S::kQs;
   v8<T>* dOs = smem + S::kdOs;
@@ -267,7 +268,8 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
 }
 
 // ===========================================================================
-// dq, generic.  Groups that are not whole tiles as in the generic forward.
+// dq, fp32 ("generic", as above).  Groups that are not whole tiles as in the
+// fp32 forward.
 // ===========================================================================
 template <typename T, int D>
 struct DqShape {
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
     int N, int H, int Hkv, int G, int shift_heads, int wrap, float scale) {
   using S = DqShape<T, D>;
   constexpr int BR = S::kBR, BC = S::kBC, KCPR = S::kKCPR, TCPR = S::kTCPR, KRPT = S::kKRowsPerThread;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ __align__(16) unsigned char smem_raw[S::kLdsBytes];
   v8<T>* smem = reinterpret_cast<v8<T>*>(smem_raw);
   v8<T>* Ks = smem + S::kKs;
   v8<T>* Vs = smem + S::kVs;
@@ -534,12 +536,14 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     load_lds16(kb + g, lds + S::kK + cb * 16);
     load_lds16(vb + g, lds + S::kV + cb * 16);
   }
-  // Q, dO (this batch) and lse*log2(e), Dvec as buffers: 32-bit byte offsets
-  // (the launcher checks that they fit), per-lane parts fixed here
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(const_cast<bf16*>(q + (size_t)b * N * qstride), (int)((size_t)N * qstride * 2));
-  const __amdgpu_buffer_rsrc_t dors = make_rsrc(const_cast<bf16*>(dO + (size_t)b * N * qstride), (int)((size_t)N * qstride * 2));
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(const_cast<float*>(lse2 + (size_t)b * H * N), H * N * 4);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(const_cast<float*>(dvec + (size_t)b * H * N), H * N * 4);
+  // Q, dO of this batch and lse*log2(e), Dvec of its heads; a query tile is
+  // loaded through buffers based at its first row, with the per-lane byte
+  // offsets inside the tile fixed here (the host bounds 64 rows of Q below
+  // 2^31 bytes)
+  const bf16* qbb = q + (size_t)b * N * qstride;
+  const bf16* dobb = dO + (size_t)b * N * qstride;
+  const float* lbb = lse2 + (size_t)b * H * N;
+  const float* dbb = dvec + (size_t)b * H * N;
   int qoff[S::kQLoads];
 #pragma unroll
   for (int i = 0; i < S::kQLoads; ++i) {
@@ -614,28 +618,30 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
       for (int i = 0; i < S::kQLoads; ++i) {
         const int p = (wave + S::kWaves * i) * 64 + lane;
         const int row = p / CPR, pc = p % CPR;
-        const int tok = token_of_row<SWAP>(min(qt * BQ + row, N - 1), sig, N, G);
-        const int off = (tok * (int)qstride + h * D + (pc ^ swz2<CPR>(row)) * 8) * 2;
+        const size_t tok = token_of_row<SWAP>(min(qt * BQ + row, N - 1), sig, N, G);
+        const size_t off = tok * qstride + (size_t)h * D + (pc ^ swz2<CPR>(row)) * 8;
         const int cb = (wave + S::kWaves * i) * 64 * 16;
-        buffer_load_lds16(qrs, off, 0, lds + S::kQ + stage * S::kQTileB + cb);
-        buffer_load_lds16(dors, off, 0, lds + S::kdO + stage * S::kQTileB + cb);
+        load_lds16(qbb + off, lds + S::kQ + stage * S::kQTileB + cb);
+        load_lds16(dobb + off, lds + S::kdO + stage * S::kQTileB + cb);
       }
-      const int loff = (h * N + token_of_row<SWAP>(min(qt * BQ + lane, N - 1), sig, N, G)) * 4;
-      if (wave == 0) buffer_load_lds4(lrs, loff, 0, lds + S::kF + stage * 2 * BQ * 4);
-      if (wave == 1) buffer_load_lds4(drs, loff, 0, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
+      const size_t loff = (size_t)h * N + token_of_row<SWAP>(min(qt * BQ + lane, N - 1), sig, N, G);
+      if (wave == 0) load_lds4(lbb + loff, lds + S::kF + stage * 2 * BQ * 4);
+      if (wave == 1) load_lds4(dbb + loff, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
       return;
     }
-    const int t0 = token_of_row<SWAP>(qt * BQ, sig, N, G);   // a 64-row tile is contiguous
-    const int soff = (t0 * (int)qstride + h * D) * 2;
+    const size_t t0 = token_of_row<SWAP>(qt * BQ, sig, N, G);   // a 64-row tile is contiguous
+    const size_t qo = t0 * qstride + (size_t)h * D;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(const_cast<bf16*>(qbb + qo), BQ * (int)qstride * 2);
+    const __amdgpu_buffer_rsrc_t dors = make_rsrc(const_cast<bf16*>(dobb + qo), BQ * (int)qstride * 2);
 #pragma unroll
     for (int i = 0; i < S::kQLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
-      buffer_load_lds16(qrs, qoff[i], soff, lds + S::kQ + stage * S::kQTileB + cb);
-      buffer_load_lds16(dors, qoff[i], soff, lds + S::kdO + stage * S::kQTileB + cb);
+      buffer_load_lds16(qrs, qoff[i], 0, lds + S::kQ + stage * S::kQTileB + cb);
+      buffer_load_lds16(dors, qoff[i], 0, lds + S::kdO + stage * S::kQTileB + cb);
     }
-    const int loff = (h * N + t0) * 4;
-    if (wave == 0) buffer_load_lds4(lrs, lane * 4, loff, lds + S::kF + stage * 2 * BQ * 4);
-    if (wave == 1) buffer_load_lds4(drs, lane * 4, loff, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
+    const size_t lo = (size_t)h * N + t0;
+    if (wave == 0) buffer_load_lds4(make_rsrc(const_cast<float*>(lbb + lo), BQ * 4), lane * 4, 0, lds + S::kF + stage * 2 * BQ * 4);
+    if (wave == 1) buffer_load_lds4(make_rsrc(const_cast<float*>(dbb + lo), BQ * 4), lane * 4, 0, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
   };
 
   f32x16 dkacc[S::kDT], dvacc[S::kDT];
@@ -869,11 +875,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     dvec_q = -dvec[rix];
   }
 
-  // K and V of this (batch, KV head) as buffers (32-bit byte offsets, which
-  // the launcher checks); per-lane byte offsets of the chunks this lane moves
-  const int kvbytes = (int)(((size_t)N * kvstride - (size_t)c * D) * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(const_cast<bf16*>(kb), kvbytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(const_cast<bf16*>(vb), kvbytes);
+  // Per-lane byte offsets, inside a 64-row tile, of the chunks this lane moves
+  // (the host bounds 64 rows of K / V below 2^31 bytes)
   int toff[S::kLoads];
 #pragma unroll
   for (int i = 0; i < S::kLoads; ++i) {
@@ -885,26 +888,29 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     char* kd = kbuf(stage);
     char* vd = vbuf(stage);
     // EDGE: a tile whose rows wrap from token N-1 to token 0, or run past row
-    // N, takes each row's own address (rows past N read row N-1: masked keys)
+    // N, takes each row's own 64-bit address (rows past N read row N-1: masked keys)
     if (EDGE && (kt0 + BC > N || (sigma != 0 && kt0 < N - sigma && kt0 + BC > N - sigma))) {
 #pragma unroll
       for (int i = 0; i < S::kLoads; ++i) {
         const int p = (wave + S::kWaves * i) * 64 + lane;
         const int row = p / CPR, pc = p % CPR;
-        const int tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, G);
+        const size_t tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, G);
         const int cb = (wave + S::kWaves * i) * 64 * 16;
-        const int off = (tok * (int)kvstride + (pc ^ swz2<CPR>(row)) * 8) * 2;
-        buffer_load_lds16(krs, off, 0, kd + cb);
-        buffer_load_lds16(vrs, off, 0, vd + cb);
+        const size_t off = tok * kvstride + (pc ^ swz2<CPR>(row)) * 8;
+        load_lds16(kb + off, kd + cb);
+        load_lds16(vb + off, vd + cb);
       }
       return;
     }
-    const int t0 = token_of_row<SWAP>(kt0, sigma, N, G) * (int)kvstride * 2;   // whole tile is contiguous
+    // a whole tile is contiguous: buffers based at its first row
+    const size_t t0 = token_of_row<SWAP>(kt0, sigma, N, G);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(const_cast<bf16*>(kb + t0 * kvstride), BC * (int)kvstride * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(const_cast<bf16*>(vb + t0 * kvstride), BC * (int)kvstride * 2);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
-      buffer_load_lds16(krs, toff[i], t0, kd + cb);
-      buffer_load_lds16(vrs, toff[i], t0, vd + cb);
+      buffer_load_lds16(krs, toff[i], 0, kd + cb);
+      buffer_load_lds16(vrs, toff[i], 0, vd + cb);
     }
   };
 
@@ -1003,15 +1009,6 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
 // ===========================================================================
 // launchers
 // ===========================================================================
-template <typename K>
-hipError_t raise_lds_limit(K kernel, size_t bytes, bool& done) {
-  if (done) return hipSuccess;   // idempotent; a race only repeats the call
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done = true;
-  return e;
-}
-
 template <typename T, int D>
 hipError_t launch_bwd_prep(const void* o, const void* dO, const float* lse, float* dvec, float* lse2,
                            int B, int H, int N, hipStream_t stream) {
@@ -1052,11 +1049,8 @@ hipError_t launch_dkdv_generic(const void* q, const void* k, const void* v, cons
                                const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
                                int shift_heads, int wrap, float scale, hipStream_t stream) {
   using S = DkdvShape<T, D>;
-  static bool attr = false;
-  hipError_t e = raise_lds_limit(&s2attn_bwd_dkdv<T, D>, S::kLdsBytes, attr);
-  if (e != hipSuccess) return e;
   const dim3 grid(B * Hkv * ((N + G - 1) / G) * ((G + S::kBKV - 1) / S::kBKV));
-  hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), grid, dim3(S::kThreads), S::kLdsBytes,
+  hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), grid, dim3(S::kThreads), 0,
                      stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dk, (T*)dv, N,
                      H, Hkv, G, shift_heads, wrap, scale);
   return hipGetLastError();
@@ -1067,12 +1061,11 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
                            int shift_heads, int wrap, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
-  if constexpr (sizeof(T) == 2) {
-    // the fast kernel addresses one batch's Q / dO with 31-bit byte offsets
-    if ((size_t)N * H * D * sizeof(T) < (size_t(1) << 31))
-      return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
-  }
-  return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
+  if constexpr (std::is_same_v<T, bf16>)
+    return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
+  else
+    return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale,
+                                     stream);
 }
 
 // o and lse non-NULL: prep fused in (writes lse2 and dvec); else reads them.
@@ -1109,21 +1102,11 @@ hipError_t launch_dq_generic(const void* q, const void* k, const void* v, const 
                              const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
                              int wrap, float scale, hipStream_t stream) {
   using S = DqShape<T, D>;
-  static bool attr = false;
-  hipError_t e = raise_lds_limit(&s2attn_bwd_dq<T, D>, S::kLdsBytes, attr);
-  if (e != hipSuccess) return e;
   const dim3 grid(B * H * ((N + G - 1) / G) * ((G + S::kBR - 1) / S::kBR));
-  hipLaunchKernelGGL((s2attn_bwd_dq<T, D>), grid, dim3(S::kThreads), S::kLdsBytes, stream,
+  hipLaunchKernelGGL((s2attn_bwd_dq<T, D>), grid, dim3(S::kThreads), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dq, N, H, Hkv, G,
                      shift_heads, wrap, scale);
   return hipGetLastError();
-}
-
-// the fast dq kernel addresses one batch's K / V with 31-bit byte offsets
-template <typename T, int D>
-bool dq_fast(int N, int Hkv, int G) {
-  (void)G;
-  return sizeof(T) == 2 && (size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31);
 }
 
 template <typename T, int D>
@@ -1131,27 +1114,27 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* dvec, void* dq, int B, int H, int Hkv, int N, int G, int shift_heads,
                          int wrap, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
-  if constexpr (sizeof(T) == 2) {
-    if (dq_fast<T, D>(N, Hkv, G))
-      return launch_dq_bf16<D>(q, k, v, dO, nullptr, nullptr, const_cast<float*>(lse2), const_cast<float*>(dvec),
-                               dq, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
-  }
-  return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
+  if constexpr (std::is_same_v<T, bf16>)
+    return launch_dq_bf16<D>(q, k, v, dO, nullptr, nullptr, const_cast<float*>(lse2), const_cast<float*>(dvec),
+                             dq, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
+  else
+    return launch_dq_generic<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
 }
 
-// prep and dq in one launch where the fast dq kernel runs, else one after the other
+// prep and dq: one launch for bf16 (prep fused into the dq kernel), prep then
+// dq for fp32
 template <typename T, int D>
 hipError_t launch_bwd_prep_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
                               const void* dO, float* lse2, float* dvec, void* dq, int B, int H, int Hkv, int N,
                               int G, int shift_heads, int wrap, hipStream_t stream) {
-  if constexpr (sizeof(T) == 2) {
-    if (dq_fast<T, D>(N, Hkv, G))
-      return launch_dq_bf16<D>(q, k, v, dO, o, lse, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap,
-                               1.0f / sqrtf((float)D), stream);
+  if constexpr (std::is_same_v<T, bf16>) {
+    return launch_dq_bf16<D>(q, k, v, dO, o, lse, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap,
+                             1.0f / sqrtf((float)D), stream);
+  } else {
+    const hipError_t e = launch_bwd_prep<T, D>(o, dO, lse, dvec, lse2, B, H, N, stream);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dq<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap, stream);
   }
-  const hipError_t e = launch_bwd_prep<T, D>(o, dO, lse, dvec, lse2, B, H, N, stream);
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap, stream);
 }
 
 #define S2A_INST_BWD(T, D)                                                                                 \

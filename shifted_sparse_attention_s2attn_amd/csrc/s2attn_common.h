@@ -171,11 +171,18 @@ __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// The same with 4 bytes per lane.
+__device__ __forceinline__ void load_lds4(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 // Raw buffer resource over [base, base + nbytes): loads through it take a
 // 32-bit byte offset, per lane (voff) plus wave-uniform (soff, a scalar
-// register); offsets past nbytes read zeros.
+// register); offsets past nbytes read zeros.  The kernels base one at the
+// first row of each tile they load (a 64-bit scalar address), so that no
+// offset grows with the sequence length or the batch.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, int nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
 }

@@ -22,7 +22,7 @@
 //     its 32 keys split across lanes l and l ^ 32)
 //     O^T += V^T P^T     (P^T comes straight from the S^T registers)
 // Finally O = O^T / l is stored at the original rows with lse = m + ln l.
-// This kernel (fp32, and bf16 slices over 2 GiB) also takes groups that are not
+// This kernel (fp32 inputs: fp32 matrix cores) also takes groups that are not
 // whole tiles (a short last group when G does not divide N, or any G): query
 // rows past the group compute on a copy of its last row and are not stored, key
 // rows past it (the next group, or past N, clamped to a real row) follow every
@@ -325,11 +325,8 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     for (int cc = 0; cc < S::kDC; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(qrow + cc * 16 + hf * 8);
   }
 
-  // K and V of this (batch, KV head) as buffers (32-bit byte offsets, which
-  // the launcher checks); per-lane byte offsets of the chunks this lane moves
-  const int kvbytes = (int)(((size_t)N * kvstride - (size_t)c * D) * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(const_cast<bf16*>(kb), kvbytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(const_cast<bf16*>(vb), kvbytes);
+  // Per-lane byte offsets, inside a 64-row tile, of the chunks this lane moves
+  // (the host bounds 64 rows of K / V below 2^31 bytes)
   int koff[S::kLoads], voff[S::kLoads];
 #pragma unroll
   for (int i = 0; i < S::kLoads; ++i) {
@@ -342,25 +339,28 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     char* kd = kbuf(stage);
     char* vd = vbuf(stage);
     // EDGE: a tile whose rows wrap from token N-1 to token 0, or run past row
-    // N, takes each row's own address (rows past N read row N-1: masked keys)
+    // N, takes each row's own 64-bit address (rows past N read row N-1: masked keys)
     if (EDGE && (kt0 + BC > N || (sigma != 0 && kt0 < N - sigma && kt0 + BC > N - sigma))) {
 #pragma unroll
       for (int i = 0; i < S::kLoads; ++i) {
         const int p = (wave + S::kWaves * i) * 64 + lane;
         const int row = p / CPR, pc = p % CPR;
-        const int tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, G);
+        const size_t tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, G);
         const int cb = (wave + S::kWaves * i) * 64 * 16;
-        buffer_load_lds16(krs, (tok * (int)kvstride + (pc ^ swz_k<CPR>(row)) * 8) * 2, 0, kd + cb);
-        buffer_load_lds16(vrs, (tok * (int)kvstride + (pc ^ swz_v<CPR>(row)) * 8) * 2, 0, vd + cb);
+        load_lds16(kb + tok * kvstride + (pc ^ swz_k<CPR>(row)) * 8, kd + cb);
+        load_lds16(vb + tok * kvstride + (pc ^ swz_v<CPR>(row)) * 8, vd + cb);
       }
       return;
     }
-    const int t0 = token_of_row<SWAP>(kt0, sigma, N, G) * (int)kvstride * 2;   // whole tile is contiguous
+    // a whole tile is contiguous: buffers based at its first row
+    const size_t t0 = token_of_row<SWAP>(kt0, sigma, N, G);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(const_cast<bf16*>(kb + t0 * kvstride), BC * (int)kvstride * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(const_cast<bf16*>(vb + t0 * kvstride), BC * (int)kvstride * 2);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int cb = (wave + S::kWaves * i) * 64 * 16;
-      buffer_load_lds16(krs, koff[i], t0, kd + cb);
-      buffer_load_lds16(vrs, voff[i], t0, vd + cb);
+      buffer_load_lds16(krs, koff[i], 0, kd + cb);
+      buffer_load_lds16(vrs, voff[i], 0, vd + cb);
     }
   };
 
@@ -506,20 +506,20 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   return hipGetLastError();
 }
 
+// bf16: the kernel above at every size; fp32: the fp32 kernel.
 template <typename T, int D>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int Hkv, int N, int G, int shift_heads, int wrap, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
-  if constexpr (sizeof(T) == 2) {
-    // the fast kernel addresses one batch's K / V with 31-bit byte offsets
-    if ((size_t)N * Hkv * D * sizeof(T) < (size_t(1) << 31))
-      return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
+  if constexpr (std::is_same_v<T, bf16>) {
+    return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
+  } else {
+    constexpr int BR = FwdShape<T, D>::kBR;
+    dim3 grid(B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
+    hipLaunchKernelGGL((s2attn_fwd_kernel<T, D>), grid, dim3(256), 0, stream,
+                       (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, wrap, scale);
+    return hipGetLastError();
   }
-  constexpr int BR = FwdShape<T, D>::kBR;
-  dim3 grid(B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
-  hipLaunchKernelGGL((s2attn_fwd_kernel<T, D>), grid, dim3(256), 0, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, H, Hkv, G, shift_heads, wrap, scale);
-  return hipGetLastError();
 }
 
 template hipError_t launch_fwd<bf16, 64>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, int, hipStream_t);

@@ -101,8 +101,15 @@ def test_grid_size_limit(lib):
     assert fwd_status(lib, B=1 << 20, H=1 << 10, Hkv=1 << 10, S=0, N=256) == _lib.S2ATTN_ERR_UNSUPPORTED
 
 
+def test_row_width_limit(lib):
+    """A 64-row tile is addressed with 32-bit byte offsets from its first row, so
+    one token row of q (H * d elements) must stay below 2^24 elements."""
+    assert fwd_status(lib, ptrs=False, B=1, H=1 << 17, Hkv=1, S=0, d=128, N=256) == _lib.S2ATTN_ERR_UNSUPPORTED
+    assert fwd_status(lib, ptrs=False, B=1, H=(1 << 17) - 1, Hkv=1, S=0, d=128, N=256) == _lib.S2ATTN_ERR_NULL
+
+
 def test_unaligned_group_sizes_pass_validation(lib):
-    """G need not divide N, nor be a multiple of 128 (generic kernels): only the
+    """G need not divide N, nor be a multiple of 128 (EDGE instantiations): only the
     pointers are left to reject (NULL here)."""
     for kw in (dict(N=500), dict(G=129, N=129 * 4), dict(G=64, N=512), dict(G=1365, N=8192), dict(G=1, N=7),
                dict(G=512, N=512)):

@@ -301,10 +301,10 @@ def test_full_size_table7_sixth_group():
 
 
 def test_slice_over_2gib():
-    """One batch's q / dO slice over 2 GiB (B=1, H=64, d=128, N=131072): the
-    dK/dV stage leaves its 32-bit-offset fast kernel for the generic one, the
-    forward and dQ keep theirs (their buffers are the smaller K / V).  Sampled
-    as the other full-size workloads: a shifted and an unshifted KV head."""
+    """One batch's q / dO slice of 2 GiB (B=1, H=64, d=128, N=131072): the
+    dK/dV kernel reads query tiles 2 GiB into the slice, through buffers based
+    at each tile.  Sampled as the other full-size workloads: a shifted and an
+    unshifted KV head."""
     w = small_workload("gqa-131k", B=1, H=64, Hkv=8, d=128, N=131072, G=8192, shift_heads=32)
     assert w.N * w.H * w.d * 2 >= 2 ** 31
     say(f"case {w} (generating inputs on the GPU)")
@@ -313,6 +313,24 @@ def test_slice_over_2gib():
     say("  kernels done; global checks")
     check_global(w, t, out)
     for c, g0 in [(7, 15), (0, 3)]:
+        check_sampled(w, t, out, c, g0)
+
+
+def test_kv_slice_over_2gib():
+    """K / V slices of 2.5 GiB per batch (B=1, H=Hkv=32, d=128, N=327680,
+    G=8192): the forward and dQ kernels read key tiles past byte offset 2^31 of
+    the slice (every tensor is 2.5 GiB, 20 GiB in all), with the same kernels as
+    every other bf16 size.  Sampled: the wrap group of a shifted head, which
+    reads the last and the first tokens, and an unshifted group wholly past
+    2 GiB (tokens 286720..294911)."""
+    w = small_workload("mha-320k", B=1, H=32, Hkv=32, d=128, N=327680, G=8192, shift_heads=16)
+    assert 286720 * w.Hkv * w.d * 2 >= 2 ** 31
+    say(f"case {w} (generating inputs on the GPU)")
+    t = make_inputs(w, seed=0, device="cuda")
+    out = run_gpu(w, t)
+    say("  kernels done; global checks")
+    check_global(w, t, out)
+    for c, g0 in [(31, 39), (0, 35)]:
         check_sampled(w, t, out, c, g0)
 
 
