@@ -74,7 +74,8 @@ typedef enum {
                                     split / swap rule above, or the grid or H * d size limit */
     S2ATTN_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError) */
     S2ATTN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
-    S2ATTN_ERR_ALIGN = 6         /* an element tensor pointer not 16-byte aligned, or lse not 4-byte */
+    S2ATTN_ERR_ALIGN = 6,        /* an element tensor pointer not 16-byte aligned, or lse not 4-byte */
+    S2ATTN_ERR_SCRATCH = 7       /* s2attn_bwd_noalloc: B * H * N above S2ATTN_NOALLOC_MAX_ROWS */
 } s2attn_status;
 
 /*
@@ -197,6 +198,29 @@ int s2attn_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO
                      void* dq, void* workspace, size_t workspace_bytes,
                      int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
                      int dtype, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the backward
+ * of s2attn_bwd_ex without a caller workspace.  Its scratch (the fp32 -Dvec
+ * and lse * log2(e) rows, 8 bytes per query row) lives in a device array of
+ * the library, S2ATTN_NOALLOC_MAX_ROWS rows (32 MiB) on every GPU the call runs
+ * on, held until the process ends; its address is looked up once per device
+ * (the device current at the call) and the call allocates nothing.  Same
+ * arguments, checks and results as s2attn_bwd_ex, bit for bit; B * H * N above
+ * S2ATTN_NOALLOC_MAX_ROWS returns S2ATTN_ERR_SCRATCH (after the size checks,
+ * before the pointer checks and any HIP call).  The scratch needs no clearing:
+ * the backward's first stage writes every row its second stage reads.  Every
+ * call on one GPU shares that GPU's scratch: calls whose kernels can overlap
+ * on one GPU (other streams, other host threads) race and must be serialised
+ * by the caller.  S2ATTN_ERR_HIP also reports a failed lookup of the scratch.
+ */
+#define S2ATTN_NOALLOC_MAX_ROWS (1 << 22)
+int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dO,
+                       void* dq, void* dk, void* dv,
+                       int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                       int dtype, void* stream);
 
 /*
  * Rotary position embedding with Position Interpolation, the step before the

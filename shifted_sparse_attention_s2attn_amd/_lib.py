@@ -17,6 +17,8 @@ S2ATTN_ERR_UNSUPPORTED = 3
 S2ATTN_ERR_HIP = 4
 S2ATTN_ERR_WORKSPACE = 5
 S2ATTN_ERR_ALIGN = 6
+S2ATTN_ERR_SCRATCH = 7
+S2ATTN_NOALLOC_MAX_ROWS = 1 << 22
 S2ATTN_BF16 = 0
 S2ATTN_F32 = 1
 S2ATTN_WRAP_ROLL = 0
@@ -26,7 +28,7 @@ WRAPS = {"roll": S2ATTN_WRAP_ROLL, "split": S2ATTN_WRAP_SPLIT, "swap": S2ATTN_WR
 
 EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes", "s2attn_bwd_prep", "s2attn_bwd_dkdv",
            "s2attn_bwd_dq", "s2attn_bwd_prep_dq", "s2attn_fwd_ex", "s2attn_bwd_ex", "s2attn_bwd_dkdv_ex",
-           "s2attn_bwd_dq_ex", "s2attn_rope", "s2attn_status_str")
+           "s2attn_bwd_dq_ex", "s2attn_bwd_noalloc", "s2attn_rope", "s2attn_status_str")
 
 _lib = None
 
@@ -65,6 +67,8 @@ def load():
     lib.s2attn_bwd_dq_ex.restype = i
     lib.s2attn_bwd_prep_dq.argtypes = [vp, vp, vp, vp, fp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, i, vp]
     lib.s2attn_bwd_prep_dq.restype = i
+    lib.s2attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, fp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
+    lib.s2attn_bwd_noalloc.restype = i
     dbl = ctypes.c_double
     lib.s2attn_rope.argtypes = [vp, vp, i, i, i, i, dbl, dbl, i, i, vp]
     lib.s2attn_rope.restype = i

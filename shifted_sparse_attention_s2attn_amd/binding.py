@@ -11,7 +11,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["S2AttnError", "s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes",
+__all__ = ["S2AttnError", "s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes", "s2attn_bwd_noalloc",
            "s2attn_bwd_prep", "s2attn_bwd_dkdv", "s2attn_bwd_dq", "s2attn_bwd_prep_dq",
            "s2attn_status_str", "S2Attn", "s2attn", "s2attn_rope", "RoPE", "rope"]
 
@@ -135,6 +135,22 @@ def s2attn_bwd(q, k, v, o, lse, do, G, shift_heads=None, workspace=None, stream=
     if st != _lib.S2ATTN_OK:
         raise S2AttnError(st, "s2attn_bwd")
     return dq, dk, dv
+
+
+def s2attn_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, G, shift_heads=None, stream=None, wrap="roll"):
+    """The backward of s2attn_bwd into caller-given dq, dk, dv, with no
+    workspace: the library's own per-device scratch array holds the row sums
+    (B * H * N <= S2ATTN_NOALLOC_MAX_ROWS), so the call allocates nothing.
+    Calls that can overlap on one GPU race on that scratch."""
+    _check_tensors(q, k, v, (("o", o, None, None), ("lse", lse, _lse_shape(q), torch.float32),
+                             ("do", do, None, None), ("dq", dq, None, None), ("dk", dk, k.shape, None),
+                             ("dv", dv, k.shape, None)))
+    B, H, Hkv, N, d, S = _dims(q, k, shift_heads)
+    with torch.cuda.device(q.device):
+        _check(_lib.load().s2attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), _ptr(do),
+                                              _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, G, S,
+                                              _wrap_code(wrap), _dtype_code(q), _stream(stream)),
+               "s2attn_bwd_noalloc")
 
 
 def _dims(q, k, shift_heads):

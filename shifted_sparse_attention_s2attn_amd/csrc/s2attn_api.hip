@@ -1,10 +1,13 @@
 // C ABI of libs2attn: host-side validation, workspace sizing and launch.
 // Every check runs on the host before any HIP call, so a rejected call
-// launches nothing.  The library keeps no state.
+// launches nothing.  The library keeps no state, apart from the per-device
+// address of the scratch array of s2attn_bwd_noalloc (at the end of this file).
 #include "s2attn.h"
 
 #include <math.h>
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 #include <stdint.h>
 #include "s2attn_common.h"
 
@@ -285,6 +288,66 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
                        shift_heads, S2ATTN_WRAP_ROLL, dtype, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// s2attn_bwd_noalloc: the backward's scratch in a file-scope device array.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up per device with hipGetSymbolAddress and only
+// that address is passed to kernels.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = 2 * (size_t)S2ATTN_NOALLOC_MAX_ROWS * sizeof(float);   // -Dvec | lse*log2(e)
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (the current device), looked
+// up once per device; NULL if the lookup failed.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(scratch_once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) scratch_ptr[dev].store(p);
+  });
+  return scratch_ptr[dev].load();
+}
+
+}  // namespace
+
+extern "C" {
+
+int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                       void* dq, void* dk, void* dv,
+                       int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap, int dtype,
+                       void* stream) {
+  int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st == S2ATTN_OK) st = check_wrap(wrap, N, G);
+  if (st != S2ATTN_OK) return st;
+  const size_t rows = (size_t)B * H * N;
+  if (rows > (size_t)S2ATTN_NOALLOC_MAX_ROWS) return S2ATTN_ERR_SCRATCH;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
+  if (misaligned16({q, k, v, o, dO, dq, dk, dv}) || misaligned4(lse)) return S2ATTN_ERR_ALIGN;
+  void* base = scratch_address();
+  if (!base) return S2ATTN_ERR_HIP;
+  // the workspace layout of s2attn_bwd_ex, inside the scratch array
+  const size_t need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (need > kScratchBytes) return S2ATTN_ERR_SCRATCH;
+  Workspace ws;
+  st = check_workspace(base, need, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
+  if (st != S2ATTN_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = dispatch<PrepDq>(dtype, d, q, k, v, o, lse, dO, dq, ws, B, H, Hkv, N, G, shift_heads, wrap, s);
+  if (e == hipSuccess)
+    e = dispatch<Dkdv>(dtype, d, q, k, v, dO, dk, dv, ws, B, H, Hkv, N, G, shift_heads, wrap, s);
+  return status_of(e);
+}
+
 int s2attn_rope(const void* x, void* y, int B, int N, int Hx, int d, double pos_scale, double base,
                 int inverse, int dtype, void* stream) {
   if (B < 0 || N < 0 || Hx <= 0 || d <= 0) return S2ATTN_ERR_SHAPE;
@@ -314,6 +377,7 @@ const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     case S2ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (element tensors need 16 bytes, lse 4)";
+    case S2ATTN_ERR_SCRATCH: return "B * H * N exceeds the rows of the library's scratch array (S2ATTN_NOALLOC_MAX_ROWS)";
     default: return "unknown status";
   }
 }

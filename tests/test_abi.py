@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert lib.s2attn_status_str(code)
     assert lib.s2attn_status_str(99) == b"unknown status"
 
@@ -99,6 +99,28 @@ def test_grid_size_limit(lib):
     large as long as B * H * N / 128 stays below 2^31."""
     assert lib.s2attn_bwd_workspace_bytes(70000, 1, 1, 128, 64, 128, 0, 0) == 70000 * 128 * 4 * 2
     assert fwd_status(lib, B=1 << 20, H=1 << 10, Hkv=1 << 10, S=0, N=256) == _lib.S2ATTN_ERR_UNSUPPORTED
+
+
+def test_noalloc_scratch_limit(lib):
+    """s2attn_bwd_noalloc keeps its row sums in a fixed device array of
+    S2ATTN_NOALLOC_MAX_ROWS rows: larger problems are rejected after the size
+    checks and before the pointers or any HIP call (NULL pointers here)."""
+    text = open(HEADER).read()
+    assert re.search(r"#define S2ATTN_NOALLOC_MAX_ROWS \(1 << 22\)", text)
+    assert _lib.S2ATTN_NOALLOC_MAX_ROWS == 1 << 22
+    rows = _lib.S2ATTN_NOALLOC_MAX_ROWS
+
+    def call(B, H, N, G=128, d=64, S=0, wrap=0):
+        return lib.s2attn_bwd_noalloc(*([None] * 9), B, H, H, N, d, G, S, wrap, 0, None)
+
+    assert call(1, 32, rows // 32) == _lib.S2ATTN_ERR_NULL                 # at the limit: only pointers left
+    assert call(1, 32, rows // 32 + 128) == _lib.S2ATTN_ERR_SCRATCH
+    assert call(2, 64, 32768) == _lib.S2ATTN_ERR_NULL                      # B * H * N = 2^22 exactly
+    assert call(2, 64, 32768 + 128) == _lib.S2ATTN_ERR_SCRATCH
+    assert call(1, 4, 512, G=1024) == _lib.S2ATTN_ERR_SHAPE                # size errors come first
+    assert call(1, 4, 512, wrap=5) == _lib.S2ATTN_ERR_UNSUPPORTED
+    assert call(0, 4, 512) == _lib.S2ATTN_OK                               # empty problem: a no-op
+    assert lib.s2attn_status_str(_lib.S2ATTN_ERR_SCRATCH).startswith(b"B * H * N exceeds")
 
 
 def test_row_width_limit(lib):
