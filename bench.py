@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the S2-Attn hot path on one MI355X: forward + backward per step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--range W1,W2,..]
 
 A step is one forward (s2attn_fwd) and one backward (its two launches, as
 s2attn_bwd runs them: prep fused into dQ, then dK/dV) over one batch of seeded
@@ -13,7 +13,9 @@ stream around every kernel launch give each kernel's average duration; the
 longest one is the roofline kernel.  Afterwards a vendor bf16 GEMM on
 standard-normal operands is timed as the practical matrix-core ceiling for
 data of this distribution, and the float64 CPU oracle is timed on a bounded
-sample of the same workload (rank 0, one GPU only).
+sample of the same workload (rank 0, one GPU only).  The other workloads of
+the metric's N range (8k, 100k, and the 70B GQA shape at 32k) are then timed
+for a few steps each and reported under "range" (outside the timed region).
 
 Prints one JSON line.
 """
@@ -161,6 +163,59 @@ def gemm_reference(torch, dev, n=16384, reps=5):
             "operands": "bf16, seeded standard normal", "library": "torch.matmul (hipBLASLt)"}
 
 
+def time_workload(torch, w, wrap, steps, warmup):
+    """Forward and backward of one more workload (the same launches as the timed
+    step), HIP events on the launch stream; per-kernel and per-pass averages."""
+    from shifted_sparse_attention_s2attn_amd import (s2attn_bwd_dkdv, s2attn_bwd_prep_dq,
+                                                     s2attn_bwd_workspace_bytes, s2attn_fwd)
+    from shifted_sparse_attention_s2attn_amd import flops as F
+    from shifted_sparse_attention_s2attn_amd.inputs import make_inputs
+    dev = torch.device("cuda:0")
+    t = make_inputs(w, seed=0, device="cuda")
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(s2attn_bwd_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.G, w.shift_heads, q.dtype),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        s2attn_fwd(q, k, v, w.G, w.shift_heads, out=o, lse=lse, wrap=wrap)
+        if ev:
+            ev[1].record(stream)
+        s2attn_bwd_prep_dq(q, k, v, o, lse, do, dq, ws, w.G, w.shift_heads, wrap=wrap)
+        if ev:
+            ev[2].record(stream)
+        s2attn_bwd_dkdv(q, k, v, do, dk, dv, ws, w.G, w.shift_heads, wrap=wrap)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms = [sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps for j in range(3)]
+    fwd_f = F.fwd_flops(w.B, w.H, w.N, w.G, w.d, w.shift_heads, wrap)
+    bwd_f = F.bwd_flops(w.B, w.H, w.N, w.G, w.d, w.shift_heads, wrap)
+    peak = F.MI355X_BF16_PEAK_TFLOPS if w.dtype == "bf16" else F.MI355X_F32_PEAK_TFLOPS
+    bwd_ms = ms[1] + ms[2]
+    del t, q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return {"N": w.N, "G": w.G, "H": w.H, "Hkv": w.Hkv, "steps": steps,
+            "ms_per_step": round(ms[0] + bwd_ms, 4),
+            "tflops": round((fwd_f + bwd_f) / (ms[0] + bwd_ms) / 1e9, 1),
+            "frac_of_peak": round((fwd_f + bwd_f) / (ms[0] + bwd_ms) / 1e9 / peak, 4),
+            "fwd": {"ms": round(ms[0], 4), "frac_of_peak": round(fwd_f / ms[0] / 1e9 / peak, 4)},
+            "bwd": {"ms": round(bwd_ms, 4), "frac_of_peak": round(bwd_f / bwd_ms / 1e9 / peak, 4),
+                    "prep_dq_ms": round(ms[1], 4), "dkdv_ms": round(ms[2], 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +227,10 @@ def main():
     ap.add_argument("--rope", action="store_true",
                     help="also time the rotary embedding with Position Interpolation on q and k (and its inverse "
                          "on dq and dk), the step before the attention; reported apart from the step")
+    ap.add_argument("--range", default="llama2-7b-8k,llama2-7b-100k,llama2-70b-gqa-32k",
+                    help="comma-separated workloads also timed (forward and backward only, a few steps each) and "
+                         "reported under \"range\", so the metric's whole N range is measured in one run; empty = none")
+    ap.add_argument("--range-steps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-reference", action="store_true")
@@ -194,6 +253,10 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    range_names = [n for n in args.range.split(",") if n and n != w.name]
+    for n in range_names:
+        if n not in WORKLOADS:
+            ap.error(f"unknown workload in --range: {n}")
     t = make_inputs(w, seed=0, device="cuda")
     q, k, v, do = t["q"], t["k"], t["v"], t["do"]
     o = torch.empty_like(q)
@@ -321,6 +384,10 @@ def main():
         result["gemm_reference"] = ref
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds, args.wrap)
+    if range_names:
+        del t, q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+        result["range"] = {n: time_workload(torch, WORKLOADS[n], args.wrap, args.range_steps, 3) for n in range_names}
     print(json.dumps(result), flush=True)
 
 

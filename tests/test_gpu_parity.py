@@ -210,11 +210,16 @@ def test_tiny_f32_workload(seed):
 # full-size workloads: sampled slices + global properties
 # ---------------------------------------------------------------------------
 
-SAMPLES = {   # (key/value head, group index in the frame of that KV head's first query head)
-    "llama2-7b-8k": [(0, 1), (31, 3)],
-    "llama2-7b-32k": [(0, 0), (31, 3)],
-    "llama2-7b-100k": [(5, 2), (31, 3)],
-    "llama2-70b-gqa-32k": [(0, 2), (7, 3)],
+# (key/value head, group index in the frame of that KV head's first query head).
+# The kernels number their blocks in chunks of 32 (batch, head, group) pairs
+# (4 groups per head here, so a chunk is 8 consecutive query heads): the MHA
+# workloads sample one slice in each of their 4 chunks, the GQA workload 5 of its
+# 8 KV heads (one chunk each), wrap groups of shifted heads included.
+SAMPLES = {
+    "llama2-7b-8k": [(0, 1), (10, 2), (20, 0), (31, 3)],
+    "llama2-7b-32k": [(0, 0), (12, 1), (17, 3), (31, 3)],
+    "llama2-7b-100k": [(5, 2), (9, 0), (22, 1), (31, 3)],
+    "llama2-70b-gqa-32k": [(0, 2), (2, 1), (4, 3), (5, 0), (7, 3)],
 }
 
 
@@ -366,6 +371,25 @@ def test_full_size_swap():
     assert torch.equal(out[0][:, 0, h], t["v"][:, 0, h // (w.H // w.Hkv)])
     for c, g0 in [(31, 3), (0, 3)]:
         check_sampled(w, t, out, c, g0, wrap="swap")
+
+
+@pytest.mark.parametrize("wrap", ["split", "swap"])
+def test_full_size_gqa_wrap_options(wrap):
+    """The split and swap options at the 70B GQA shape (64 query heads over 8
+    KV heads, 32 shifted): the wrap group of a shifted KV head (8 query heads,
+    dk / dv summed over them) and a group of an unshifted one."""
+    w = WORKLOADS["llama2-70b-gqa-32k"]
+    say(f"case {w} wrap={wrap} (generating inputs on the GPU)")
+    t = make_inputs(w, seed=0, device="cuda")
+    out = run_gpu(w, t, wrap=wrap)
+    say("  kernels done")
+    for name, x in zip(("o", "lse", "dq", "dk", "dv"), out):
+        assert bool(torch.isfinite(x).all()), f"non-finite values in {name}"
+    # token 0 of a shifted head opens a causal group of its own (split) or the wrap group (swap)
+    h = w.H - 1
+    assert torch.equal(out[0][:, 0, h], t["v"][:, 0, h // (w.H // w.Hkv)])
+    for c, g0 in [(6, 3), (1, 2)]:
+        check_sampled(w, t, out, c, g0, wrap=wrap)
 
 
 def test_full_size_full_attention():
