@@ -226,7 +226,9 @@ def main():
                     help="wrap handling of the shifted heads (split, swap: Table 8's Variants 2, 3)")
     ap.add_argument("--rope", action="store_true",
                     help="also time the rotary embedding with Position Interpolation on q and k (and its inverse "
-                         "on dq and dk), the step before the attention; reported apart from the step")
+                         "on dq and dk), the step before the attention, and a whole step with the rotary passes "
+                         "stand-alone against one with them fused into the attention kernels (k's pass kept); "
+                         "reported apart from the step")
     ap.add_argument("--range", default="llama2-7b-8k,llama2-7b-100k,llama2-70b-gqa-32k",
                     help="comma-separated workloads also timed (forward and backward only, a few steps each) and "
                          "reported under \"range\", so the metric's whole N range is measured in one run; empty = none")
@@ -305,9 +307,9 @@ def main():
     dominant = max(kern_ms, key=kern_ms.get)
     kernels = {}
     for n, ms in kern_ms.items():
-        v = kern_all[n]
-        kernels[n] = {"ms": round(ms, 4), "ms_min": round(v[0], 4), "ms_median": round(v[len(v) // 2], 4),
-                      "ms_max": round(v[-1], 4)}
+        times = kern_all[n]
+        kernels[n] = {"ms": round(ms, 4), "ms_min": round(times[0], 4),
+                      "ms_median": round(times[len(times) // 2], 4), "ms_max": round(times[-1], 4)}
         if n in kern_flops:
             kernels[n]["tflops"] = round(kern_flops[n] / ms / 1e9, 1)
             kernels[n]["frac_of_peak"] = round(kern_flops[n] / ms / 1e9 / peak, 4)
@@ -354,7 +356,7 @@ def main():
         result["hbm_copy_bytes"] = src.numel() * 4
         del src, dst
     if args.rope:
-        from shifted_sparse_attention_s2attn_amd import s2attn_rope
+        from shifted_sparse_attention_s2attn_amd import s2attn_bwd_rope, s2attn_fwd_rope, s2attn_rope
         pi = 4096 / w.N                          # Position Interpolation from a 4k model to this context
         qr, kr = torch.empty_like(q), torch.empty_like(k)
 
@@ -364,18 +366,45 @@ def main():
             s2attn_rope(dq, pi, inverse=True, out=qr)
             s2attn_rope(dk, pi, inverse=True, out=kr)
 
-        for _ in range(3):
-            rope_step()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            rope_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
+        def unfused_step():                      # rotary passes around the plain attention step
+            s2attn_rope(q, pi, out=qr)
+            s2attn_rope(k, pi, out=kr)
+            s2attn_fwd(qr, kr, v, w.G, w.shift_heads, out=o, lse=lse, wrap=args.wrap)
+            s2attn_bwd_prep_dq(qr, kr, v, o, lse, do, dq, ws, w.G, w.shift_heads, wrap=args.wrap)
+            s2attn_bwd_dkdv(qr, kr, v, do, dk, dv, ws, w.G, w.shift_heads, wrap=args.wrap)
+            s2attn_rope(dq, pi, inverse=True, out=dq)
+            s2attn_rope(dk, pi, inverse=True, out=dk)
+
+        qrot = torch.empty_like(q)
+
+        def fused_step():                        # k's pass only; q, dq, dk turned inside the kernels
+            s2attn_rope(k, pi, out=kr)
+            s2attn_fwd_rope(q, kr, v, w.G, w.shift_heads, pi, wrap=args.wrap, out=o, lse=lse, q_rot=qrot)
+            s2attn_bwd_rope(qrot, kr, v, o, lse, do, w.G, w.shift_heads, pi, wrap=args.wrap, workspace=ws,
+                            grads=(dq, dk, dv))
+
+        def timed(fn, reps):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms = timed(rope_step, args.steps)
         nbytes = 2 * 2 * (q.numel() + k.numel()) * q.element_size()   # read + write, forward and inverse
         result["rope"] = {"ms": round(ms, 4), "gbps": round(nbytes / ms / 1e6, 1), "bytes": nbytes,
                           "pos_scale": pi, "bound": "hbm", "frac_of_8tbs": round(nbytes / ms / 1e6 / 8000, 4)}
+        # the two routes alternated, so both see the same clock
+        un, fu = [], []
+        for _ in range(3):
+            un.append(timed(unfused_step, args.steps))
+            fu.append(timed(fused_step, args.steps))
+        result["rope"]["step_ms_standalone"] = round(sorted(un)[1], 4)
+        result["rope"]["step_ms_fused"] = round(sorted(fu)[1], 4)
     result["device_peak"] = device_peak()
     if w.dtype == "bf16" and not args.no_gemm_reference:
         ref = gemm_reference(torch, dev)

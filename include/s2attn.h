@@ -250,6 +250,34 @@ int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* 
 int s2attn_rope(const void* x, void* y, int B, int N, int Hx, int d, double pos_scale, double base,
                 int inverse, int dtype, void* stream);
 
+/*
+ * The attention with the rotary embedding (Position Interpolation) of
+ * s2attn_rope fused in, bf16 only (other dtypes: S2ATTN_ERR_UNSUPPORTED).  The
+ * fine-tuning path of the pages (section 3.2 Phase 1 item 2, "Model setup")
+ * rotates q and k before the attention; here
+ *   k_rot = s2attn_rope(k)                    (the stand-alone pass, for k only)
+ *   s2attn_fwd_rope: takes q unrotated and k_rot; rotates q in the kernel's
+ *       registers (bit-equal to s2attn_rope(q)), writes o, lse as s2attn_fwd_ex
+ *       on the rotated q and k_rot, and the rotated q to q_rot [B,N,H,d] for
+ *       the backward;
+ *   s2attn_bwd_rope: takes q_rot and k_rot, writes dv as s2attn_bwd_ex and dq,
+ *       dk already turned back by the inverse rotation, i.e. the gradients with
+ *       respect to the unrotated q and k (the stand-alone route applies
+ *       s2attn_rope(.., inverse=1) to the bf16-rounded gradients; here the
+ *       fp32 sums are turned before rounding).
+ * Arguments, checks and workspace as the _ex calls, plus pos_scale and base as
+ * s2attn_rope (S2ATTN_ERR_UNSUPPORTED when out of range).  q_rot must not
+ * overlap any other tensor.
+ */
+int s2attn_fwd_rope(const void* q, const void* k_rot, const void* v, void* o, float* lse, void* q_rot,
+                    int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                    double pos_scale, double base, int dtype, void* stream);
+int s2attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const void* o,
+                    const float* lse, const void* dO,
+                    void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                    int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                    double pos_scale, double base, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* s2attn_status_str(int status);
 

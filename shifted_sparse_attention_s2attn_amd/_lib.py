@@ -28,7 +28,8 @@ WRAPS = {"roll": S2ATTN_WRAP_ROLL, "split": S2ATTN_WRAP_SPLIT, "swap": S2ATTN_WR
 
 EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes", "s2attn_bwd_prep", "s2attn_bwd_dkdv",
            "s2attn_bwd_dq", "s2attn_bwd_prep_dq", "s2attn_fwd_ex", "s2attn_bwd_ex", "s2attn_bwd_dkdv_ex",
-           "s2attn_bwd_dq_ex", "s2attn_bwd_noalloc", "s2attn_rope", "s2attn_status_str")
+           "s2attn_bwd_dq_ex", "s2attn_bwd_noalloc", "s2attn_rope", "s2attn_fwd_rope", "s2attn_bwd_rope",
+           "s2attn_status_str")
 
 _lib = None
 
@@ -72,6 +73,10 @@ def load():
     dbl = ctypes.c_double
     lib.s2attn_rope.argtypes = [vp, vp, i, i, i, i, dbl, dbl, i, i, vp]
     lib.s2attn_rope.restype = i
+    lib.s2attn_fwd_rope.argtypes = [vp, vp, vp, vp, fp, vp, i, i, i, i, i, i, i, i, dbl, dbl, i, vp]
+    lib.s2attn_fwd_rope.restype = i
+    lib.s2attn_bwd_rope.argtypes = [vp, vp, vp, vp, fp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, dbl, dbl, i, vp]
+    lib.s2attn_bwd_rope.restype = i
     lib.s2attn_status_str.argtypes = [i]
     lib.s2attn_status_str.restype = ctypes.c_char_p
     _lib = lib

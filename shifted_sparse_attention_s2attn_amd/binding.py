@@ -13,7 +13,8 @@ from . import _lib
 
 __all__ = ["S2AttnError", "s2attn_fwd", "s2attn_bwd", "s2attn_bwd_workspace_bytes", "s2attn_bwd_noalloc",
            "s2attn_bwd_prep", "s2attn_bwd_dkdv", "s2attn_bwd_dq", "s2attn_bwd_prep_dq",
-           "s2attn_status_str", "S2Attn", "s2attn", "s2attn_rope", "RoPE", "rope"]
+           "s2attn_status_str", "S2Attn", "s2attn", "s2attn_rope", "RoPE", "rope", "s2attn_fwd_rope",
+           "s2attn_bwd_rope", "S2AttnRoPE", "s2attn_with_rope"]
 
 
 class S2AttnError(RuntimeError):
@@ -279,3 +280,81 @@ class RoPE(torch.autograd.Function):
 def rope(x, pos_scale=1.0, base=10000.0):
     """Differentiable rotary embedding with Position Interpolation (see s2attn_rope)."""
     return RoPE.apply(x, pos_scale, base)
+
+
+def s2attn_fwd_rope(q, k_rot, v, G, shift_heads=None, pos_scale=1.0, base=10000.0, wrap="roll", out=None, lse=None,
+                    q_rot=None, stream=None):
+    """S2-Attn forward with the rotary embedding of q fused in (bf16): q is
+    unrotated, k_rot = s2attn_rope(k).  Returns (o, lse, q_rot), q_rot being q
+    rotated (bit-equal to s2attn_rope(q)) for s2attn_bwd_rope."""
+    _check_tensors(q, k_rot, v)
+    B, N, H, d = q.shape
+    Hkv = k_rot.shape[2]
+    if shift_heads is None:
+        shift_heads = H // 2
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    qr = torch.empty_like(q) if q_rot is None else q_rot
+    _check_tensors(q, k_rot, v, (("out", o, None, None), ("lse", lse_t, (B, H, N), torch.float32),
+                                 ("q_rot", qr, None, None)))
+    with torch.cuda.device(q.device):
+        _check(_lib.load().s2attn_fwd_rope(_ptr(q), _ptr(k_rot), _ptr(v), _ptr(o), _fptr(lse_t), _ptr(qr),
+                                           B, H, Hkv, N, d, G, shift_heads, _wrap_code(wrap), float(pos_scale),
+                                           float(base), _dtype_code(q), _stream(stream)),
+               "s2attn_fwd_rope")
+    return o, lse_t, qr
+
+
+def s2attn_bwd_rope(q_rot, k_rot, v, o, lse, do, G, shift_heads=None, pos_scale=1.0, base=10000.0, wrap="roll",
+                    workspace=None, grads=None, stream=None):
+    """Backward of s2attn_fwd_rope: (dq, dk, dv) with dq, dk the gradients with
+    respect to the unrotated q and k (turned back inside the kernels)."""
+    _check_tensors(q_rot, k_rot, v, (("o", o, None, None), ("lse", lse, _lse_shape(q_rot), torch.float32),
+                                     ("do", do, None, None)))
+    B, H, Hkv, N, d, S = _dims(q_rot, k_rot, shift_heads)
+    need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, S, q_rot.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_rot.device)
+    _check_workspace(q_rot, workspace)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q_rot), torch.empty_like(k_rot), torch.empty_like(v)
+    else:
+        dq, dk, dv = grads
+        _check_tensors(q_rot, k_rot, v, (("dq", dq, None, None), ("dk", dk, k_rot.shape, None),
+                                         ("dv", dv, k_rot.shape, None)))
+    with torch.cuda.device(q_rot.device):
+        _check(_lib.load().s2attn_bwd_rope(_ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(o), _fptr(lse), _ptr(do),
+                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                           B, H, Hkv, N, d, G, S, _wrap_code(wrap), float(pos_scale), float(base),
+                                           _dtype_code(q_rot), _stream(stream)),
+               "s2attn_bwd_rope")
+    return dq, dk, dv
+
+
+class S2AttnRoPE(torch.autograd.Function):
+    """autograd wrapper of rotary embedding + S2-Attn with the q rotation and the
+    inverse rotations of dq and dk fused into the attention kernels; k takes the
+    stand-alone rotary pass."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, G, shift_heads, pos_scale, base, wrap="roll"):
+        k_rot = s2attn_rope(k, pos_scale, base)
+        o, lse, q_rot = s2attn_fwd_rope(q, k_rot, v, G, shift_heads, pos_scale, base, wrap=wrap)
+        ctx.save_for_backward(q_rot, k_rot, v, o, lse)
+        ctx.args = (G, shift_heads, pos_scale, base, wrap)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q_rot, k_rot, v, o, lse = ctx.saved_tensors
+        G, shift_heads, pos_scale, base, wrap = ctx.args
+        dq, dk, dv = s2attn_bwd_rope(q_rot, k_rot, v, o, lse, do.contiguous(), G, shift_heads, pos_scale, base,
+                                     wrap=wrap)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def s2attn_with_rope(q, k, v, G, shift_heads=None, pos_scale=1.0, base=10000.0, wrap="roll"):
+    """Differentiable rotary embedding (Position Interpolation) of q and k followed
+    by S2-Attn, bf16; q, k unrotated [B, N, heads, d]."""
+    return S2AttnRoPE.apply(q, k, v, G, q.shape[2] // 2 if shift_heads is None else shift_heads, pos_scale, base,
+                            wrap)

@@ -28,6 +28,13 @@ hipError_t launch_bwd_dq(const void*, const void*, const void*, const void*, con
 template <typename T, int D>
 hipError_t launch_bwd_prep_dq(const void*, const void*, const void*, const void*, const float*, const void*,
                               float*, float*, void*, int, int, int, int, int, int, int, hipStream_t);
+template <int D>
+hipError_t launch_fwd_rope(const void*, const void*, const void*, void*, float*, void*, int, int, int, int, int, int,
+                           int, double, double, hipStream_t);
+template <int D>
+hipError_t launch_bwd_rope(const void*, const void*, const void*, const void*, const float*, const void*, float*,
+                           float*, void*, void*, void*, int, int, int, int, int, int, int, double, double,
+                           hipStream_t);
 }  // namespace s2a
 
 namespace {
@@ -84,6 +91,12 @@ int check_wrap(int wrap, int N, int G) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Rotary embedding parameters: a finite, non-negative position scale and a
+// finite base above 1.
+bool bad_rope(double pos_scale, double base) {
+  return !isfinite(pos_scale) || pos_scale < 0 || !isfinite(base) || !(base > 1);
+}
 
 }  // namespace
 
@@ -288,6 +301,48 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
                        shift_heads, S2ATTN_WRAP_ROLL, dtype, stream);
 }
 
+int s2attn_fwd_rope(const void* q, const void* k_rot, const void* v, void* o, float* lse, void* q_rot,
+                    int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                    double pos_scale, double base, int dtype, void* stream) {
+  int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st == S2ATTN_OK) st = check_wrap(wrap, N, G);
+  if (st != S2ATTN_OK) return st;
+  if (dtype != S2ATTN_BF16 || bad_rope(pos_scale, base)) return S2ATTN_ERR_UNSUPPORTED;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!q || !k_rot || !v || !o || !lse || !q_rot) return S2ATTN_ERR_NULL;
+  if (misaligned16({q, k_rot, v, o, q_rot}) || misaligned4(lse)) return S2ATTN_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e =
+      d == 64 ? s2a::launch_fwd_rope<64>(q, k_rot, v, o, lse, q_rot, B, H, Hkv, N, G, shift_heads, wrap, pos_scale,
+                                         log2(base), s)
+              : s2a::launch_fwd_rope<128>(q, k_rot, v, o, lse, q_rot, B, H, Hkv, N, G, shift_heads, wrap, pos_scale,
+                                          log2(base), s);
+  return status_of(e);
+}
+
+int s2attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const void* o, const float* lse,
+                    const void* dO, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                    int B, int H, int Hkv, int N, int d, int G, int shift_heads, int wrap,
+                    double pos_scale, double base, int dtype, void* stream) {
+  int st = check_problem(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (st == S2ATTN_OK) st = check_wrap(wrap, N, G);
+  if (st != S2ATTN_OK) return st;
+  if (dtype != S2ATTN_BF16 || bad_rope(pos_scale, base)) return S2ATTN_ERR_UNSUPPORTED;
+  if (empty_problem(B, N)) return S2ATTN_OK;
+  if (!q_rot || !k_rot || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
+  if (misaligned16({q_rot, k_rot, v, o, dO, dq, dk, dv}) || misaligned4(lse)) return S2ATTN_ERR_ALIGN;
+  Workspace ws;
+  st = check_workspace(workspace, workspace_bytes, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
+  if (st != S2ATTN_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e =
+      d == 64 ? s2a::launch_bwd_rope<64>(q_rot, k_rot, v, o, lse, dO, ws.lse2, ws.dvec, dq, dk, dv, B, H, Hkv, N, G,
+                                         shift_heads, wrap, pos_scale, log2(base), s)
+              : s2a::launch_bwd_rope<128>(q_rot, k_rot, v, o, lse, dO, ws.lse2, ws.dvec, dq, dk, dv, B, H, Hkv, N, G,
+                                          shift_heads, wrap, pos_scale, log2(base), s);
+  return status_of(e);
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
@@ -353,8 +408,7 @@ int s2attn_rope(const void* x, void* y, int B, int N, int Hx, int d, double pos_
   if (B < 0 || N < 0 || Hx <= 0 || d <= 0) return S2ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return S2ATTN_ERR_UNSUPPORTED;
   if (dtype != S2ATTN_BF16 && dtype != S2ATTN_F32) return S2ATTN_ERR_UNSUPPORTED;
-  if (!isfinite(pos_scale) || pos_scale < 0 || !isfinite(base) || !(base > 1) || (inverse != 0 && inverse != 1))
-    return S2ATTN_ERR_UNSUPPORTED;
+  if (bad_rope(pos_scale, base) || (inverse != 0 && inverse != 1)) return S2ATTN_ERR_UNSUPPORTED;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!x || !y) return S2ATTN_ERR_NULL;
   if (misaligned16({x, y})) return S2ATTN_ERR_ALIGN;
@@ -373,7 +427,7 @@ const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_OK: return "ok";
     case S2ATTN_ERR_NULL: return "a required pointer is NULL";
     case S2ATTN_ERR_SHAPE: return "invalid shape (a size < 0, H, Hkv, d or G <= 0, G > N, shift_heads outside [0,H], or H % Hkv != 0)";
-    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split, swap or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, grid too large, H * d >= 2^24, or a rotary scale, base or direction out of range)";
+    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split, swap or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, grid too large, H * d >= 2^24, a rotary scale, base or direction out of range, or an fp32 problem for the fused rotary calls)";
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     case S2ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (element tensors need 16 bytes, lse 4)";

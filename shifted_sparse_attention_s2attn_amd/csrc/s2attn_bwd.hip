@@ -485,17 +485,49 @@ __device__ __forceinline__ f32x4 lds_f32x4(const char* base, int off) {
   return *reinterpret_cast<const f32x4*>(base + off);
 }
 
+// Store a gradient row held as D/32 accumulator tiles (element
+// dt * 32 + u * 16 + 8 hf + e in register 8 u + e of tile dt), times `scale`,
+// turned back by the rotary embedding at position pos (the transpose of the
+// forward rotation): the gradient with respect to the unrotated input.
+// Element i < D/2 and its partner i + D/2 sit in tiles dt and dt + D/64 of the
+// same lane.
+template <int D>
+__device__ __forceinline__ void store_turned_back(bf16* row, const f32x16* acc, float scale, double pos,
+                                                  double log2_base, int hf) {
+  constexpr int HT = D / 64;
+#pragma unroll
+  for (int dt = 0; dt < HT; ++dt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 ya, yb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float cs, sn, y0, y1;
+        rope_cs(pos, rope_rev_per_pos<D>(dt * 32 + u * 16 + hf * 8 + e, log2_base), cs, sn);
+        rope_turn(acc[dt][u * 8 + e] * scale, acc[dt + HT][u * 8 + e] * scale, cs, -sn, y0, y1);
+        ya[e] = (bf16)y0;
+        yb[e] = (bf16)y1;
+      }
+      *reinterpret_cast<bf16x8*>(row + dt * 32 + u * 16 + hf * 8) = ya;
+      *reinterpret_cast<bf16x8*>(row + (dt + HT) * 32 + u * 16 + hf * 8) = yb;
+    }
+}
+
 // SPLIT: the split wrap option; EDGE: groups that are not whole tiles (query
 // rows of the next group are masked, tiles that cross the wrap point or the
 // end of the sequence take per-row addresses, keys past the group are not
 // stored); SWAP: the swap wrap option's row map (token_of_row).  Each is
 // compiled separately, so that the main method's step loop carries no trace
 // of any of them.
+// rope.on: q and k arrive rotated by the rotary embedding; dk is turned back
+// (the transpose of the rotation) before it is stored, so it is the gradient
+// with respect to the unrotated k.
 template <int D, bool SPLIT, bool EDGE, bool SWAP>
 __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
-    bf16* __restrict__ dk, bf16* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, float scale) {
+    bf16* __restrict__ dk, bf16* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, float scale,
+    RopeArgs rope) {
   using S = DkdvB16Shape<D>;
   constexpr int BKV = S::kBKV, BQ = S::kBQ, CPR = S::kCPR, RB = S::kRowB;
   // static, so that tile addresses are compile-time constants and every LDS
@@ -769,10 +801,17 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
 #pragma unroll
     for (int dt = 0; dt < S::kDT; ++dt)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        *reinterpret_cast<bf16x8*>(dkrow + dt * 32 + u * 16 + hf * 8) = scale8<bf16>(dkacc[dt], u * 8, scale);
+      for (int u = 0; u < 2; ++u)
         *reinterpret_cast<bf16x8*>(dvrow + dt * 32 + u * 16 + hf * 8) = pack8<bf16>(dvacc[dt], u * 8);
-      }
+    if (rope.on) {
+      store_turned_back<D>(dkrow, dkacc, scale, (double)tk * rope.pos_scale, rope.log2_base, hf);
+      return;
+    }
+#pragma unroll
+    for (int dt = 0; dt < S::kDT; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<bf16x8*>(dkrow + dt * 32 + u * 16 + hf * 8) = scale8<bf16>(dkacc[dt], u * 8, scale);
   }
 }
 // ---------------------------------------------------------------------------
@@ -798,12 +837,14 @@ struct DqB16Shape {
   static constexpr int kDT = D / 32;
 };
 
+// rope.on: q and k arrive rotated; dq is turned back before it is stored (the
+// gradient with respect to the unrotated q).
 template <int D, bool PREP, bool EDGE, bool SWAP>
 __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const bf16* __restrict__ o, const float* __restrict__ lse,
     float* __restrict__ lse2, float* __restrict__ dvec,
-    bf16* __restrict__ dq, int N, int H, int Hkv, int G, int shift_heads, int split, float scale) {
+    bf16* __restrict__ dq, int N, int H, int Hkv, int G, int shift_heads, int split, float scale, RopeArgs rope) {
   using S = DqB16Shape<D>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTile;
   constexpr int RB = D * 2;
@@ -999,6 +1040,10 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
 
   if (!q_ok) return;
   bf16* dqrow = dq + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+  if (rope.on) {
+    store_turned_back<D>(dqrow, dqacc, scale, (double)tq * rope.pos_scale, rope.log2_base, hf);
+    return;
+  }
 #pragma unroll
   for (int dt = 0; dt < S::kDT; ++dt)
 #pragma unroll
@@ -1022,7 +1067,7 @@ hipError_t launch_bwd_prep(const void* o, const void* dO, const float* lse, floa
 template <int D>
 hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                             const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                            int shift_heads, int wrap, float scale, hipStream_t stream) {
+                            int shift_heads, int wrap, float scale, RopeArgs rope, hipStream_t stream) {
   using S = DkdvB16Shape<D>;
   constexpr int BKV = S::kBKV;
   const bool whole = N % G == 0 && G % BKV == 0;     // the split and swap options imply whole tiles
@@ -1031,7 +1076,7 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
 #define S2A_DKDV_LAUNCH(SPLIT, EDGE, SWAP)                                                                     \
   hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, SPLIT, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,     \
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk, (bf16*)dv, N, H, Hkv, \
-                     G, shift_heads, scale)
+                     G, shift_heads, scale, rope)
   if (wrap == kWrapSplit)
     S2A_DKDV_LAUNCH(true, false, false);
   else if (wrap == kWrapSwap)
@@ -1062,7 +1107,8 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            int shift_heads, int wrap, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (std::is_same_v<T, bf16>)
-    return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
+    return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale,
+                               RopeArgs{nullptr, 0, 0, 0}, stream);
   else
     return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale,
                                      stream);
@@ -1072,7 +1118,8 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 template <int D>
 hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO, const void* o,
                           const float* lse, float* lse2, float* dvec, void* dq, int B, int H, int Hkv, int N, int G,
-                          int shift_heads, int wrap, float scale, hipStream_t stream) {
+                          int shift_heads, int wrap, float scale, hipStream_t stream,
+                          RopeArgs rope = RopeArgs{nullptr, 0, 0, 0}) {
   using S = DqB16Shape<D>;
   constexpr int BR = S::kBR;
   const bool whole = N % G == 0 && G % BR == 0;
@@ -1081,7 +1128,7 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
 #define S2A_DQ_LAUNCH(PREP, EDGE, SWAP)                                                                       \
   hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, PREP, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,     \
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec, (bf16*)dq, N, H, Hkv, \
-                     G, shift_heads, (int)(wrap == kWrapSplit), scale)
+                     G, shift_heads, (int)(wrap == kWrapSplit), scale, rope)
   if (wrap == kWrapSwap) {
     if (o) {
       if (whole) S2A_DQ_LAUNCH(true, false, true); else S2A_DQ_LAUNCH(true, true, true);
@@ -1136,6 +1183,29 @@ hipError_t launch_bwd_prep_dq(const void* q, const void* k, const void* v, const
     return launch_bwd_dq<T, D>(q, k, v, dO, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads, wrap, stream);
   }
 }
+
+// The backward with the rotary embedding fused (bf16): q_rot and k_rot are the
+// rotated inputs the forward used; dq and dk come out turned back, i.e. with
+// respect to the unrotated q and k.  Prep + dq in one launch, then dK/dV.
+template <int D>
+hipError_t launch_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const void* o, const float* lse,
+                           const void* dO, float* lse2, float* dvec, void* dq, void* dk, void* dv, int B, int H,
+                           int Hkv, int N, int G, int shift_heads, int wrap, double pos_scale, double log2_base,
+                           hipStream_t stream) {
+  const float scale = 1.0f / sqrtf((float)D);
+  const RopeArgs rope{nullptr, pos_scale, log2_base, 1};
+  const hipError_t e = launch_dq_bf16<D>(q_rot, k_rot, v, dO, o, lse, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads,
+                                         wrap, scale, stream, rope);
+  if (e != hipSuccess) return e;
+  return launch_dkdv_bf16<D>(q_rot, k_rot, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale,
+                             rope, stream);
+}
+template hipError_t launch_bwd_rope<64>(const void*, const void*, const void*, const void*, const float*, const void*,
+                                        float*, float*, void*, void*, void*, int, int, int, int, int, int, int, double,
+                                        double, hipStream_t);
+template hipError_t launch_bwd_rope<128>(const void*, const void*, const void*, const void*, const float*,
+                                         const void*, float*, float*, void*, void*, void*, int, int, int, int, int, int,
+                                         int, double, double, hipStream_t);
 
 #define S2A_INST_BWD(T, D)                                                                                 \
   template hipError_t launch_bwd_prep<T, D>(const void*, const void*, const float*, float*, float*, int,  \

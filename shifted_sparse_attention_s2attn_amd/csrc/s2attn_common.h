@@ -161,6 +161,44 @@ __device__ __forceinline__ int frame_row(int j, int sig_from, int sig_to, int N,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotary embedding with Position Interpolation (page "LongLoRA: Efficient
+// Fine-tuning of Long-Context Large Language Models", section 3.2 Phase 1
+// item 2, and "Model setup": the pre-trained rotary embeddings rescaled by
+// Position Interpolation; the pages give no formula, the rotate-half pairing is
+// the published rotary embedding).  Pair (i, i + D/2), i < D/2, of token n turns
+// by n * pos_scale * base^(-2i/D) radians.  One set of helpers serves the
+// stand-alone pass and the attention kernels that fuse the rotation, so the two
+// produce the same bits.
+// Revolutions per position of pair i (float64):
+template <int D>
+__device__ __forceinline__ double rope_rev_per_pos(int i, double log2_base) {
+  return exp2(-(2.0 * i / D) * log2_base) * 0.15915494309189533577;
+}
+// Cosine and sine of pos * g revolutions, pos = n * pos_scale: the angle is
+// formed in float64 and reduced to [-1/2, 1/2] revolutions (a float32 angle
+// would be off by ~1e-2 rad at positions near 1e5) before the hardware sine
+// and cosine of revolutions.
+__device__ __forceinline__ void rope_cs(double pos, double g, float& cs, float& sn) {
+  const double u = pos * g;
+  const float fr = (float)(u - rint(u));
+  sn = __builtin_amdgcn_sinf(fr);
+  cs = __builtin_amdgcn_cosf(fr);
+}
+// The pair (a, b) = (x_i, x_{i + D/2}) turned by the angle (sn < 0: backwards).
+// Explicit fused multiply-adds, so every kernel rounds the same way.
+__device__ __forceinline__ void rope_turn(float a, float b, float cs, float sn, float& ya, float& yb) {
+  ya = fmaf(a, cs, -(b * sn));
+  yb = fmaf(b, cs, a * sn);
+}
+// Fused rotation of the attention kernels: `on` = rotate; pos_scale and
+// log2(base) as above; q_rot receives the rotated q written by the forward.
+struct RopeArgs {
+  bf16* q_rot;
+  double pos_scale;
+  double log2_base;
+  int on;
+};
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // Global memory straight into LDS (no registers): lane i of the wave fills

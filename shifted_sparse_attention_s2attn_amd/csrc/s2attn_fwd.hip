@@ -273,11 +273,14 @@ __device__ __forceinline__ int swz_v(int row) {
 // loaded with per-row addresses.  Compiled separately from the whole-tile case.
 // SWAP: the swap wrap option's row map (token_of_row); `split` is 1 for the
 // split option.
+// rope.on: q arrives unrotated; the kernel turns its Q rows by the rotary
+// embedding with Position Interpolation (k arrives rotated) and writes the
+// rotated rows to rope.q_rot for the backward.
 template <int D, bool EDGE, bool SWAP>
 __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse,
-    int N, int H, int Hkv, int G, int shift_heads, int split, float scale) {
+    int N, int H, int Hkv, int G, int shift_heads, int split, float scale, RopeArgs rope) {
   using S = FwdB16Shape<D>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTileChunks;
   constexpr int RB = D * 2;                       // bytes per tile row
@@ -323,6 +326,30 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     const bf16* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
 #pragma unroll
     for (int cc = 0; cc < S::kDC; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(qrow + cc * 16 + hf * 8);
+  }
+  if (rope.on) {
+    // element i < D/2 of the row sits in chunk i / 16 and its partner i + D/2 in
+    // chunk i / 16 + D/32 of the same lane: the rotation is lane-local
+    const double pos = (double)tq * rope.pos_scale;
+#pragma unroll
+    for (int cc = 0; cc < S::kDC / 2; ++cc) {
+      bf16x8 ya, yb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float cs, sn, y0, y1;
+        rope_cs(pos, rope_rev_per_pos<D>(cc * 16 + hf * 8 + e, rope.log2_base), cs, sn);
+        rope_turn((float)qf[cc][e], (float)qf[cc + S::kDC / 2][e], cs, sn, y0, y1);
+        ya[e] = (bf16)y0;
+        yb[e] = (bf16)y1;
+      }
+      qf[cc] = ya;
+      qf[cc + S::kDC / 2] = yb;
+    }
+    if (q_ok) {
+      bf16* qr = rope.q_rot + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+#pragma unroll
+      for (int cc = 0; cc < S::kDC; ++cc) *reinterpret_cast<bf16x8*>(qr + cc * 16 + hf * 8) = qf[cc];
+    }
   }
 
   // Per-lane byte offsets, inside a 64-row tile, of the chunks this lane moves
@@ -486,7 +513,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
 template <int D>
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Hkv, int N, int G, int shift_heads, int wrap, float scale,
-                           hipStream_t stream) {
+                           RopeArgs rope, hipStream_t stream) {
   constexpr int BR = FwdB16Shape<D>::kBR;
   const dim3 block(FwdB16Shape<D>::kThreads);
   const bool whole = N % G == 0 && G % BR == 0;
@@ -494,7 +521,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 #define S2A_FWD_LAUNCH(EDGE, SWAP)                                                                              \
   hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,          \
                      (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads,                \
-                     (int)(wrap == kWrapSplit), scale)
+                     (int)(wrap == kWrapSplit), scale, rope)
   if (wrap == kWrapSwap) {
     if (whole) S2A_FWD_LAUNCH(false, true);
     else S2A_FWD_LAUNCH(true, true);
@@ -512,7 +539,8 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int B, int H, int Hkv, int N, int G, int shift_heads, int wrap, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (std::is_same_v<T, bf16>) {
-    return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, scale, stream);
+    return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, scale, RopeArgs{nullptr, 0, 0, 0},
+                              stream);
   } else {
     constexpr int BR = FwdShape<T, D>::kBR;
     dim3 grid(B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
@@ -521,6 +549,19 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
     return hipGetLastError();
   }
 }
+
+// bf16 with the rotary embedding fused: q unrotated, k rotated; writes q_rot.
+template <int D>
+hipError_t launch_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse, void* q_rot,
+                           int B, int H, int Hkv, int N, int G, int shift_heads, int wrap, double pos_scale,
+                           double log2_base, hipStream_t stream) {
+  return launch_fwd_bf16<D>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, 1.0f / sqrtf((float)D),
+                            RopeArgs{(bf16*)q_rot, pos_scale, log2_base, 1}, stream);
+}
+template hipError_t launch_fwd_rope<64>(const void*, const void*, const void*, void*, float*, void*, int, int, int,
+                                        int, int, int, int, double, double, hipStream_t);
+template hipError_t launch_fwd_rope<128>(const void*, const void*, const void*, void*, float*, void*, int, int, int,
+                                         int, int, int, int, double, double, hipStream_t);
 
 template hipError_t launch_fwd<bf16, 64>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, int, hipStream_t);
 template hipError_t launch_fwd<bf16, 128>(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int, int, hipStream_t);

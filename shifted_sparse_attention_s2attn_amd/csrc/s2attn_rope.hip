@@ -10,9 +10,10 @@
 // paired with i + d/2 and turned by t = n * pos_scale * base^(-2i/d) at token n.
 //
 // An elementwise pass bound by HBM bandwidth (one read and one write of the
-// tensor).  It is not fused into the attention kernels' tile loads: those are
-// bound by the matrix cores and their issue slots, and rotating every Q and K
-// operand there would cost more than this pass.
+// tensor).  With the fused attention calls (s2attn_fwd_rope / s2attn_bwd_rope)
+// only k takes this pass: q is turned in the forward kernel's registers, and dq
+// and dk are turned back in the backward kernels' epilogues, with the helpers
+// of s2attn_common.h, so both routes give the same rotated values.
 //
 // One thread owns 8 consecutive pairs (dimensions 8c .. 8c+7 and their
 // partners d/2 + 8c ..) and strides over rows, so its 8 frequencies are
@@ -25,10 +26,6 @@
 
 namespace s2a {
 
-// sine and cosine of x revolutions (x * 2 pi radians), |x| <= 1/2
-__device__ __forceinline__ float hw_sin_rev(float x) { return __builtin_amdgcn_sinf(x); }
-__device__ __forceinline__ float hw_cos_rev(float x) { return __builtin_amdgcn_cosf(x); }
-
 // I: the row index type (32-bit while the row count allows it: cheaper division)
 template <typename T, int D, typename I>
 __global__ __launch_bounds__(256) void s2attn_rope_kernel(const T* x, T* y, I rows, int N, int Hx,
@@ -38,7 +35,7 @@ __global__ __launch_bounds__(256) void s2attn_rope_kernel(const T* x, T* y, I ro
   const int c = threadIdx.x % TPR;
   double g[8];                                // revolutions per position of each pair
 #pragma unroll
-  for (int e = 0; e < 8; ++e) g[e] = exp2(-(2.0 * (8 * c + e) / D) * log2_base) * 0.15915494309189533577;
+  for (int e = 0; e < 8; ++e) g[e] = rope_rev_per_pos<D>(8 * c + e, log2_base);
   for (I r = (I)blockIdx.x * RPB + threadIdx.x / TPR; r < rows; r += (I)gridDim.x * RPB) {
     const int n = (int)((r / (I)Hx) % (I)N);  // rows are (batch, token, head), token-major
     const double pos = (double)n * pos_scale;
@@ -49,19 +46,19 @@ __global__ __launch_bounds__(256) void s2attn_rope_kernel(const T* x, T* y, I ro
     v8<T> ya, yb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double u = pos * g[e];
-      const float fr = (float)(u - rint(u));    // the angle in revolutions, in [-1/2, 1/2]
       float sn, cs;
       if constexpr (sizeof(T) == 2) {
-        sn = hw_sin_rev(fr);
-        cs = hw_cos_rev(fr);
+        rope_cs(pos, g[e], cs, sn);
       } else {
+        const double u = pos * g[e];
+        const float fr = (float)(u - rint(u));    // the angle in revolutions, in [-1/2, 1/2]
         sincosf(fr * 6.28318530717958647692f, &sn, &cs);
       }
       if (inverse) sn = -sn;
-      const float xa = (float)a[e], xb = (float)b[e];
-      ya[e] = (T)(xa * cs - xb * sn);
-      yb[e] = (T)(xb * cs + xa * sn);
+      float y0, y1;
+      rope_turn((float)a[e], (float)b[e], cs, sn, y0, y1);
+      ya[e] = (T)y0;
+      yb[e] = (T)y1;
     }
     *reinterpret_cast<v8<T>*>(yr + 8 * c) = ya;
     *reinterpret_cast<v8<T>*>(yr + D / 2 + 8 * c) = yb;

@@ -123,6 +123,31 @@ def test_noalloc_scratch_limit(lib):
     assert lib.s2attn_status_str(_lib.S2ATTN_ERR_SCRATCH).startswith(b"B * H * N exceeds")
 
 
+def test_fused_rope_validation(lib):
+    """s2attn_fwd_rope / s2attn_bwd_rope: bf16 only, rotary parameters as
+    s2attn_rope, checked after the sizes and before the pointers (NULL here)."""
+    p = dict(GOOD)
+    dims = [p["B"], p["H"], p["Hkv"], p["N"], p["d"], p["G"], p["S"]]
+    need = lib.s2attn_bwd_workspace_bytes(*dims, 0)
+
+    def fwd(scale=1.0, base=1e4, dtype=0, wrap=0, dd=dims):
+        return lib.s2attn_fwd_rope(*([None] * 4), None, None, *dd, wrap, scale, base, dtype, None)
+
+    def bwd(scale=1.0, base=1e4, dtype=0, wrap=0, dd=dims):
+        return lib.s2attn_bwd_rope(*([None] * 4), None, *([None] * 5), need, *dd, wrap, scale, base, dtype, None)
+
+    for f in (fwd, bwd):
+        assert f() == _lib.S2ATTN_ERR_NULL
+        assert f(dtype=_lib.S2ATTN_F32) == _lib.S2ATTN_ERR_UNSUPPORTED
+        assert f(scale=-1.0) == _lib.S2ATTN_ERR_UNSUPPORTED
+        assert f(scale=float("nan")) == _lib.S2ATTN_ERR_UNSUPPORTED
+        assert f(base=1.0) == _lib.S2ATTN_ERR_UNSUPPORTED
+        assert f(wrap=9) == _lib.S2ATTN_ERR_UNSUPPORTED
+        assert f(dd=[dims[0], dims[1], dims[2], 64] + dims[4:]) == _lib.S2ATTN_ERR_SHAPE   # G > N
+        assert f(scale=0.0) == _lib.S2ATTN_ERR_NULL                                        # identity rotation: valid
+        assert f(dd=[0] + dims[1:]) == _lib.S2ATTN_OK                                       # empty problem
+
+
 def test_row_width_limit(lib):
     """A 64-row tile is addressed with 32-bit byte offsets from its first row, so
     one token row of q (H * d elements) must stay below 2^24 elements."""
