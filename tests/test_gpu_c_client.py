@@ -82,7 +82,7 @@ def test_c_client_matches_oracle_and_binding(w, wrap, tmp_path):
     o_ref, lse_ref = orc.forward(q, k, v, w.G, w.shift_heads, wrap)
     refs = orc.backward(q, k, v, do, w.G, w.shift_heads, wrap)
     assert float(np.max(np.abs(f(o) - o_ref))) <= 2e-2
-    assert float(np.max(np.abs(f(lse) - lse_ref))) <= 2.5e-3
+    assert float(np.max(np.abs(f(lse) - lse_ref))) <= 4e-3   # -ln(1 - 2^-8): bf16 row sums
     for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
         e = float(np.linalg.norm(f(a) - b) / np.linalg.norm(b))
         assert e <= 3e-2, (name, e)

@@ -2,8 +2,10 @@
 the float64 oracle, element by element, and composed with the attention.
 
 Bar: |y - y*| <= 2^-8 (|x_i| + |x_{i+d/2}|) per element for bf16 (the output
-rounding alone is 2^-9 of |y| <= |x_i| + |x_{i+d/2}|), 1e-6 of the same for
-fp32 (float32 rotation of an angle reduced in float64)."""
+rounding alone is at most the bf16 unit roundoff 2^-8 of |y| <= |x_i| +
+|x_{i+d/2}|; the float32 rotation and the hardware sine and cosine add far
+less), 1e-6 of the same for fp32 (float32 rotation of an angle reduced in
+float64)."""
 
 import numpy as np
 import pytest
