@@ -81,13 +81,14 @@ bool misaligned16(std::initializer_list<const void*> ps) {
 }
 bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) != 0; }
 
-// The split option cuts the last group at G/2 and the swap option reorders
-// its halves; both need aligned shapes.
+// The wrap options: the main method's roll, the split option (the wrap group
+// cut where the roll wraps) and the swap option (the wrap group's front tokens
+// first), on every shape.
 int check_wrap(int wrap, int N, int G) {
-  if (wrap == S2ATTN_WRAP_ROLL) return S2ATTN_OK;
-  if (wrap == S2ATTN_WRAP_SPLIT || wrap == S2ATTN_WRAP_SWAP)
-    return (N == 0 || aligned(N, G)) ? S2ATTN_OK : S2ATTN_ERR_UNSUPPORTED;
-  return S2ATTN_ERR_UNSUPPORTED;
+  (void)N;
+  (void)G;
+  return (wrap == S2ATTN_WRAP_ROLL || wrap == S2ATTN_WRAP_SPLIT || wrap == S2ATTN_WRAP_SWAP) ? S2ATTN_OK
+                                                                                              : S2ATTN_ERR_UNSUPPORTED;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -427,7 +428,7 @@ const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_OK: return "ok";
     case S2ATTN_ERR_NULL: return "a required pointer is NULL";
     case S2ATTN_ERR_SHAPE: return "invalid shape (a size < 0, H, Hkv, d or G <= 0, G > N, shift_heads outside [0,H], or H % Hkv != 0)";
-    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, split, swap or a mixed-shift KV head on a shape whose groups are not whole 128-row tiles, grid too large, H * d >= 2^24, a rotary scale, base or direction out of range, or an fp32 problem for the fused rotary calls)";
+    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, a KV head shared by shifted and unshifted query heads on a shape whose groups (and half groups) are not whole 128-row tiles, grid too large, H * d >= 2^24, a rotary scale, base or direction out of range, or an fp32 problem for the fused rotary calls)";
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     case S2ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (element tensors need 16 bytes, lse 4)";

@@ -133,7 +133,8 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   const int h0 = c * r;
   const int sig0 = (h0 >= H - shift_heads) ? G / 2 : 0;
   const bool swap = wrap == kWrapSwap;
-  auto tok = [&](int j, int sig) { return swap ? token_of_row<true>(j, sig, N, G) : orig_row(j, sig, N); };
+  const WrapGroup wg = wrap_group(N, G);
+  auto tok = [&](int j, int sig) { return swap ? token_of_row<true>(j, sig, N, wg) : orig_row(j, sig, N); };
   const int ge0 = min(grp * G + G, N);          // end of the group (a last group may be short)
   const int j0 = grp * G + pos * BKV;           // first key row, rolled frame of head h0
   if (j0 >= ge0) return;                        // a tile past the end of a short group
@@ -167,14 +168,16 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     const int h = h0 + hh;
     const int sig = (h >= H - shift_heads) ? G / 2 : 0;
     // same key rows in head h's rolled frame
-    const int jk0 = swap ? frame_row<true>(j0, sig0, sig, N, G) : frame_row<false>(j0, sig0, sig, N, G);
+    const int jk0 = swap ? frame_row<true>(j0, sig0, sig, N, wg) : frame_row<false>(j0, sig0, sig, N, wg);
     const bool split_head = wrap == kWrapSplit && sig != 0;
     // query tiles meeting the workgroup's keys, and the end of this wave's queries
-    // (queries from the next group in the last tile are masked)
-    const int q_end_g = query_end_row(jk0, G, N, false);
+    // (queries from the next group in the last tile are masked); with the split
+    // option the later of two keys sees queries at least as far
+    const int q_end_g = query_end_row(jk0, G, N, false, wg);
     const int qt_begin = jk0 / BQ;
-    const int qt_end = (min(query_end_row(jk0 + BKV - 32, G, N, split_head), q_end_g) + BQ - 1) / BQ;
-    const int q_end_w = query_end_row(jk0 + wave * 32, G, N, split_head);
+    const int qt_end = (min(query_end_row(min(jk0 + BKV - 1, q_end_g - 1), G, N, split_head, wg), q_end_g) + BQ - 1) / BQ;
+    const int q_end_w = min(query_end_row(min(jk0 + wave * 32 + 31, q_end_g - 1), G, N, split_head, wg), q_end_g);
+    const int cut = split_cut(jk0 - jk0 % G, split_head, wg);   // queries from here see no key before it
     const T* qb = q + (size_t)b * N * qstride + (size_t)h * D;
     const T* dob = dO + (size_t)b * N * qstride + (size_t)h * D;
     const float* lse_h = lse2 + ((size_t)b * H + h) * N;
@@ -228,14 +231,15 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
         }
       }
       // P and dS
-      const bool need_mask = jk0 + wave * 32 + 31 > jq0 || jq0 + BQ > q_end_g;
+      const bool need_mask = jk0 + wave * 32 + 31 > jq0 || jq0 + BQ > q_end_g ||
+                             (jk0 + wave * 32 < cut && jq0 + BQ - 1 >= cut);
 #pragma unroll
       for (int qs = 0; qs < NQS; ++qs)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qi = qs * 32 + (i >> 3) * 16 + hf * 8 + (i & 7);
           float p = fast_exp2(fmaf(sacc[qs][i], c2, -lse_s[qi]));
-          if (need_mask && (jkey > jq0 + qi || jq0 + qi >= q_end_g)) p = 0.f;
+          if (need_mask && (jkey > jq0 + qi || jq0 + qi >= q_end_g || (jkey < cut && jq0 + qi >= cut))) p = 0.f;
           sacc[qs][i] = p;
           pacc[qs][i] = p * (pacc[qs][i] - dvec_s[qi]);
         }
@@ -314,11 +318,13 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
   const bool split_head = wrap == kWrapSplit && sigma != 0;
   const bool swap_head = wrap == kWrapSwap && sigma != 0;
-  auto tok = [&](int j) { return swap_head ? token_of_row<true>(j, sigma, N, G) : orig_row(j, sigma, N); };
+  const WrapGroup wg = wrap_group(N, G);
+  auto tok = [&](int j) { return swap_head ? token_of_row<true>(j, sigma, N, wg) : orig_row(j, sigma, N); };
   const int ge = min(grp * G + G, N);           // end of the group (a last group may be short)
   const int j0 = grp * G + pos * BR;
   if (j0 >= ge) return;                         // a tile past the end of a short group
-  const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
+  const int kv_begin = first_key_row(j0, G, split_head, wg);  // first key row any wave sees
+  const int cut = split_cut(grp * G, split_head, wg);         // split option: rows from here see no key before
   const int ntiles = (min(j0 + BR, ge) - kv_begin + BC - 1) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
   const int jq = jw + l32;
   const bool q_ok = jq < ge;
   const int tq = tok(q_ok ? jq : ge - 1);
-  const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
+  const int kw0 = first_key_row(jw, G, split_head, wg);       // this wave's first key
   v8<T> qf[S::kDC], dof[S::kDC];
   {
     const T* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
     store_transposed<T, KRPT, TCPR>(Kt, kr, k_dc, k_kg * KRPT);
     __syncthreads();
     if (it + 1 < ntiles) load_tile(kt0 + BC);
-    if (kt0 > jw + 31 || kt0 < kw0 || jw >= ge) continue;   // nothing of this tile for this wave
+    if (kt0 > jw + 31 || kt0 + BC <= kw0 || jw >= ge) continue;   // nothing of this tile for this wave
 
     // S^T = K Q^T, dP^T = V dO^T : keys on tile rows, queries on lanes
     f32x16 s[2], dp[2];
@@ -391,13 +397,14 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dq(
         mma32(dp[ks], Vs[chunk_at<KCPR>(row, cc * 2 + hf)], dof[cc]);
       }
     }
-    const bool need_mask = kt0 + BC - 1 > jw;
+    const bool need_mask = kt0 + BC - 1 > jw || (kt0 < cut && jw + 31 >= cut);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(fmaf(s[ks][i], c2, -lse_q));
-        if (need_mask && kt0 + ks * 32 + (i >> 3) * 16 + hf * 8 + (i & 7) > jq) p = 0.f;
+        const int key = kt0 + ks * 32 + (i >> 3) * 16 + hf * 8 + (i & 7);
+        if (need_mask && (key > jq || (key < cut && jq >= cut))) p = 0.f;
         dp[ks][i] = p * (dp[ks][i] - dvec_q);
       }
     // dQ^T += K^T dS^T
@@ -549,6 +556,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   const int r = H / Hkv;
   const int h0 = c * r;
   const int sig0 = (h0 >= H - shift_heads) ? G / 2 : 0;
+  const WrapGroup wg = wrap_group(N, G);
   const int j0 = grp * G + pos * BKV;                 // key rows, rolled frame of head h0
   const int ge0 = EDGE ? min(grp * G + G, N) : grp * G + G;   // end of their group
   if (EDGE && j0 >= ge0) return;                      // a tile past the end of a short group
@@ -563,7 +571,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const int cb = (wave + S::kWaves * i) * 64;
     const int p = cb + lane;
     const int row = p / CPR, pc = p % CPR;
-    const size_t g = (size_t)token_of_row<SWAP>(EDGE ? min(j0 + row, N - 1) : j0 + row, sig0, N, G) * kvstride +
+    const size_t g = (size_t)token_of_row<SWAP>(EDGE ? min(j0 + row, N - 1) : j0 + row, sig0, N, wg) * kvstride +
                      (pc ^ swz2<CPR>(row)) * 8;
     load_lds16(kb + g, lds + S::kK + cb * 16);
     load_lds16(vb + g, lds + S::kV + cb * 16);
@@ -619,15 +627,17 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   int fr_jk0[2], fr_qb[2], fr_qe[2], fr_wqe[2], fr_qge[2];
 #pragma unroll
   for (int sh = 0; sh < 2; ++sh) {
-    const int jk = frame_row<SWAP>(j0, sig0, sh * (G / 2), N, G);
+    const int jk = frame_row<SWAP>(j0, sig0, sh * (G / 2), N, wg);
     const bool split_head = SPLIT && sh;
-    const int qge = query_end_row(jk, G, N, false);
+    const int qge = query_end_row(jk, G, N, false, wg);
     fr_jk0[sh] = jk;
     fr_qb[sh] = jk / BQ;
-    fr_qe[sh] = EDGE ? (min(query_end_row(jk + BKV - 32, G, N, false), qge) + BQ - 1) / BQ
-                     : query_end_row(jk + BKV - 32, G, N, split_head) / BQ;
-    fr_wqe[sh] = EDGE ? min(query_end_row(jk + kg * 32, G, N, false), qge)
-                      : query_end_row(jk + kg * 32, G, N, split_head);
+    // EDGE: the split option's cut may fall inside a 32-key run, whose later
+    // keys see queries at least as far: take the run's last key in the group
+    fr_qe[sh] = EDGE ? (min(query_end_row(min(jk + BKV - 1, qge - 1), G, N, split_head, wg), qge) + BQ - 1) / BQ
+                     : query_end_row(jk + BKV - 32, G, N, split_head, wg) / BQ;
+    fr_wqe[sh] = EDGE ? min(query_end_row(min(jk + kg * 32 + 31, qge - 1), G, N, split_head, wg), qge)
+                      : query_end_row(jk + kg * 32, G, N, split_head, wg);
     fr_qge[sh] = qge;
   }
   auto head_frame = [&](int hh, int& sig, int& jk0, int& qt_b, int& qt_e, int& wqe) {
@@ -641,27 +651,30 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   // EDGE: the group end; one frame only (a KV head shared by shifted and
   // unshifted query heads needs whole tiles)
   const int qge = fr_qge[sig0 != 0];
+  // EDGE with the split option: query rows from the cut on see no key row before it
+  const int cut = (EDGE && SPLIT) ? split_cut(fr_jk0[sig0 != 0] - fr_jk0[sig0 != 0] % G, sig0 != 0, wg) : -1;
   auto issue_step = [&](int hh, int qt, int sig, int stage) {
     const int h = h0 + hh;
-    // EDGE: a query tile that wraps from token N-1 to token 0, or runs past row
-    // N, takes each row's own address (rows past N read row N-1: masked)
-    if (EDGE && (qt * BQ + BQ > N || (sig != 0 && qt * BQ < N - sig && qt * BQ + BQ > N - sig))) {
+    // EDGE: a query tile whose rows are not consecutive tokens (it crosses the
+    // wrap from token N-1 to token 0, a break of the swap option's map, or row
+    // N) takes each row's own address (rows past N read row N-1: masked)
+    if (EDGE && !rows_contiguous<SWAP>(qt * BQ, BQ, sig, N, wg)) {
 #pragma unroll
       for (int i = 0; i < S::kQLoads; ++i) {
         const int p = (wave + S::kWaves * i) * 64 + lane;
         const int row = p / CPR, pc = p % CPR;
-        const size_t tok = token_of_row<SWAP>(min(qt * BQ + row, N - 1), sig, N, G);
+        const size_t tok = token_of_row<SWAP>(min(qt * BQ + row, N - 1), sig, N, wg);
         const size_t off = tok * qstride + (size_t)h * D + (pc ^ swz2<CPR>(row)) * 8;
         const int cb = (wave + S::kWaves * i) * 64 * 16;
         load_lds16(qbb + off, lds + S::kQ + stage * S::kQTileB + cb);
         load_lds16(dobb + off, lds + S::kdO + stage * S::kQTileB + cb);
       }
-      const size_t loff = (size_t)h * N + token_of_row<SWAP>(min(qt * BQ + lane, N - 1), sig, N, G);
+      const size_t loff = (size_t)h * N + token_of_row<SWAP>(min(qt * BQ + lane, N - 1), sig, N, wg);
       if (wave == 0) load_lds4(lbb + loff, lds + S::kF + stage * 2 * BQ * 4);
       if (wave == 1) load_lds4(dbb + loff, lds + S::kF + stage * 2 * BQ * 4 + BQ * 4);
       return;
     }
-    const size_t t0 = token_of_row<SWAP>(qt * BQ, sig, N, G);   // a 64-row tile is contiguous
+    const size_t t0 = token_of_row<SWAP>(qt * BQ, sig, N, wg);   // a 64-row tile is contiguous
     const size_t qo = t0 * qstride + (size_t)h * D;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(const_cast<bf16*>(qbb + qo), BQ * (int)qstride * 2);
     const __amdgpu_buffer_rsrc_t dors = make_rsrc(const_cast<bf16*>(dobb + qo), BQ * (int)qstride * 2);
@@ -715,7 +728,9 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
       for (int i = 0; i < 8; ++i) {
         const float lq = i < 4 ? l0[i] : l1[i - 4];
         float p = fast_exp2(fmaf(sacc[u * 8 + i], c2, -lq));
-        if (MASK && (jkey > jq_first + u * 16 + i || (EDGE && jq_first + u * 16 + i >= qge))) p = 0.f;
+        if (MASK && (jkey > jq_first + u * 16 + i || (EDGE && jq_first + u * 16 + i >= qge) ||
+                     (EDGE && SPLIT && jkey < cut && jq_first + u * 16 + i >= cut)))
+          p = 0.f;
         pv[i] = p;
         sv[i] = p * pacc[u * 8 + i];
       }
@@ -737,7 +752,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     if (key_lo > q_lo + 31) return;                   // every key follows every query: P = 0
     if ((SPLIT || EDGE) && q_lo >= wqe) return;       // queries of another group than the wave's keys
     const int jkey = key_lo + l32, jq_first = q_lo + hf * 8;
-    if (key_lo + 31 > q_lo || (EDGE && q_lo + 31 >= qge))
+    if (key_lo + 31 > q_lo || (EDGE && q_lo + 31 >= qge) || (EDGE && SPLIT && key_lo < cut && q_lo + 31 >= cut))
       compute(stg_c, std::integral_constant<bool, true>(), jkey, jq_first);
     else
       compute(stg_c, std::integral_constant<bool, false>(), jkey, jq_first);
@@ -795,7 +810,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
         dvacc[dt][i] += xs[((1 * S::kDT + dt) * 16 + i) * 64 + lane];
       }
     if (EDGE && j0 + key_row >= ge0) return;          // a key of the next group
-    const int tk = token_of_row<SWAP>(j0 + key_row, sig0, N, G);
+    const int tk = token_of_row<SWAP>(j0 + key_row, sig0, N, wg);
     bf16* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
     bf16* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
 #pragma unroll
@@ -839,7 +854,9 @@ struct DqB16Shape {
 
 // rope.on: q and k arrive rotated; dq is turned back before it is stored (the
 // gradient with respect to the unrotated q).
-template <int D, bool PREP, bool EDGE, bool SWAP>
+// CUT (with EDGE, the split option): the cut may fall inside a tile, masked
+// per element.
+template <int D, bool PREP, bool EDGE, bool SWAP, bool CUT>
 __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const bf16* __restrict__ o, const float* __restrict__ lse,
@@ -868,10 +885,13 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
   const bool split_head = split && sigma != 0;
+  const WrapGroup wg = wrap_group(N, G);
   const int ge = EDGE ? min(grp * G + G, N) : grp * G + G;   // end of the group
   const int j0 = grp * G + pos * BR;
   if (EDGE && j0 >= ge) return;                      // a tile past the end of a short group
-  const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
+  const int kv_begin = first_key_row(j0, G, split_head, wg);  // first key row any wave sees
+  // CUT: the split option's cut may fall inside a tile (per-element mask)
+  const int cut = CUT ? split_cut(grp * G, split_head, wg) : -1;
   const int ntiles = EDGE ? (min(j0 + BR, ge) - kv_begin + BC - 1) / BC : (j0 + BR - kv_begin) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
@@ -881,8 +901,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
   const bool q_ok = !EDGE || jq < ge;                // EDGE: rows past the group read its last row
-  const int tq = token_of_row<SWAP>(q_ok ? jq : ge - 1, sigma, N, G);
-  const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
+  const int tq = token_of_row<SWAP>(q_ok ? jq : ge - 1, sigma, N, wg);
+  const int kw0 = first_key_row(jw, G, split_head, wg);       // this wave's first key
   bf16x8 qf[S::kDC], dof[S::kDC];
   {
     const bf16* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
@@ -928,14 +948,15 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
   auto issue_tile = [&](int kt0, int stage) {
     char* kd = kbuf(stage);
     char* vd = vbuf(stage);
-    // EDGE: a tile whose rows wrap from token N-1 to token 0, or run past row
-    // N, takes each row's own 64-bit address (rows past N read row N-1: masked keys)
-    if (EDGE && (kt0 + BC > N || (sigma != 0 && kt0 < N - sigma && kt0 + BC > N - sigma))) {
+    // EDGE: a tile whose rows are not consecutive tokens (the wrap from token
+    // N-1 to token 0, a break of the swap option's map, or row N inside it)
+    // takes each row's own 64-bit address (rows past N read row N-1: masked keys)
+    if (EDGE && !rows_contiguous<SWAP>(kt0, BC, sigma, N, wg)) {
 #pragma unroll
       for (int i = 0; i < S::kLoads; ++i) {
         const int p = (wave + S::kWaves * i) * 64 + lane;
         const int row = p / CPR, pc = p % CPR;
-        const size_t tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, G);
+        const size_t tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, wg);
         const int cb = (wave + S::kWaves * i) * 64 * 16;
         const size_t off = tok * kvstride + (pc ^ swz2<CPR>(row)) * 8;
         load_lds16(kb + off, kd + cb);
@@ -944,7 +965,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
       return;
     }
     // a whole tile is contiguous: buffers based at its first row
-    const size_t t0 = token_of_row<SWAP>(kt0, sigma, N, G);
+    const size_t t0 = token_of_row<SWAP>(kt0, sigma, N, wg);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(const_cast<bf16*>(kb + t0 * kvstride), BC * (int)kvstride * 2);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(const_cast<bf16*>(vb + t0 * kvstride), BC * (int)kvstride * 2);
 #pragma unroll
@@ -1000,7 +1021,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float p = fast_exp2(fmaf(s[u * 8 + i], c2, -lse_q));
-          if (MASK && kt0 + ks * 32 + u * 16 + hf * 8 + i > jq) p = 0.f;
+          const int key = kt0 + ks * 32 + u * 16 + hf * 8 + i;
+          if (MASK && (key > jq || (CUT && key < cut && jq >= cut))) p = 0.f;
           dsv[i] = p * (dp[u * 8 + i] - dvec_q);
         }
         sf[2 * ks + u] = __builtin_convertvector(dsv, bf16x8);
@@ -1022,9 +1044,9 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
     wait_vmem_all();
     __syncthreads();
     if (it + 1 < ntiles) issue_tile(kt0 + BC, STG ^ 1);
-    if (kt0 > jw + 31 || kt0 < kw0) return;      // tile after this wave's queries, or outside its group
+    if (kt0 > jw + 31 || kt0 + BC <= kw0) return;   // tile after this wave's queries, or before its first key
     if (EDGE && jw >= ge) return;                // every query of this wave is past the group
-    if (kt0 + BC - 1 > jw)
+    if (kt0 + BC - 1 > jw || (CUT && kt0 < cut && jw + 31 >= cut))
       compute(stg_c, std::integral_constant<bool, true>(), kt0);
     else
       compute(stg_c, std::integral_constant<bool, false>(), kt0);
@@ -1070,18 +1092,18 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
                             int shift_heads, int wrap, float scale, RopeArgs rope, hipStream_t stream) {
   using S = DkdvB16Shape<D>;
   constexpr int BKV = S::kBKV;
-  const bool whole = N % G == 0 && G % BKV == 0;     // the split and swap options imply whole tiles
+  const bool whole = N % G == 0 && G % BKV == 0;
   const dim3 grid(whole ? B * Hkv * (N / BKV) : B * Hkv * ((N + G - 1) / G) * ((G + BKV - 1) / BKV));
   const dim3 block(S::kThreads);
 #define S2A_DKDV_LAUNCH(SPLIT, EDGE, SWAP)                                                                     \
   hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, SPLIT, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,     \
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk, (bf16*)dv, N, H, Hkv, \
                      G, shift_heads, scale, rope)
-  if (wrap == kWrapSplit)
-    S2A_DKDV_LAUNCH(true, false, false);
-  else if (wrap == kWrapSwap)
-    S2A_DKDV_LAUNCH(false, false, true);   // the swap option implies whole tiles too
-  else if (whole)
+  if (wrap == kWrapSplit) {
+    if (whole) S2A_DKDV_LAUNCH(true, false, false); else S2A_DKDV_LAUNCH(true, true, false);
+  } else if (wrap == kWrapSwap) {
+    if (whole) S2A_DKDV_LAUNCH(false, false, true); else S2A_DKDV_LAUNCH(false, true, true);
+  } else if (whole)
     S2A_DKDV_LAUNCH(false, false, false);
   else
     S2A_DKDV_LAUNCH(false, true, false);
@@ -1126,7 +1148,7 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
   const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR)), block(S::kThreads);
   const bf16* ob = (const bf16*)o;
 #define S2A_DQ_LAUNCH(PREP, EDGE, SWAP)                                                                       \
-  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, PREP, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,     \
+  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, PREP, EDGE, SWAP, false>), grid, block, 0, stream, (const bf16*)q, \
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec, (bf16*)dq, N, H, Hkv, \
                      G, shift_heads, (int)(wrap == kWrapSplit), scale, rope)
   if (wrap == kWrapSwap) {
@@ -1135,6 +1157,15 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
     } else {
       if (whole) S2A_DQ_LAUNCH(false, false, true); else S2A_DQ_LAUNCH(false, true, true);
     }
+  } else if (wrap == kWrapSplit && !whole) {
+    if (o)
+      hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, true, true, false, true>), grid, block, 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec, (bf16*)dq, N, H, Hkv,
+                         G, shift_heads, 1, scale, rope);
+    else
+      hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, false, true, false, true>), grid, block, 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec, (bf16*)dq, N, H, Hkv,
+                         G, shift_heads, 1, scale, rope);
   } else if (o) {
     if (whole) S2A_DQ_LAUNCH(true, false, false); else S2A_DQ_LAUNCH(true, true, false);
   } else {

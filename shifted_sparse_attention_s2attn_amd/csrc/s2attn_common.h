@@ -103,46 +103,64 @@ __device__ __forceinline__ int orig_row(int j, int sigma, int N) {
 // like Table 7's 1/6 of the context).
 __device__ __forceinline__ int num_groups(int N, int G) { return (N + G - 1) / G; }
 
-// Wrap option of the shifted heads (page section 5, "Ablation Studies and
-// Robustness Checks", Table 8 / Figure 6, Variant 2).  With `split_head` (the
-// option is on and the head is shifted), the last rolled group -- the last G/2
-// tokens followed by the first G/2, which the roll carried from the front --
-// is cut at G/2 into two causal groups; every other group is unchanged.
-// Rows are in the head's rolled frame and G/2 is a multiple of 32, so a run of
-// 32 rows starting at j lies in one half.
-// First key row visible to the query rows starting at j:
-__device__ __forceinline__ int first_key_row(int j, int G, int N, bool split_head) {
-  const int gs = j - j % G;
-  return (split_head && gs == N - G && j - gs >= G / 2) ? gs + G / 2 : gs;
-}
-// One past the last query row that sees the key rows starting at j (a group
-// that G does not fill ends at N):
-__device__ __forceinline__ int query_end_row(int j, int G, int N, bool split_head) {
-  const int gs = j - j % G;
-  return (split_head && gs == N - G && j - gs < G / 2) ? gs + G / 2 : min(gs + G, N);
+// The wrap group of a shifted head (rolled by sigma = floor(G/2)): the rolled
+// group in which the rolled order wraps from token N-1 to token 0.  It spans
+// rows [gw0, ge); rows [gw0, c) hold tokens gw0 + sigma .. N-1 and rows
+// [c, ge) the L = ge - c tokens 0 .. L-1 that the roll carried from the front,
+// with c = N - sigma.  When G divides N it is the last group (gw0 = N - G,
+// c = N - G/2, ge = N, L = G/2).  L = 0 when the wrap falls on a group
+// boundary: no group wraps.
+struct WrapGroup { int gw0, c, ge, L; };
+__device__ __forceinline__ WrapGroup wrap_group(int N, int G) {
+  const int c = N - G / 2;
+  const int gw0 = c - c % G;
+  const int ge = min(gw0 + G, N);
+  return {gw0, c, ge, c > gw0 ? ge - c : 0};
 }
 
 // Wrap options as the kernels take them (the values of s2attn_wrap).
 constexpr int kWrapRoll = 0, kWrapSplit = 1, kWrapSwap = 2;
 
-// Swap wrap option (Table 8 / Figure 6, Variant 3): in a shifted head the last
-// rolled group (rows N-G .. N-1) keeps its tokens, but the G/2 tokens the roll
-// carried from the front of the sequence come first, so that causal order in
-// that group is token order: rows N-G .. N-G/2-1 hold tokens 0 .. G/2-1 and
-// rows N-G/2 .. N-1 hold tokens N-G/2 .. N-1.  Whole groups only (G divides N,
-// G/2 a multiple of 64, so no 64-row tile straddles a break of the map).
+// Split wrap option (page section 5, "Ablation Studies and Robustness Checks",
+// Table 8 / Figure 6, Variant 2).  With `split_head` (the option is on and the
+// head is shifted) the wrap group is cut at row c into two causal groups: the
+// end tokens [gw0, c) and the front tokens [c, ge); every other group is
+// unchanged.  Rows are in the head's rolled frame.
+// First key row visible to query row j:
+__device__ __forceinline__ int first_key_row(int j, int G, bool split_head, const WrapGroup& wg) {
+  const int gs = j - j % G;
+  return (split_head && wg.L > 0 && gs == wg.gw0 && j >= wg.c) ? wg.c : gs;
+}
+// One past the last query row that sees key row j (a group that G does not
+// fill ends at N):
+__device__ __forceinline__ int query_end_row(int j, int G, int N, bool split_head, const WrapGroup& wg) {
+  const int gs = j - j % G;
+  return (split_head && wg.L > 0 && gs == wg.gw0 && j < wg.c) ? wg.c : min(gs + G, N);
+}
+// The split option's cut inside the group starting at row gs: query rows at or
+// after it see no key row before it.  -1 (no cut) for every other group.
+__device__ __forceinline__ int split_cut(int gs, bool split_head, const WrapGroup& wg) {
+  return (split_head && wg.L > 0 && gs == wg.gw0) ? wg.c : -1;
+}
+
+// Swap wrap option (Table 8 / Figure 6, Variant 3): in a shifted head the wrap
+// group keeps its tokens, but the L tokens the roll carried from the front of
+// the sequence come first, so that causal order in that group is token order:
+// rows gw0 .. gw0+L-1 hold tokens 0 .. L-1 and rows gw0+L .. ge-1 hold tokens
+// gw0 + sigma .. N-1.
 // Token held at rolled row j of a head rolled by sigma:
 template <bool SWAP>
-__device__ __forceinline__ int token_of_row(int j, int sigma, int N, int G) {
-  if (SWAP && sigma != 0 && j >= N - G) return j < N - G / 2 ? j - (N - G) : j;
+__device__ __forceinline__ int token_of_row(int j, int sigma, int N, const WrapGroup& wg) {
+  if (SWAP && sigma != 0 && j >= wg.gw0 && j < wg.ge && wg.L > 0)
+    return j < wg.gw0 + wg.L ? j - wg.gw0 : j - wg.L + sigma;
   return orig_row(j, sigma, N);
 }
 // ... and its inverse, the row of token t:
 template <bool SWAP>
-__device__ __forceinline__ int row_of_token(int t, int sigma, int N, int G) {
-  if (SWAP && sigma != 0) {
-    if (t < G / 2) return N - G + t;
-    if (t >= N - G / 2) return t;
+__device__ __forceinline__ int row_of_token(int t, int sigma, int N, const WrapGroup& wg) {
+  if (SWAP && sigma != 0 && wg.L > 0) {
+    if (t < wg.L) return wg.gw0 + t;
+    if (t >= wg.gw0 + sigma) return t - sigma + wg.L;
   }
   const int j = t - sigma;
   return j < 0 ? j + N : j;
@@ -151,12 +169,26 @@ __device__ __forceinline__ int row_of_token(int t, int sigma, int N, int G) {
 // The row that rolled row j of a head rolled by sig_from has in the frame of a
 // head rolled by sig_to (the same token).
 template <bool SWAP>
-__device__ __forceinline__ int frame_row(int j, int sig_from, int sig_to, int N, int G) {
-  if (SWAP) return row_of_token<true>(token_of_row<true>(j, sig_from, N, G), sig_to, N, G);
+__device__ __forceinline__ int frame_row(int j, int sig_from, int sig_to, int N, const WrapGroup& wg) {
+  if (SWAP) return row_of_token<true>(token_of_row<true>(j, sig_from, N, wg), sig_to, N, wg);
   int r = j + sig_from - sig_to;
   if (r < 0) r += N;
   if (r >= N) r -= N;
   return r;
+}
+
+// Whether rows [j, j + n) of a head rolled by sigma hold n consecutive tokens
+// (one buffer based at the first row's token then serves the whole tile): all
+// rows below N and no break of the row -> token map strictly inside.  Breaks:
+// row c (token N-1 -> 0) of the roll; under the swap option rows gw0, gw0 + L
+// and ge instead; and row N.
+template <bool SWAP>
+__device__ __forceinline__ bool rows_contiguous(int j, int n, int sigma, int N, const WrapGroup& wg) {
+  if (j + n > N) return false;
+  auto inside = [&](int r) { return j < r && r < j + n; };
+  if (sigma == 0) return true;
+  if (SWAP && wg.L > 0) return !inside(wg.gw0) && !inside(wg.gw0 + wg.L) && !inside(wg.ge);
+  return !inside(N - sigma);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -76,11 +76,13 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
 
   const bool split_head = wrap == kWrapSplit && sigma != 0;
   const bool swap_head = wrap == kWrapSwap && sigma != 0;
-  auto tok = [&](int j) { return swap_head ? token_of_row<true>(j, sigma, N, G) : orig_row(j, sigma, N); };
+  const WrapGroup wg = wrap_group(N, G);
+  auto tok = [&](int j) { return swap_head ? token_of_row<true>(j, sigma, N, wg) : orig_row(j, sigma, N); };
   const int ge = min(grp * G + G, N);           // end of the group (a last group may be short)
   const int j0 = grp * G + pos * BR;            // first query row (rolled)
   if (j0 >= ge) return;                         // a tile past the end of a short group
-  const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
+  const int kv_begin = first_key_row(j0, G, split_head, wg);  // first key row any wave sees
+  const int cut = split_cut(grp * G, split_head, wg);         // split option: rows from here see no key before
   const int ntiles = (min(j0 + BR, ge) - kv_begin + BC - 1) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
   const int jq = jw + l32;                      // this lane's query (rolled)
   const bool q_ok = jq < ge;                    // rows past the group compute on a copy, are not stored
   const int tq = tok(q_ok ? jq : ge - 1);
-  const int kw0 = first_key_row(jw, G, N, split_head);        // ... and this wave's first key
+  const int kw0 = first_key_row(jw, G, split_head, wg);       // ... and this wave's first key
   v8<T> qf[S::kDC];
 #pragma unroll
   for (int cc = 0; cc < S::kDC; ++cc)
@@ -155,8 +157,8 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
     __syncthreads();
     if (it + 1 < ntiles) load_tile(kt0 + BC);
 
-    if (kt0 > jw + 31 || kt0 < kw0 || jw >= ge) continue;   // nothing of this tile for this wave
-    const bool need_mask = kt0 + BC - 1 > jw;
+    if (kt0 > jw + 31 || kt0 + BC <= kw0 || jw >= ge) continue;   // nothing of this tile for this wave
+    const bool need_mask = kt0 + BC - 1 > jw || (kt0 < cut && jw + 31 >= cut);
 
     // S^T = K Q^T
     f32x16 s[S::kKS];
@@ -177,14 +179,16 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
       for (int r = 0; r < 16; ++r) {
         if (need_mask) {
           const int key = kt0 + ks * 32 + (r >> 3) * 16 + hf * 8 + (r & 7);
-          if (key > jq) s[ks][r] = -INFINITY;
+          if (key > jq || (key < cut && jq >= cut)) s[ks][r] = -INFINITY;
         }
         mloc = fmaxf(mloc, s[ks][r]);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);     // finite: the wave's first key is in its first tile
-    const float alpha = fast_exp2((m_run - m_new) * c2);
-    const float nm = -m_new * c2;
+    // m_new stays -inf for a row behind the split cut whose keys so far are all
+    // masked: then nothing is accumulated (alpha 0) and its p are 0
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c2);
+    const float nm = m_new == -INFINITY ? 0.f : -m_new * c2;
     float lsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < S::kKS; ++ks)
@@ -276,7 +280,9 @@ __device__ __forceinline__ int swz_v(int row) {
 // rope.on: q arrives unrotated; the kernel turns its Q rows by the rotary
 // embedding with Position Interpolation (k arrives rotated) and writes the
 // rotated rows to rope.q_rot for the backward.
-template <int D, bool EDGE, bool SWAP>
+// CUT (with EDGE, the split option): the cut may fall inside a tile, masked
+// per element.
+template <int D, bool EDGE, bool SWAP, bool CUT>
 __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse,
@@ -305,10 +311,14 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   const int c = h / (H / Hkv);
   const int sigma = (h >= H - shift_heads) ? G / 2 : 0;
   const bool split_head = split && sigma != 0;
+  const WrapGroup wg = wrap_group(N, G);
   const int ge = EDGE ? min(grp * G + G, N) : grp * G + G;   // end of the group
   const int j0 = grp * G + pos * BR;
   if (EDGE && j0 >= ge) return;                      // a tile past the end of a short group
-  const int kv_begin = first_key_row(j0, G, N, split_head);   // first key row any wave sees
+  const int kv_begin = first_key_row(j0, G, split_head, wg);  // first key row any wave sees
+  // CUT: the split option's cut may fall inside a tile; query rows at or
+  // after it see no key row before it (per element)
+  const int cut = CUT ? split_cut(grp * G, split_head, wg) : -1;
   const int ntiles = EDGE ? (min(j0 + BR, ge) - kv_begin + BC - 1) / BC : (j0 + BR - kv_begin) / BC;
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
@@ -319,8 +329,8 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   const int jw = j0 + wave * 32;
   const int jq = jw + l32;
   const bool q_ok = !EDGE || jq < ge;
-  const int tq = token_of_row<SWAP>(q_ok ? jq : ge - 1, sigma, N, G);
-  const int kw0 = first_key_row(jw, G, N, split_head);        // this wave's first key
+  const int tq = token_of_row<SWAP>(q_ok ? jq : ge - 1, sigma, N, wg);
+  const int kw0 = first_key_row(jw, G, split_head, wg);       // this wave's first key
   bf16x8 qf[S::kDC];
   {
     const bf16* qrow = q + ((size_t)b * N + tq) * qstride + (size_t)h * D;
@@ -365,14 +375,15 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   auto issue_tile = [&](int kt0, int stage) {
     char* kd = kbuf(stage);
     char* vd = vbuf(stage);
-    // EDGE: a tile whose rows wrap from token N-1 to token 0, or run past row
-    // N, takes each row's own 64-bit address (rows past N read row N-1: masked keys)
-    if (EDGE && (kt0 + BC > N || (sigma != 0 && kt0 < N - sigma && kt0 + BC > N - sigma))) {
+    // EDGE: a tile whose rows are not consecutive tokens (it crosses the wrap
+    // from token N-1 to token 0, a break of the swap option's map, or row N)
+    // takes each row's own 64-bit address (rows past N read row N-1: masked keys)
+    if (EDGE && !rows_contiguous<SWAP>(kt0, BC, sigma, N, wg)) {
 #pragma unroll
       for (int i = 0; i < S::kLoads; ++i) {
         const int p = (wave + S::kWaves * i) * 64 + lane;
         const int row = p / CPR, pc = p % CPR;
-        const size_t tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, G);
+        const size_t tok = token_of_row<SWAP>(min(kt0 + row, N - 1), sigma, N, wg);
         const int cb = (wave + S::kWaves * i) * 64 * 16;
         load_lds16(kb + tok * kvstride + (pc ^ swz_k<CPR>(row)) * 8, kd + cb);
         load_lds16(vb + tok * kvstride + (pc ^ swz_v<CPR>(row)) * 8, vd + cb);
@@ -380,7 +391,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
       return;
     }
     // a whole tile is contiguous: buffers based at its first row
-    const size_t t0 = token_of_row<SWAP>(kt0, sigma, N, G);
+    const size_t t0 = token_of_row<SWAP>(kt0, sigma, N, wg);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(const_cast<bf16*>(kb + t0 * kvstride), BC * (int)kvstride * 2);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(const_cast<bf16*>(vb + t0 * kvstride), BC * (int)kvstride * 2);
 #pragma unroll
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt0 + ks * 32 + (r >> 3) * 16 + hf * 8 + (r & 7);
-          if (key > jq) s[ks][r] = -INFINITY;
+          if (key > jq || (CUT && key < cut && jq >= cut)) s[ks][r] = -INFINITY;
         }
     }
     float mloc = -INFINITY;
@@ -446,7 +457,8 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     mloc = max_halves(mloc);
     if (wave_any((mloc - m_run) * c2 > 8.f)) {
       const float m_new = fmaxf(m_run, mloc);
-      const float alpha = fast_exp2((m_run - m_new) * c2);
+      // (CUT: m_run = -inf means nothing accumulated yet; scaling by 0 avoids -inf - -inf)
+      const float alpha = (CUT && m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c2);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < S::kDT; ++dt)
@@ -454,7 +466,9 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
       m_run = m_new;
     }
-    const float nm = -m_run * c2;
+    // CUT: a row behind the split cut may meet only masked keys in its first
+    // tiles (m_run still -inf): its p are 0 until its first key
+    const float nm = (CUT && m_run == -INFINITY) ? 0.f : -m_run * c2;
     bf16x8 pf[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -482,9 +496,9 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
     wait_vmem_all();                             // this lane's tile loads have landed
     __syncthreads();                             // ... and everyone's; the other stage is free
     if (it + 1 < ntiles) issue_tile(kt0 + BC, STG ^ 1);
-    if (kt0 > jw + 31 || kt0 < kw0) return;      // tile after this wave's queries, or outside its group
+    if (kt0 > jw + 31 || kt0 + BC <= kw0) return;   // tile after this wave's queries, or before its first key
     if (EDGE && jw >= ge) return;                // every query of this wave is past the group
-    if (kt0 + BC - 1 > jw)
+    if (kt0 + BC - 1 > jw || (CUT && kt0 < cut && jw + 31 >= cut))
       compute(stg_c, std::integral_constant<bool, true>(), kt0);
     else
       compute(stg_c, std::integral_constant<bool, false>(), kt0);
@@ -519,12 +533,15 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   const bool whole = N % G == 0 && G % BR == 0;
   const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
 #define S2A_FWD_LAUNCH(EDGE, SWAP)                                                                              \
-  hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,          \
+  hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, EDGE, SWAP, false>), grid, block, 0, stream, (const bf16*)q,   \
                      (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads,                \
                      (int)(wrap == kWrapSplit), scale, rope)
   if (wrap == kWrapSwap) {
     if (whole) S2A_FWD_LAUNCH(false, true);
     else S2A_FWD_LAUNCH(true, true);
+  } else if (wrap == kWrapSplit && !whole) {
+    hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, true, false, true>), grid, block, 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads, 1, scale, rope);
   } else {
     if (whole) S2A_FWD_LAUNCH(false, false);
     else S2A_FWD_LAUNCH(true, false);

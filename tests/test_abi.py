@@ -182,11 +182,10 @@ def test_wrap_option_validation(lib):
     bad[3] = 64                                          # shape errors come first (G > N)
     assert lib.s2attn_fwd_ex(None, None, None, None, None, *bad, 7, 0, None) == _lib.S2ATTN_ERR_SHAPE
     unaligned = list(dims)
-    unaligned[3] = 500                                   # split and swap need whole groups of whole tiles
+    unaligned[3] = 500                                   # split and swap take any shape
     for wrap in (_lib.S2ATTN_WRAP_SPLIT, _lib.S2ATTN_WRAP_SWAP):
-        assert lib.s2attn_fwd_ex(None, None, None, None, None, *unaligned, wrap, 0, None) == \
-            _lib.S2ATTN_ERR_UNSUPPORTED
-        assert lib.s2attn_bwd_ex(*([None] * 10), need, *unaligned, wrap, 0, None) == _lib.S2ATTN_ERR_UNSUPPORTED
+        assert lib.s2attn_fwd_ex(None, None, None, None, None, *unaligned, wrap, 0, None) == _lib.S2ATTN_ERR_NULL
+        assert lib.s2attn_bwd_ex(*([None] * 10), need, *unaligned, wrap, 0, None) == _lib.S2ATTN_ERR_NULL
     assert lib.s2attn_fwd_ex(None, None, None, None, None, *unaligned, _lib.S2ATTN_WRAP_ROLL, 0, None) == \
         _lib.S2ATTN_ERR_NULL
     empty = list(dims)

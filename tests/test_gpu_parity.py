@@ -141,13 +141,26 @@ def test_small_parity_unaligned(w):
     check_full(w, inp, out)
 
 
+# the split and swap options on the same shapes: the wrap group is the rolled
+# group containing the wrap from token N-1 to token 0 (not necessarily the last
+# one), and its cut (split) or the boundary between its front and end tokens
+# (swap) falls inside tiles of every kernel
+@pytest.mark.parametrize("wrap", ["split", "swap"])
+@pytest.mark.parametrize("w", UNALIGNED, ids=[w.name for w in UNALIGNED])
+def test_small_parity_unaligned_wrap_options(w, wrap):
+    say(f"case {w} wrap={wrap}")
+    inp = make_inputs(w, seed=13)
+    out = run_gpu(w, to_gpu(inp), wrap=wrap)
+    check_full(w, inp, out, wrap=wrap)
+
+
 def random_cases(n=24, seed=2024, wide=False):
     """Seeded random small problems over every option the ABI accepts: d, dtype,
     B, GQA ratio, shifted-head count, aligned and unaligned G, every wrap mode.
-    Combinations the ABI rejects (split, swap or a mixed-shift KV head on groups
-    that are not whole 128-row tiles, G/2 not whole tiles for a mixed KV head)
-    are redrawn.  ``wide``: larger batches, GQA ratios and groups (bf16 only,
-    N up to 4096)."""
+    Combinations the ABI rejects (a KV head shared by shifted and unshifted query
+    heads on groups or half groups that are not whole 128-row tiles) are
+    redrawn.  ``wide``: larger batches, GQA ratios and groups (bf16 only, N up to
+    4096)."""
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
@@ -165,8 +178,6 @@ def random_cases(n=24, seed=2024, wide=False):
         B = int(rng.choice([1, 2, 3] if wide else [1, 2]))
         aligned = N % G == 0 and G % 128 == 0
         wrap = str(rng.choice(["roll", "split", "swap"]))
-        if wrap != "roll" and not aligned:
-            continue
         if r > 1 and (H - S) % r != 0 and not (aligned and (G // 2) % 128 == 0):
             continue
         cases.append((small_workload(f"rand{len(cases)}", B=B, H=H, Hkv=Hkv, d=d, N=N, G=G, shift_heads=S,
@@ -290,6 +301,23 @@ def test_full_size_workload(name):
     check_global(w, t, out)
     for c, g0 in SAMPLES[name]:
         check_sampled(w, t, out, c, g0)
+
+
+@pytest.mark.parametrize("wrap", ["split", "swap"])
+def test_full_size_table7_sixth_group_wrap_options(wrap):
+    """Table 7's 1/6 group (G = 1365 at N = 8192, shift 682) with the split and
+    swap options: the wrap group is rolled group 5 (rows 6825..8189, the wrap
+    after row 7509, 680 front tokens), followed by the 2-row group 6; sampled
+    for a shifted head, with an unshifted head's group."""
+    w = WORKLOADS["llama2-7b-8k-g1365"]
+    say(f"case {w} wrap={wrap} (generating inputs on the GPU)")
+    t = make_inputs(w, seed=0, device="cuda")
+    out = run_gpu(w, t, wrap=wrap)
+    say("  kernels done")
+    for name, x in zip(("o", "lse", "dq", "dk", "dv"), out):
+        assert bool(torch.isfinite(x).all()), f"non-finite values in {name}"
+    for c, g0 in [(31, 5), (31, 6), (0, 5)]:
+        check_sampled(w, t, out, c, g0, wrap=wrap)
 
 
 def test_full_size_table7_sixth_group():
@@ -575,5 +603,7 @@ def test_rejected_shape_raises():
     q = torch.zeros((1, 500, 2, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(S2AttnError):
         s2attn_fwd(q, q, q, 1024, 1)            # group longer than the sequence
+    k = torch.zeros((1, 500, 1, 64), dtype=torch.bfloat16, device="cuda")
+    q3 = torch.zeros((1, 500, 2, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(S2AttnError):
-        s2attn_fwd(q, q, q, 100, 1, wrap="split")   # split needs whole groups of whole tiles
+        s2attn_fwd(q3, k, k, 100, 1)            # a KV head shared by a shifted and an unshifted head, G = 100
