@@ -15,7 +15,9 @@ standard-normal operands is timed as the practical matrix-core ceiling for
 data of this distribution, and the float64 CPU oracle is timed on a bounded
 sample of the same workload (rank 0, one GPU only).  The other workloads of
 the metric's N range (8k, 100k, and the 70B GQA shape at 32k) are then timed
-for a few steps each and reported under "range" (outside the timed region).
+and reported under "range" (outside the timed region): each is warmed up for
+at least half a second, so the clock has left the idle state the CPU timing
+leaves it in, and timed over at least a quarter second of steps.
 
 Prints one JSON line.
 """
@@ -163,6 +165,9 @@ def gemm_reference(torch, dev, n=16384, reps=5):
             "operands": "bf16, seeded standard normal", "library": "torch.matmul (hipBLASLt)"}
 
 
+WARM_S, TIMED_S = 0.5, 0.25
+
+
 def time_workload(torch, w, wrap, steps, warmup):
     """Forward and backward of one more workload (the same launches as the timed
     step), HIP events on the launch stream; per-kernel and per-pass averages."""
@@ -193,8 +198,21 @@ def time_workload(torch, w, wrap, steps, warmup):
         if ev:
             ev[3].record(stream)
 
-    for _ in range(warmup):
+    # Warm-up: at least `warmup` steps and at least WARM_S seconds of them, so
+    # the engine clock has left its idle state (the host-side oracle timing
+    # before this leaves the GPU idle for seconds); then at least `steps`
+    # steps and at least TIMED_S seconds' worth, so that short workloads are
+    # not timed over a few hundred microseconds.
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while n < warmup or time.perf_counter() - t0 < WARM_S:
         step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    per_step = (time.perf_counter() - t0) / n
+    steps = max(steps, min(int(TIMED_S / per_step) + 1, 2000))
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
