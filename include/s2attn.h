@@ -35,18 +35,21 @@
  * input.  Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  * stream); the library never allocates, frees or synchronises.  Errors raised
  * while kernels run surface at the caller's next synchronisation, as for any
- * HIP call.  The library holds no state (no flags, caches or allocations),
- * so every call is reentrant and may run from any host thread.
+ * HIP call.  Apart from s2attn_bwd_noalloc's scratch array (below: one device
+ * array per GPU and its address, looked up once per device under a
+ * std::call_once), the library holds no state, so every call is reentrant and
+ * may run from any host thread.
  *
  * Supported: d in {64, 128}; dtype bf16 (fp32 accumulation, P and dS rounded
  * to bf16 for the matrix cores) or fp32 (fp32 matrix cores throughout);
  * 1 <= G <= N.  bf16 runs one family of kernels laid out for the bf16 matrix
  * cores at every size and G (groups that are not whole 128-row tiles take
  * instantiations that address rows one by one near group ends); fp32 runs
- * kernels on the fp32 matrix cores.  When a key/value head is shared by shifted and unshifted
- * query heads (H - shift_heads not a multiple of H / Hkv), and for the split
- * and swap wrap options, the groups must be whole tiles (for the shared head,
- * G a multiple of 256).  Grids: B * H * ceil(N / G) * ceil(G / 128) < 2^31;
+ * kernels on the fp32 matrix cores.  Every wrap option runs on every shape.
+ * When a key/value head is shared by shifted and unshifted query heads
+ * (H - shift_heads not a multiple of H / Hkv), the groups must be whole tiles
+ * and G a multiple of 256 (the two frames, G/2 apart, then cut the key rows
+ * into the same tiles).  Grids: B * H * ceil(N / G) * ceil(G / 128) < 2^31;
  * one token row of q: H * d < 2^24 elements.
  * B == 0 or N == 0 is an empty problem: every call validates the other sizes,
  * then returns S2ATTN_OK without reading any pointer or touching the GPU.
@@ -70,8 +73,8 @@ typedef enum {
     S2ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
     S2ATTN_ERR_SHAPE = 2,        /* B or N < 0, H, Hkv, d or G <= 0, G > N (N > 0),
                                     shift_heads outside [0, H], H % Hkv != 0 */
-    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype or wrap option, the mixed-shift or
-                                    split / swap rule above, or the grid or H * d size limit */
+    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype or wrap option, the mixed-shift
+                                    rule above, or the grid or H * d size limit */
     S2ATTN_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError) */
     S2ATTN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
     S2ATTN_ERR_ALIGN = 6,        /* an element tensor pointer not 16-byte aligned, or lse not 4-byte */
