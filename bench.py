@@ -5,8 +5,9 @@
 
 A step is one forward (s2attn_fwd) and one backward (its two launches, as
 s2attn_bwd runs them: prep fused into dQ, then dK/dV) over one batch of seeded
-synthetic inputs already resident in HBM.  W untimed steps,
-then K steps between two device synchronisations; the wall time of those K
+synthetic inputs already resident in HBM.  Untimed steps for half a second
+(the clock ramp, so the engine clock has left its idle state), W untimed
+warm-up steps, then K steps between two device synchronisations; the wall time of those K
 steps gives ``value`` (effective TFLOP/s: group-local causal pairs only, 4d
 FLOP per pair forward, 10d backward).  HIP events recorded on the launch
 stream around every kernel launch give each kernel's average duration; the
@@ -301,6 +302,17 @@ def main():
         if ev:
             ev[3].record(stream)
 
+    # Clock ramp: untimed steps for at least WARM_S seconds, so the engine clock
+    # has left its idle state before the W warm-up steps (a short workload's
+    # few warm-up steps would otherwise be timed on a clock still rising);
+    # their count is reported as "clock_ramp_steps".
+    torch.cuda.synchronize()
+    t_ramp, ramp_steps = time.perf_counter(), 0
+    while time.perf_counter() - t_ramp < WARM_S:
+        step()
+        ramp_steps += 1
+        if ramp_steps % 8 == 0:
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
@@ -348,6 +360,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_steps": ramp_steps,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
