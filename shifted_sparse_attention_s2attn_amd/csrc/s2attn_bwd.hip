@@ -839,11 +839,11 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
 // lse * log2(e) itself and writes both to the workspace for the dK/dV stage.
 // EDGE: groups that are not whole tiles, as in the forward kernel.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int W = 8>
 struct DqB16Shape {
-  static constexpr int kWaves = 8;
-  static constexpr int kThreads = 512;
-  static constexpr int kBR = 256;
+  static constexpr int kWaves = W;
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kBR = 32 * W;
   static constexpr int kBC = 64;
   static constexpr int kCPR = D / 8;
   static constexpr int kTile = kBC * kCPR;               // chunks per K (or V) tile
@@ -856,13 +856,13 @@ struct DqB16Shape {
 // gradient with respect to the unrotated q).
 // CUT (with EDGE, the split option): the cut may fall inside a tile, masked
 // per element.
-template <int D, bool PREP, bool EDGE, bool SWAP, bool CUT>
-__global__ __launch_bounds__(512) void s2attn_bwd_dq_bf16(
+template <int D, int W, bool PREP, bool EDGE, bool SWAP, bool CUT>
+__global__ __launch_bounds__(64 * W, 8 / W) void s2attn_bwd_dq_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const bf16* __restrict__ o, const float* __restrict__ lse,
     float* __restrict__ lse2, float* __restrict__ dvec,
     bf16* __restrict__ dq, int N, int H, int Hkv, int G, int shift_heads, int split, float scale, RopeArgs rope) {
-  using S = DqB16Shape<D>;
+  using S = DqB16Shape<D, W>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTile;
   constexpr int RB = D * 2;
   // one LDS object per (stage, tensor), so reads of one stage are not made to
@@ -1136,43 +1136,56 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                                      stream);
 }
 
+// Wave count of a dq launch: as the forward's (8 waves for whole 256-row
+// tiles and long groups, 4 for short groups that are not whole tiles).
+inline int dq_waves(int N, int G) {
+  const bool whole = N % G == 0 && G % 256 == 0;
+  return (!whole && G % 256 != 0 && G < 4096) ? 4 : 8;
+}
+
+template <int D, int W>
+hipError_t launch_dq_bf16_w(const void* q, const void* k, const void* v, const void* dO, const void* o,
+                            const float* lse, float* lse2, float* dvec, void* dq, int B, int H, int Hkv, int N,
+                            int G, int shift_heads, int wrap, float scale, hipStream_t stream, RopeArgs rope) {
+  using S = DqB16Shape<D, W>;
+  constexpr int BR = S::kBR;
+  const bool whole = N % G == 0 && G % BR == 0;
+  const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR)), block(S::kThreads);
+  const bf16* ob = (const bf16*)o;
+#define S2A_DQ_LAUNCH(PREP, EDGE, SWAP, CUT)                                                                  \
+  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, W, PREP, EDGE, SWAP, CUT>), grid, block, 0, stream,             \
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec,    \
+                     (bf16*)dq, N, H, Hkv, G, shift_heads, (int)(wrap == kWrapSplit), scale, rope)
+#define S2A_DQ_LAUNCH_P(EDGE, SWAP, CUT) \
+  do {                                   \
+    if (o) S2A_DQ_LAUNCH(true, EDGE, SWAP, CUT); \
+    else S2A_DQ_LAUNCH(false, EDGE, SWAP, CUT);  \
+  } while (0)
+  if constexpr (W == 8) {
+    if (whole) {
+      if (wrap == kWrapSwap) S2A_DQ_LAUNCH_P(false, true, false);
+      else S2A_DQ_LAUNCH_P(false, false, false);
+      return hipGetLastError();
+    }
+  }
+  if (wrap == kWrapSwap) S2A_DQ_LAUNCH_P(true, true, false);
+  else if (wrap == kWrapSplit) S2A_DQ_LAUNCH_P(true, false, true);
+  else S2A_DQ_LAUNCH_P(true, false, false);
+#undef S2A_DQ_LAUNCH_P
+#undef S2A_DQ_LAUNCH
+  return hipGetLastError();
+}
+
 // o and lse non-NULL: prep fused in (writes lse2 and dvec); else reads them.
 template <int D>
 hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO, const void* o,
                           const float* lse, float* lse2, float* dvec, void* dq, int B, int H, int Hkv, int N, int G,
                           int shift_heads, int wrap, float scale, hipStream_t stream,
                           RopeArgs rope = RopeArgs{nullptr, 0, 0, 0}) {
-  using S = DqB16Shape<D>;
-  constexpr int BR = S::kBR;
-  const bool whole = N % G == 0 && G % BR == 0;
-  const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR)), block(S::kThreads);
-  const bf16* ob = (const bf16*)o;
-#define S2A_DQ_LAUNCH(PREP, EDGE, SWAP)                                                                       \
-  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, PREP, EDGE, SWAP, false>), grid, block, 0, stream, (const bf16*)q, \
-                     (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec, (bf16*)dq, N, H, Hkv, \
-                     G, shift_heads, (int)(wrap == kWrapSplit), scale, rope)
-  if (wrap == kWrapSwap) {
-    if (o) {
-      if (whole) S2A_DQ_LAUNCH(true, false, true); else S2A_DQ_LAUNCH(true, true, true);
-    } else {
-      if (whole) S2A_DQ_LAUNCH(false, false, true); else S2A_DQ_LAUNCH(false, true, true);
-    }
-  } else if (wrap == kWrapSplit && !whole) {
-    if (o)
-      hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, true, true, false, true>), grid, block, 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec, (bf16*)dq, N, H, Hkv,
-                         G, shift_heads, 1, scale, rope);
-    else
-      hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, false, true, false, true>), grid, block, 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec, (bf16*)dq, N, H, Hkv,
-                         G, shift_heads, 1, scale, rope);
-  } else if (o) {
-    if (whole) S2A_DQ_LAUNCH(true, false, false); else S2A_DQ_LAUNCH(true, true, false);
-  } else {
-    if (whole) S2A_DQ_LAUNCH(false, false, false); else S2A_DQ_LAUNCH(false, true, false);
-  }
-#undef S2A_DQ_LAUNCH
-  return hipGetLastError();
+  return dq_waves(N, G) == 4 ? launch_dq_bf16_w<D, 4>(q, k, v, dO, o, lse, lse2, dvec, dq, B, H, Hkv, N, G,
+                                                      shift_heads, wrap, scale, stream, rope)
+                             : launch_dq_bf16_w<D, 8>(q, k, v, dO, o, lse, lse2, dvec, dq, B, H, Hkv, N, G,
+                                                      shift_heads, wrap, scale, stream, rope);
 }
 
 template <typename T, int D>

@@ -245,11 +245,11 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
 // exp2 units), so the accumulator is rarely rescaled; P stays <= 256.
 // Row sums are taken on the bf16 P actually fed to the matrix cores.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int W = 8>
 struct FwdB16Shape {
-  static constexpr int kWaves = 8;
-  static constexpr int kThreads = 512;
-  static constexpr int kBR = 256;
+  static constexpr int kWaves = W;
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kBR = 32 * W;
   static constexpr int kBC = 64;
   static constexpr int kCPR = D / 8;                      // 16-byte chunks per tile row
   static constexpr int kTileChunks = kBC * kCPR;
@@ -282,12 +282,12 @@ __device__ __forceinline__ int swz_v(int row) {
 // rotated rows to rope.q_rot for the backward.
 // CUT (with EDGE, the split option): the cut may fall inside a tile, masked
 // per element.
-template <int D, bool EDGE, bool SWAP, bool CUT>
-__global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
+template <int D, int W, bool EDGE, bool SWAP, bool CUT>
+__global__ __launch_bounds__(64 * W, 8 / W) void s2attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse,
     int N, int H, int Hkv, int G, int shift_heads, int split, float scale, RopeArgs rope) {
-  using S = FwdB16Shape<D>;
+  using S = FwdB16Shape<D, W>;
   constexpr int BR = S::kBR, BC = S::kBC, CPR = S::kCPR, TC = S::kTileChunks;
   constexpr int RB = D * 2;                       // bytes per tile row
   // one LDS object per (stage, tensor): the compiler then sees that reads of one
@@ -524,30 +524,49 @@ __global__ __launch_bounds__(512) void s2attn_fwd_bf16_kernel(
   if (hf == 0) lse[((size_t)b * H + h) * N + tq] = m_run * scale + logf(l_tot);
 }
 
+// Wave count of a launch.  Whole tiles of whole groups: 8 waves (256 query
+// rows: each K/V tile serves twice as many queries as with 4).  Groups that
+// are not whole 256-row tiles and shorter than 4096 rows: 4 waves (128 rows,
+// two workgroups per CU), so less of each group's partial tile and diagonal
+// block sits idle.
+inline int fwd_waves(int N, int G) {
+  const bool whole = N % G == 0 && G % 256 == 0;
+  return (!whole && G % 256 != 0 && G < 4096) ? 4 : 8;
+}
+
+template <int D, int W>
+hipError_t launch_fwd_bf16_w(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Hkv, int N, int G, int shift_heads, int wrap, float scale,
+                             RopeArgs rope, hipStream_t stream) {
+  constexpr int BR = FwdB16Shape<D, W>::kBR;
+  const dim3 block(FwdB16Shape<D, W>::kThreads);
+  const bool whole = N % G == 0 && G % BR == 0;
+  const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
+#define S2A_FWD_LAUNCH(EDGE, SWAP, CUT)                                                                        \
+  hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, W, EDGE, SWAP, CUT>), grid, block, 0, stream, (const bf16*)q,  \
+                     (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads,                \
+                     (int)(wrap == kWrapSplit), scale, rope)
+  if constexpr (W == 8) {
+    if (whole) {
+      if (wrap == kWrapSwap) S2A_FWD_LAUNCH(false, true, false);
+      else S2A_FWD_LAUNCH(false, false, false);
+      return hipGetLastError();
+    }
+  }
+  if (wrap == kWrapSwap) S2A_FWD_LAUNCH(true, true, false);
+  else if (wrap == kWrapSplit) S2A_FWD_LAUNCH(true, false, true);
+  else S2A_FWD_LAUNCH(true, false, false);
+#undef S2A_FWD_LAUNCH
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Hkv, int N, int G, int shift_heads, int wrap, float scale,
                            RopeArgs rope, hipStream_t stream) {
-  constexpr int BR = FwdB16Shape<D>::kBR;
-  const dim3 block(FwdB16Shape<D>::kThreads);
-  const bool whole = N % G == 0 && G % BR == 0;
-  const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
-#define S2A_FWD_LAUNCH(EDGE, SWAP)                                                                              \
-  hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, EDGE, SWAP, false>), grid, block, 0, stream, (const bf16*)q,   \
-                     (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads,                \
-                     (int)(wrap == kWrapSplit), scale, rope)
-  if (wrap == kWrapSwap) {
-    if (whole) S2A_FWD_LAUNCH(false, true);
-    else S2A_FWD_LAUNCH(true, true);
-  } else if (wrap == kWrapSplit && !whole) {
-    hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, true, false, true>), grid, block, 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads, 1, scale, rope);
-  } else {
-    if (whole) S2A_FWD_LAUNCH(false, false);
-    else S2A_FWD_LAUNCH(true, false);
-  }
-#undef S2A_FWD_LAUNCH
-  return hipGetLastError();
+  return fwd_waves(N, G) == 4
+             ? launch_fwd_bf16_w<D, 4>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, scale, rope, stream)
+             : launch_fwd_bf16_w<D, 8>(q, k, v, o, lse, B, H, Hkv, N, G, shift_heads, wrap, scale, rope, stream);
 }
 
 // bf16: the kernel above at every size; fp32: the fp32 kernel.

@@ -122,9 +122,14 @@ def test_small_parity_swap(w):
 
 # group sizes that do not divide the sequence, or are not whole 128-row tiles
 # (EDGE instantiations of the bf16 kernels, generic kernels for fp32): the last
-# group is short, the shift floor(G/2)
+# group is short, the shift floor(G/2).  The forward and dq run 4-wave
+# workgroups (128 query rows) for groups shorter than 4096 that are not whole
+# 256-row tiles, 8-wave ones otherwise: both counts appear below.
 UNALIGNED = [
     small_workload("bf16-short-last-group", B=1, H=4, Hkv=4, d=128, N=1000, G=256, shift_heads=2),
+    # G not a multiple of 256 but long enough that the forward and dq keep 8
+    # waves (256-row tiles): partial tiles in every group, a short last group
+    small_workload("bf16-g4100", B=1, H=2, Hkv=2, d=128, N=9000, G=4100, shift_heads=1),
     small_workload("bf16-g100-gqa", B=2, H=2, Hkv=1, d=64, N=777, G=100, shift_heads=2),
     small_workload("bf16-table7-sixth", B=1, H=2, Hkv=2, d=128, N=8192, G=1365, shift_heads=1),
     small_workload("bf16-g3", B=1, H=2, Hkv=2, d=64, N=100, G=3, shift_heads=1),
