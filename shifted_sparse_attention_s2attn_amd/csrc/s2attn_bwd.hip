@@ -507,10 +507,12 @@ __device__ __forceinline__ void store_turned_back(bf16* row, const f32x16* acc, 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       bf16x8 ya, yb;
+      double g[8];
+      rope_revs8<D>(dt * 32 + u * 16 + hf * 8, log2_base, g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float cs, sn, y0, y1;
-        rope_cs(pos, rope_rev_per_pos<D>(dt * 32 + u * 16 + hf * 8 + e, log2_base), cs, sn);
+        rope_cs(pos, g[e], cs, sn);
         rope_turn(acc[dt][u * 8 + e] * scale, acc[dt + HT][u * 8 + e] * scale, cs, -sn, y0, y1);
         ya[e] = (bf16)y0;
         yb[e] = (bf16)y1;
@@ -526,10 +528,10 @@ __device__ __forceinline__ void store_turned_back(bf16* row, const f32x16* acc, 
 // stored); SWAP: the swap wrap option's row map (token_of_row).  Each is
 // compiled separately, so that the main method's step loop carries no trace
 // of any of them.
-// rope.on: q and k arrive rotated by the rotary embedding; dk is turned back
+// ROPE (launched for rope.on): q and k arrive rotated by the rotary embedding; dk is turned back
 // (the transpose of the rotation) before it is stored, so it is the gradient
 // with respect to the unrotated k.
-template <int D, bool SPLIT, bool EDGE, bool SWAP>
+template <int D, bool SPLIT, bool EDGE, bool SWAP, bool ROPE>
 __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
@@ -818,7 +820,7 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         *reinterpret_cast<bf16x8*>(dvrow + dt * 32 + u * 16 + hf * 8) = pack8<bf16>(dvacc[dt], u * 8);
-    if (rope.on) {
+    if (ROPE) {
       store_turned_back<D>(dkrow, dkacc, scale, (double)tk * rope.pos_scale, rope.log2_base, hf);
       return;
     }
@@ -852,11 +854,11 @@ struct DqB16Shape {
   static constexpr int kDT = D / 32;
 };
 
-// rope.on: q and k arrive rotated; dq is turned back before it is stored (the
+// ROPE (launched for rope.on): q and k arrive rotated; dq is turned back before it is stored (the
 // gradient with respect to the unrotated q).
 // CUT (with EDGE, the split option): the cut may fall inside a tile, masked
 // per element.
-template <int D, int W, bool PREP, bool EDGE, bool SWAP, bool CUT>
+template <int D, int W, bool PREP, bool EDGE, bool SWAP, bool CUT, bool ROPE>
 __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_bwd_dq_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const bf16* __restrict__ o, const float* __restrict__ lse,
@@ -1062,7 +1064,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_bwd_dq_bf16(
 
   if (!q_ok) return;
   bf16* dqrow = dq + ((size_t)b * N + tq) * qstride + (size_t)h * D;
-  if (rope.on) {
+  if (ROPE) {
     store_turned_back<D>(dqrow, dqacc, scale, (double)tq * rope.pos_scale, rope.log2_base, hf);
     return;
   }
@@ -1095,10 +1097,15 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
   const bool whole = N % G == 0 && G % BKV == 0;
   const dim3 grid(whole ? B * Hkv * (N / BKV) : B * Hkv * ((N + G - 1) / G) * ((G + BKV - 1) / BKV));
   const dim3 block(S::kThreads);
-#define S2A_DKDV_LAUNCH(SPLIT, EDGE, SWAP)                                                                     \
-  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, SPLIT, EDGE, SWAP>), grid, block, 0, stream, (const bf16*)q,     \
-                     (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk, (bf16*)dv, N, H, Hkv, \
-                     G, shift_heads, scale, rope)
+#define S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, ROPE)                                                             \
+  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, SPLIT, EDGE, SWAP, ROPE>), grid, block, 0, stream,              \
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk,   \
+                     (bf16*)dv, N, H, Hkv, G, shift_heads, scale, rope)
+#define S2A_DKDV_LAUNCH(SPLIT, EDGE, SWAP)                    \
+  do {                                                        \
+    if (rope.on) S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, true);  \
+    else S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, false);         \
+  } while (0)
   if (wrap == kWrapSplit) {
     if (whole) S2A_DKDV_LAUNCH(true, false, false); else S2A_DKDV_LAUNCH(true, true, false);
   } else if (wrap == kWrapSwap) {
@@ -1108,6 +1115,7 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
   else
     S2A_DKDV_LAUNCH(false, true, false);
 #undef S2A_DKDV_LAUNCH
+#undef S2A_DKDV_LAUNCH_R
   return hipGetLastError();
 }
 
@@ -1152,14 +1160,16 @@ hipError_t launch_dq_bf16_w(const void* q, const void* k, const void* v, const v
   const bool whole = N % G == 0 && G % BR == 0;
   const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR)), block(S::kThreads);
   const bf16* ob = (const bf16*)o;
-#define S2A_DQ_LAUNCH(PREP, EDGE, SWAP, CUT)                                                                  \
-  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, W, PREP, EDGE, SWAP, CUT>), grid, block, 0, stream,             \
+#define S2A_DQ_LAUNCH(PREP, EDGE, SWAP, CUT, ROPE)                                                            \
+  hipLaunchKernelGGL((s2attn_bwd_dq_bf16<D, W, PREP, EDGE, SWAP, CUT, ROPE>), grid, block, 0, stream,       \
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, ob, lse, lse2, dvec,    \
                      (bf16*)dq, N, H, Hkv, G, shift_heads, (int)(wrap == kWrapSplit), scale, rope)
-#define S2A_DQ_LAUNCH_P(EDGE, SWAP, CUT) \
-  do {                                   \
-    if (o) S2A_DQ_LAUNCH(true, EDGE, SWAP, CUT); \
-    else S2A_DQ_LAUNCH(false, EDGE, SWAP, CUT);  \
+  // the rotary route runs with the prep fused in (s2attn_bwd_rope)
+#define S2A_DQ_LAUNCH_P(EDGE, SWAP, CUT)                       \
+  do {                                                         \
+    if (o && rope.on) S2A_DQ_LAUNCH(true, EDGE, SWAP, CUT, true); \
+    else if (o) S2A_DQ_LAUNCH(true, EDGE, SWAP, CUT, false);   \
+    else S2A_DQ_LAUNCH(false, EDGE, SWAP, CUT, false);         \
   } while (0)
   if constexpr (W == 8) {
     if (whole) {

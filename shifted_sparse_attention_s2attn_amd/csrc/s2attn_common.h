@@ -201,10 +201,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // by n * pos_scale * base^(-2i/D) radians.  One set of helpers serves the
 // stand-alone pass and the attention kernels that fuse the rotation, so the two
 // produce the same bits.
-// Revolutions per position of pair i (float64):
+// Revolutions per position of the 8 pairs i0 .. i0+7 (i0 a multiple of 8),
+// float64: base^(-2 i0 / D) / (2 pi) from one exp2, then successive products
+// with base^(-2/D) (7 roundings: a relative error below 1e-15, ~1e-11
+// revolutions at positions near 1e5), so each run of 8 costs two exp2 instead
+// of eight.  Every kernel takes its frequencies from here.
 template <int D>
-__device__ __forceinline__ double rope_rev_per_pos(int i, double log2_base) {
-  return exp2(-(2.0 * i / D) * log2_base) * 0.15915494309189533577;
+__device__ __forceinline__ void rope_revs8(int i0, double log2_base, double g[8]) {
+  const double r = exp2(-(2.0 / D) * log2_base);
+  g[0] = exp2(-(2.0 * i0 / D) * log2_base) * 0.15915494309189533577;
+#pragma unroll
+  for (int e = 1; e < 8; ++e) g[e] = g[e - 1] * r;
 }
 // Cosine and sine of pos * g revolutions, pos = n * pos_scale: the angle is
 // formed in float64 and reduced to [-1/2, 1/2] revolutions (a float32 angle

@@ -277,12 +277,12 @@ __device__ __forceinline__ int swz_v(int row) {
 // loaded with per-row addresses.  Compiled separately from the whole-tile case.
 // SWAP: the swap wrap option's row map (token_of_row); `split` is 1 for the
 // split option.
-// rope.on: q arrives unrotated; the kernel turns its Q rows by the rotary
+// ROPE (launched for rope.on): q arrives unrotated; the kernel turns its Q rows by the rotary
 // embedding with Position Interpolation (k arrives rotated) and writes the
 // rotated rows to rope.q_rot for the backward.
 // CUT (with EDGE, the split option): the cut may fall inside a tile, masked
 // per element.
-template <int D, int W, bool EDGE, bool SWAP, bool CUT>
+template <int D, int W, bool EDGE, bool SWAP, bool CUT, bool ROPE>
 __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse,
@@ -337,17 +337,19 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_fwd_bf16_kernel(
 #pragma unroll
     for (int cc = 0; cc < S::kDC; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(qrow + cc * 16 + hf * 8);
   }
-  if (rope.on) {
+  if (ROPE) {
     // element i < D/2 of the row sits in chunk i / 16 and its partner i + D/2 in
     // chunk i / 16 + D/32 of the same lane: the rotation is lane-local
     const double pos = (double)tq * rope.pos_scale;
 #pragma unroll
     for (int cc = 0; cc < S::kDC / 2; ++cc) {
       bf16x8 ya, yb;
+      double g[8];
+      rope_revs8<D>(cc * 16 + hf * 8, rope.log2_base, g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float cs, sn, y0, y1;
-        rope_cs(pos, rope_rev_per_pos<D>(cc * 16 + hf * 8 + e, rope.log2_base), cs, sn);
+        rope_cs(pos, g[e], cs, sn);
         rope_turn((float)qf[cc][e], (float)qf[cc + S::kDC / 2][e], cs, sn, y0, y1);
         ya[e] = (bf16)y0;
         yb[e] = (bf16)y1;
@@ -542,10 +544,15 @@ hipError_t launch_fwd_bf16_w(const void* q, const void* k, const void* v, void* 
   const dim3 block(FwdB16Shape<D, W>::kThreads);
   const bool whole = N % G == 0 && G % BR == 0;
   const dim3 grid(whole ? B * H * (N / BR) : B * H * ((N + G - 1) / G) * ((G + BR - 1) / BR));
-#define S2A_FWD_LAUNCH(EDGE, SWAP, CUT)                                                                        \
-  hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, W, EDGE, SWAP, CUT>), grid, block, 0, stream, (const bf16*)q,  \
-                     (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads,                \
+#define S2A_FWD_LAUNCH_R(EDGE, SWAP, CUT, ROPE)                                                                \
+  hipLaunchKernelGGL((s2attn_fwd_bf16_kernel<D, W, EDGE, SWAP, CUT, ROPE>), grid, block, 0, stream,           \
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, H, Hkv, G, shift_heads, \
                      (int)(wrap == kWrapSplit), scale, rope)
+#define S2A_FWD_LAUNCH(EDGE, SWAP, CUT)        \
+  do {                                         \
+    if (rope.on) S2A_FWD_LAUNCH_R(EDGE, SWAP, CUT, true); \
+    else S2A_FWD_LAUNCH_R(EDGE, SWAP, CUT, false);        \
+  } while (0)
   if constexpr (W == 8) {
     if (whole) {
       if (wrap == kWrapSwap) S2A_FWD_LAUNCH(false, true, false);
@@ -557,6 +564,7 @@ hipError_t launch_fwd_bf16_w(const void* q, const void* k, const void* v, void* 
   else if (wrap == kWrapSplit) S2A_FWD_LAUNCH(true, false, true);
   else S2A_FWD_LAUNCH(true, false, false);
 #undef S2A_FWD_LAUNCH
+#undef S2A_FWD_LAUNCH_R
   return hipGetLastError();
 }
 

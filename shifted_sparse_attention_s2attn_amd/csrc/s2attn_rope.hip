@@ -34,8 +34,7 @@ __global__ __launch_bounds__(256) void s2attn_rope_kernel(const T* x, T* y, I ro
   constexpr int RPB = 256 / TPR;              // rows per block per pass
   const int c = threadIdx.x % TPR;
   double g[8];                                // revolutions per position of each pair
-#pragma unroll
-  for (int e = 0; e < 8; ++e) g[e] = rope_rev_per_pos<D>(8 * c + e, log2_base);
+  rope_revs8<D>(8 * c, log2_base, g);
   for (I r = (I)blockIdx.x * RPB + threadIdx.x / TPR; r < rows; r += (I)gridDim.x * RPB) {
     const int n = (int)((r / (I)Hx) % (I)N);  // rows are (batch, token, head), token-major
     const double pos = (double)n * pos_scale;
