@@ -278,8 +278,8 @@ __device__ __forceinline__ int swz_v(int row) {
 // SWAP: the swap wrap option's row map (token_of_row); `split` is 1 for the
 // split option.
 // ROPE (launched for rope.on): q arrives unrotated; the kernel turns its Q rows by the rotary
-// embedding with Position Interpolation (k arrives rotated) and writes the
-// rotated rows to rope.q_rot for the backward.
+// embedding with Position Interpolation (k arrives rotated) and, after its
+// key loop, writes the rotated rows to rope.q_rot for the backward.
 // CUT (with EDGE, the split option): the cut may fall inside a tile, masked
 // per element.
 template <int D, int W, bool EDGE, bool SWAP, bool CUT, bool ROPE>
@@ -356,11 +356,6 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_fwd_bf16_kernel(
       }
       qf[cc] = ya;
       qf[cc + S::kDC / 2] = yb;
-    }
-    if (q_ok) {
-      bf16* qr = rope.q_rot + ((size_t)b * N + tq) * qstride + (size_t)h * D;
-#pragma unroll
-      for (int cc = 0; cc < S::kDC; ++cc) *reinterpret_cast<bf16x8*>(qr + cc * 16 + hf * 8) = qf[cc];
     }
   }
 
@@ -516,6 +511,13 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_fwd_bf16_kernel(
 
   const float l_tot = sum_halves(l_run);
   if (!q_ok) return;
+  if (ROPE) {
+    // the rotated rows for the backward, written here rather than before the
+    // loop, where the stores would compete with the first tiles' loads
+    bf16* qr = rope.q_rot + ((size_t)b * N + tq) * qstride + (size_t)h * D;
+#pragma unroll
+    for (int cc = 0; cc < S::kDC; ++cc) *reinterpret_cast<bf16x8*>(qr + cc * 16 + hf * 8) = qf[cc];
+  }
   const float inv = 1.f / l_tot;
   bf16* orow = o + ((size_t)b * N + tq) * qstride + (size_t)h * D;
 #pragma unroll
