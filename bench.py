@@ -35,16 +35,26 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "shifted_sparse_attention_s2attn_amd", "csrc")
 
 
+def _code_only(text):
+    """C++ source without its comments and blank lines, each line stripped, so
+    that an edit of a comment does not count as a change of the kernels."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).strip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_hash():
     """Hash of the device code and its launchers: every csrc file except
-    s2attn_api.hip, which only validates arguments before calling them."""
+    s2attn_api.hip, which only validates arguments before calling them;
+    comments and layout are ignored."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name == "s2attn_api.hip":
             continue
-        with open(os.path.join(CSRC, name), "rb") as f:
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

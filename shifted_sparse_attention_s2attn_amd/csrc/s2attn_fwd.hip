@@ -234,11 +234,14 @@ __global__ __launch_bounds__(256) void s2attn_fwd_kernel(
 // bf16 forward (any G: whole 256-row query tiles of whole groups, or the EDGE
 // instantiation below).
 //
-// 8 waves (two per SIMD, so one wave's matrix-core work overlaps another's
-// softmax) share each 64-row key/value tile; each wave owns 32 query rows.
-// Key and value tiles go from HBM straight into LDS (global_load_lds, no
-// register staging), double-buffered with one barrier per tile; a 64-row tile
-// never straddles the roll's wrap point, so its base row is one scalar.
+// W waves share each 64-row key/value tile; each wave owns 32 query rows, so a
+// workgroup covers 32 W query rows.  W = 8 (256 rows, one workgroup and two
+// waves per SIMD, so one wave's matrix-core work overlaps another's softmax)
+// except for short groups that are not whole tiles, which take W = 4 (128
+// rows, two workgroups per CU).  Key and value tiles go from HBM straight into
+// LDS (buffer loads to LDS, no register staging), double-buffered with one
+// barrier per tile, each through a buffer descriptor based at its first row;
+// a tile whose rows are not consecutive tokens (EDGE) is loaded row by row.
 // V stays row-major in LDS: the V^T operand is read with ds_read_b64_tr_b16,
 // whose 16-lane groups return 4 consecutive keys of one head-dim column.
 // The running max is only raised when a tile exceeds it by more than 2^8 (in
