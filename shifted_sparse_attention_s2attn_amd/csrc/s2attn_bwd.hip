@@ -832,7 +832,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   }
 }
 // ---------------------------------------------------------------------------
-// dq, bf16: 8 waves x 32 queries (two waves per SIMD), 64-row key / value tiles
+// dq, bf16: W waves x 32 queries (W = 8: two waves per SIMD; W = 4 for short
+// groups that are not whole tiles, as in the forward), 64-row key / value tiles
 // double-buffered in LDS.  Per tile: S^T = K Q^T and dP^T = V dO^T (queries
 // on lanes, so lse and Dvec are one value per lane), dS^T in registers, and
 // dQ^T += K^T dS^T with K^T read through transposing reads.
