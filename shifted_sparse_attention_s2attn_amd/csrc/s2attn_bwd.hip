@@ -918,25 +918,13 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_bwd_dq_bf16(
   }
   const size_t rix = ((size_t)b * H + h) * N + tq;
   float lse_q, dvec_q;
+  bf16x8 oc[PREP ? S::kDC : 1];
+  float lse_raw = 0.f;
   if constexpr (PREP) {
-    // Dvec = dO . O over this lane's half of the row, then the two halves
     const bf16* orow = o + ((size_t)b * N + tq) * qstride + (size_t)h * D;
-    float part = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < S::kDC; ++cc) {
-      const bf16x8 oc = *reinterpret_cast<const bf16x8*>(orow + cc * 16 + hf * 8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) part = fmaf((float)oc[i], (float)dof[cc][i], part);
-    }
-    dvec_q = sum_halves(part);
-    lse_q = lse[rix] * kLog2e;
-    if (hf == 0 && q_ok) {
-      dvec[rix] = -dvec_q;
-      lse2[rix] = lse_q;
-    }
-  } else {
-    lse_q = lse2[rix];
-    dvec_q = -dvec[rix];
+    for (int cc = 0; cc < S::kDC; ++cc) oc[cc] = *reinterpret_cast<const bf16x8*>(orow + cc * 16 + hf * 8);
+    lse_raw = lse[rix];
   }
 
   // Per-lane byte offsets, inside a 64-row tile, of the chunks this lane moves
@@ -978,6 +966,27 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_bwd_dq_bf16(
       buffer_load_lds16(vrs, toff[i], 0, vd + cb);
     }
   };
+
+
+  // the first key / value tile is in flight while the prep arithmetic runs
+  issue_tile(kv_begin, 0);
+  if constexpr (PREP) {
+    // Dvec = dO . O over this lane's half of the row, then the two halves
+    float part = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < S::kDC; ++cc)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) part = fmaf((float)oc[cc][i], (float)dof[cc][i], part);
+    dvec_q = sum_halves(part);
+    lse_q = lse_raw * kLog2e;
+    if (hf == 0 && q_ok) {
+      dvec[rix] = -dvec_q;
+      lse2[rix] = lse_q;
+    }
+  } else {
+    lse_q = lse2[rix];
+    dvec_q = -dvec[rix];
+  }
 
   // per-lane LDS byte offsets: K / V A-operand rows perm32(l32) (+32 for the
   // second half of the tile); K^T transposing reads, rows 8hf + 4t + ts (+16 kc)
@@ -1055,7 +1064,6 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_bwd_dq_bf16(
       compute(stg_c, std::integral_constant<bool, false>(), kt0);
   };
 
-  issue_tile(kv_begin, 0);
   for (int it = 0;;) {
     tile(std::integral_constant<int, 0>(), it);
     if (++it == ntiles) break;

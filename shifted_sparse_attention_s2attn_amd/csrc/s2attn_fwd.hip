@@ -340,28 +340,6 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_fwd_bf16_kernel(
 #pragma unroll
     for (int cc = 0; cc < S::kDC; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(qrow + cc * 16 + hf * 8);
   }
-  if (ROPE) {
-    // element i < D/2 of the row sits in chunk i / 16 and its partner i + D/2 in
-    // chunk i / 16 + D/32 of the same lane: the rotation is lane-local
-    const double pos = (double)tq * rope.pos_scale;
-#pragma unroll
-    for (int cc = 0; cc < S::kDC / 2; ++cc) {
-      bf16x8 ya, yb;
-      double g[8];
-      rope_revs8<D>(cc * 16 + hf * 8, rope.log2_base, g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float cs, sn, y0, y1;
-        rope_cs(pos, g[e], cs, sn);
-        rope_turn((float)qf[cc][e], (float)qf[cc + S::kDC / 2][e], cs, sn, y0, y1);
-        ya[e] = (bf16)y0;
-        yb[e] = (bf16)y1;
-      }
-      qf[cc] = ya;
-      qf[cc + S::kDC / 2] = yb;
-    }
-  }
-
   // Per-lane byte offsets, inside a 64-row tile, of the chunks this lane moves
   // (the host bounds 64 rows of K / V below 2^31 bytes)
   int koff[S::kLoads], voff[S::kLoads];
@@ -505,6 +483,29 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_fwd_bf16_kernel(
   };
 
   issue_tile(kv_begin, 0);
+  if (ROPE) {
+    // (after the first tile is issued, so its loads fly while the rows turn)
+    // element i < D/2 of the row sits in chunk i / 16 and its partner i + D/2 in
+    // chunk i / 16 + D/32 of the same lane: the rotation is lane-local
+    const double pos = (double)tq * rope.pos_scale;
+#pragma unroll
+    for (int cc = 0; cc < S::kDC / 2; ++cc) {
+      bf16x8 ya, yb;
+      double g[8];
+      rope_revs8<D>(cc * 16 + hf * 8, rope.log2_base, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float cs, sn, y0, y1;
+        rope_cs(pos, g[e], cs, sn);
+        rope_turn((float)qf[cc][e], (float)qf[cc + S::kDC / 2][e], cs, sn, y0, y1);
+        ya[e] = (bf16)y0;
+        yb[e] = (bf16)y1;
+      }
+      qf[cc] = ya;
+      qf[cc + S::kDC / 2] = yb;
+    }
+  }
+
   for (int it = 0;;) {
     tile(std::integral_constant<int, 0>(), it);
     if (++it == ntiles) break;
