@@ -699,7 +699,9 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   const float c2 = scale * kLog2e;
 
   // one query step for this wave: STG = LDS stage, MASK = causal mask needed
-  auto compute = [&](auto stg_c, auto mask_c, int jkey, int jq_first) __attribute__((always_inline)) {
+  // qend (EDGE): the end of the queries this lane's key meets: the group end,
+  // or, with the split option, the cut for a key before it
+  auto compute = [&](auto stg_c, auto mask_c, int jkey, int jq_first, int qend) __attribute__((always_inline)) {
     constexpr int STG = decltype(stg_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
     const char* Qs = lds + S::kQ + STG * S::kQTileB;
@@ -730,9 +732,13 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
       for (int i = 0; i < 8; ++i) {
         const float lq = i < 4 ? l0[i] : l1[i - 4];
         float p = fast_exp2(fmaf(sacc[u * 8 + i], c2, -lq));
-        if (MASK && (jkey > jq_first + u * 16 + i || (EDGE && jq_first + u * 16 + i >= qge) ||
-                     (EDGE && SPLIT && jkey < cut && jq_first + u * 16 + i >= cut)))
-          p = 0.f;
+        if (MASK) {
+          // bitwise, not short-circuit: one select, no branch per element
+          const int qi = jq_first + u * 16 + i;
+          bool mk = jkey > qi;
+          if (EDGE) mk = mk | (qi >= qend);
+          p = mk ? 0.f : p;
+        }
         pv[i] = p;
         sv[i] = p * pacc[u * 8 + i];
       }
@@ -754,10 +760,17 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     if (key_lo > q_lo + 31) return;                   // every key follows every query: P = 0
     if ((SPLIT || EDGE) && q_lo >= wqe) return;       // queries of another group than the wave's keys
     const int jkey = key_lo + l32, jq_first = q_lo + hf * 8;
-    if (key_lo + 31 > q_lo || (EDGE && q_lo + 31 >= qge) || (EDGE && SPLIT && key_lo < cut && q_lo + 31 >= cut))
-      compute(stg_c, std::integral_constant<bool, true>(), jkey, jq_first);
-    else
-      compute(stg_c, std::integral_constant<bool, false>(), jkey, jq_first);
+    const int qend = (EDGE && SPLIT && jkey < cut) ? min(cut, qge) : qge;
+    if constexpr (EDGE && SPLIT) {
+      // every step masked: one copy of the step body, which keeps this
+      // instantiation within the register file
+      compute(stg_c, std::integral_constant<bool, true>(), jkey, jq_first, qend);
+    } else {
+      if (key_lo + 31 > q_lo || (EDGE && q_lo + 31 >= qge))
+        compute(stg_c, std::integral_constant<bool, true>(), jkey, jq_first, qend);
+      else
+        compute(stg_c, std::integral_constant<bool, false>(), jkey, jq_first, qend);
+    }
   };
 
   int hh = 0, sig, jk0, qt_b, qt_e, wqe;
@@ -1034,7 +1047,11 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_bwd_dq_bf16(
         for (int i = 0; i < 8; ++i) {
           float p = fast_exp2(fmaf(s[u * 8 + i], c2, -lse_q));
           const int key = kt0 + ks * 32 + u * 16 + hf * 8 + i;
-          if (MASK && (key > jq || (CUT && key < cut && jq >= cut))) p = 0.f;
+          if (MASK) {
+            bool mk = key > jq;
+            if (CUT) mk = mk | ((key < cut) & (jq >= cut));   // bitwise: no branch per element
+            p = mk ? 0.f : p;
+          }
           dsv[i] = p * (dp[u * 8 + i] - dvec_q);
         }
         sf[2 * ks + u] = __builtin_convertvector(dsv, bf16x8);

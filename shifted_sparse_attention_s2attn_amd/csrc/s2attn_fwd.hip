@@ -424,7 +424,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void s2attn_fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt0 + ks * 32 + (r >> 3) * 16 + hf * 8 + (r & 7);
-          if (key > jq || (CUT && key < cut && jq >= cut)) s[ks][r] = -INFINITY;
+          bool mk = key > jq;
+          if (CUT) mk = mk | ((key < cut) & (jq >= cut));   // bitwise: no branch per element
+          s[ks][r] = mk ? -INFINITY : s[ks][r];
         }
     }
     float mloc = -INFINITY;
