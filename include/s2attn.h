@@ -46,10 +46,12 @@
  * cores at every size and G (groups that are not whole 128-row tiles take
  * instantiations that address rows one by one near group ends); fp32 runs
  * kernels on the fp32 matrix cores.  Every wrap option runs on every shape.
- * When a key/value head is shared by shifted and unshifted query heads
- * (H - shift_heads not a multiple of H / Hkv), the groups must be whole tiles
- * and G a multiple of 256 (the two frames, G/2 apart, then cut the key rows
- * into the same tiles).  Grids: B * H * ceil(N / G) * ceil(G / 128) < 2^31;
+ * A key/value head shared by shifted and unshifted query heads (H -
+ * shift_heads not a multiple of H / Hkv) sees its keys in two frames G/2
+ * apart; unless the groups are whole 128-row tiles and G a multiple of 256
+ * (then both frames cut the keys into the same tiles), dk and dv take two
+ * passes, the first leaving fp32 sums in the workspace for the second.
+ * Grids: B * H * ceil(N / G) * ceil(G / 128) < 2^31;
  * one token row of q: H * d < 2^24 elements.
  * B == 0 or N == 0 is an empty problem: every call validates the other sizes,
  * then returns S2ATTN_OK without reading any pointer or touching the GPU.
@@ -73,8 +75,8 @@ typedef enum {
     S2ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
     S2ATTN_ERR_SHAPE = 2,        /* B or N < 0, H, Hkv, d or G <= 0, G > N (N > 0),
                                     shift_heads outside [0, H], H % Hkv != 0 */
-    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype or wrap option, the mixed-shift
-                                    rule above, or the grid or H * d size limit */
+    S2ATTN_ERR_UNSUPPORTED = 3,  /* d not in {64,128}, unknown dtype or wrap option, or the grid
+                                    or H * d size limit */
     S2ATTN_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError) */
     S2ATTN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than s2attn_bwd_workspace_bytes() */
     S2ATTN_ERR_ALIGN = 6,        /* an element tensor pointer not 16-byte aligned, or lse not 4-byte */
@@ -119,7 +121,10 @@ int s2attn_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace s2attn_bwd needs: the fp32 row sums
- * -Dvec = -rowsum(dO * o) [B,H,N] (stored negated) and lse * log2(e) [B,H,N].
+ * -Dvec = -rowsum(dO * o) [B,H,N] (stored negated) and lse * log2(e) [B,H,N],
+ * plus, where dk and dv take two passes (a key/value head shared by shifted
+ * and unshifted query heads, on a shape whose frames cut the keys into
+ * different tiles), the first pass's fp32 dk and dv [2, B, N, Hkv, d].
  * Returns 0 when the arguments would be rejected by s2attn_bwd, and for an
  * empty problem (B == 0 or N == 0), which needs no workspace.
  */
@@ -211,8 +216,9 @@ int s2attn_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO
  * on, held until the process ends; its address is looked up once per device
  * (the device current at the call) and the call allocates nothing.  Same
  * arguments, checks and results as s2attn_bwd_ex, bit for bit; B * H * N above
- * S2ATTN_NOALLOC_MAX_ROWS returns S2ATTN_ERR_SCRATCH (after the size checks,
- * before the pointer checks and any HIP call).  The scratch needs no clearing:
+ * S2ATTN_NOALLOC_MAX_ROWS, or a shape whose dk and dv take two passes (see
+ * s2attn_bwd_workspace_bytes), returns S2ATTN_ERR_SCRATCH (after the size
+ * checks, before the pointer checks and any HIP call).  The scratch needs no clearing:
  * the backward's first stage writes every row its second stage reads.  Every
  * call on one GPU shares that GPU's scratch: calls whose kernels can overlap
  * on one GPU (other streams, other host threads) race and must be serialised

@@ -21,7 +21,7 @@ template <typename T, int D>
 hipError_t launch_bwd_prep(const void*, const void*, const float*, float*, float*, int, int, int, hipStream_t);
 template <typename T, int D>
 hipError_t launch_bwd_dkdv(const void*, const void*, const void*, const void*, const float*, const float*, void*,
-                           void*, int, int, int, int, int, int, int, hipStream_t);
+                           void*, int, int, int, int, int, int, int, hipStream_t, float*);
 template <typename T, int D>
 hipError_t launch_bwd_dq(const void*, const void*, const void*, const void*, const float*, const float*, void*,
                          int, int, int, int, int, int, int, hipStream_t);
@@ -34,7 +34,7 @@ hipError_t launch_fwd_rope(const void*, const void*, const void*, void*, float*,
 template <int D>
 hipError_t launch_bwd_rope(const void*, const void*, const void*, const void*, const float*, const void*, float*,
                            float*, void*, void*, void*, int, int, int, int, int, int, int, double, double,
-                           hipStream_t);
+                           hipStream_t, float*);
 }  // namespace s2a
 
 namespace {
@@ -61,13 +61,17 @@ int check_problem(int B, int H, int Hkv, int N, int d, int G, int shift_heads, i
   if ((size_t)H * (size_t)d >= ((size_t)1 << 24)) return S2ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return S2ATTN_ERR_UNSUPPORTED;
   if (dtype != S2ATTN_BF16 && dtype != S2ATTN_F32) return S2ATTN_ERR_UNSUPPORTED;
-  const int r = H / Hkv;
-  // A key/value head read by both shifted and unshifted query heads is tiled in
-  // the first head's frame; the other frame is offset by G/2, which must then
-  // be a whole number of tiles of whole groups.
-  if (r > 1 && (H - shift_heads) % r != 0 && (!aligned(N, G) || (G / 2) % kTileRows != 0))
-    return S2ATTN_ERR_UNSUPPORTED;
   return S2ATTN_OK;
+}
+
+// A key/value head read by both shifted and unshifted query heads: one dK/dV
+// launch tiles its keys in the first head's frame, and the other frame, G/2
+// away, must then cut them into whole tiles of whole groups.  Otherwise dK/dV
+// runs in two passes (unshifted heads, then shifted ones), the first leaving
+// its fp32 sums in the workspace for the second.
+bool two_pass_dkdv(int H, int Hkv, int N, int G, int shift_heads) {
+  const int r = H / Hkv;
+  return r > 1 && (H - shift_heads) % r != 0 && (!aligned(N, G) || (G / 2) % kTileRows != 0);
 }
 
 bool empty_problem(int B, int N) { return B == 0 || N == 0; }
@@ -130,17 +134,21 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t s2attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int G, int shift_heads, int dtype) {
   if (check_problem(B, H, Hkv, N, d, G, shift_heads, dtype) != S2ATTN_OK) return 0;
-  return 2 * align256((size_t)B * H * N * sizeof(float));
+  const size_t rows = 2 * align256((size_t)B * H * N * sizeof(float));
+  if (!two_pass_dkdv(H, Hkv, N, G, shift_heads)) return rows;
+  return rows + align256(2 * (size_t)B * N * Hkv * d * sizeof(float));
 }
 
 }  // extern "C"
 
 namespace {
 
-// Workspace: Dvec [B,H,N] | lse*log2(e) [B,H,N], fp32.
+// Workspace: -Dvec [B,H,N] | lse*log2(e) [B,H,N] | (two-pass dK/dV only) the first
+// pass's dK, dV sums [2][B,N,Hkv,d], fp32.
 struct Workspace {
   float* dvec;
   float* lse2;
+  float* part;   // NULL: one dK/dV pass
 };
 
 int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d, int G,
@@ -150,6 +158,10 @@ int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int H
     return S2ATTN_ERR_WORKSPACE;
   ws->dvec = static_cast<float*>(workspace);
   ws->lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)B * H * N * sizeof(float)));
+  ws->part = two_pass_dkdv(H, Hkv, N, G, shift_heads)
+                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            2 * align256((size_t)B * H * N * sizeof(float)))
+                 : nullptr;
   return S2ATTN_OK;
 }
 
@@ -171,7 +183,7 @@ template <typename T, int D>
 struct Dkdv {
   static hipError_t run(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
                         Workspace ws, int B, int H, int Hkv, int N, int G, int S, int wrap, hipStream_t s) {
-    return s2a::launch_bwd_dkdv<T, D>(q, k, v, dO, ws.lse2, ws.dvec, dk, dv, B, H, Hkv, N, G, S, wrap, s);
+    return s2a::launch_bwd_dkdv<T, D>(q, k, v, dO, ws.lse2, ws.dvec, dk, dv, B, H, Hkv, N, G, S, wrap, s, ws.part);
   }
 };
 template <typename T, int D>
@@ -338,9 +350,9 @@ int s2attn_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const v
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e =
       d == 64 ? s2a::launch_bwd_rope<64>(q_rot, k_rot, v, o, lse, dO, ws.lse2, ws.dvec, dq, dk, dv, B, H, Hkv, N, G,
-                                         shift_heads, wrap, pos_scale, log2(base), s)
+                                         shift_heads, wrap, pos_scale, log2(base), s, ws.part)
               : s2a::launch_bwd_rope<128>(q_rot, k_rot, v, o, lse, dO, ws.lse2, ws.dvec, dq, dk, dv, B, H, Hkv, N, G,
-                                          shift_heads, wrap, pos_scale, log2(base), s);
+                                          shift_heads, wrap, pos_scale, log2(base), s, ws.part);
   return status_of(e);
 }
 
@@ -386,6 +398,8 @@ int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* 
   if (st != S2ATTN_OK) return st;
   const size_t rows = (size_t)B * H * N;
   if (rows > (size_t)S2ATTN_NOALLOC_MAX_ROWS) return S2ATTN_ERR_SCRATCH;
+  // the scratch array holds the row sums only, not a two-pass dK/dV's partial sums
+  if (two_pass_dkdv(H, Hkv, N, G, shift_heads)) return S2ATTN_ERR_SCRATCH;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
   if (misaligned16({q, k, v, o, dO, dq, dk, dv}) || misaligned4(lse)) return S2ATTN_ERR_ALIGN;
@@ -428,11 +442,11 @@ const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_OK: return "ok";
     case S2ATTN_ERR_NULL: return "a required pointer is NULL";
     case S2ATTN_ERR_SHAPE: return "invalid shape (a size < 0, H, Hkv, d or G <= 0, G > N, shift_heads outside [0,H], or H % Hkv != 0)";
-    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, a KV head shared by shifted and unshifted query heads on a shape whose groups (and half groups) are not whole 128-row tiles, grid too large, H * d >= 2^24, a rotary scale, base or direction out of range, or an fp32 problem for the fused rotary calls)";
+    case S2ATTN_ERR_UNSUPPORTED: return "unsupported problem (d not 64/128, unknown dtype or wrap option, grid too large, H * d >= 2^24, a rotary scale, base or direction out of range, or an fp32 problem for the fused rotary calls)";
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     case S2ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (element tensors need 16 bytes, lse 4)";
-    case S2ATTN_ERR_SCRATCH: return "B * H * N exceeds the rows of the library's scratch array (S2ATTN_NOALLOC_MAX_ROWS)";
+    case S2ATTN_ERR_SCRATCH: return "the problem does not fit the library's scratch array (B * H * N above S2ATTN_NOALLOC_MAX_ROWS, or a key/value head shared by shifted and unshifted query heads that needs the two-pass dK/dV)";
     default: return "unknown status";
   }
 }

@@ -77,6 +77,67 @@ __device__ __forceinline__ void store_transposed(v8<T>* tile, const v8<T>* regs,
   }
 }
 
+// Query heads [hb, he) of the KV head whose first query head is h0 that a dK/dV
+// launch takes, and its epilogue mode (0: store dK, dV; 1: store fp32 sums to the
+// partial buffer; 2: add the partial buffer's sums, then store).  pass 0 takes
+// every head.  A KV head shared by unshifted and shifted query heads (whose two
+// frames do not cut its keys into the same tiles) runs in two launches: pass 1
+// takes its unshifted heads, pass 2 its shifted ones; a KV head with one kind
+// only is finished by the one pass that has heads for it.  Returns false if this
+// launch has nothing to do for the KV head.
+__device__ __forceinline__ bool dkdv_head_range(int pass, int H, int shift_heads, int h0, int r, int& hb, int& he,
+                                                int& mode) {
+  const int nu = min(max(H - shift_heads - h0, 0), r);   // its unshifted query heads (they come first)
+  hb = 0;
+  he = r;
+  mode = 0;
+  if (pass == 1) {
+    he = nu;
+    mode = nu == r ? 0 : 1;
+    return nu > 0;
+  }
+  if (pass == 2) {
+    hb = nu;
+    mode = nu == 0 ? 0 : 2;
+    return nu < r;
+  }
+  return true;
+}
+// fp32 partial sums of one key row (the layout of a dK / dV row): the lane's
+// elements dt * 32 + u * 16 + 8 hf + e, from register 8 u + e of tile dt, times s.
+template <int D>
+__device__ __forceinline__ void store_part(float* row, const f32x16* acc, float s, int hf) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 a, b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = acc[dt][u * 8 + e] * s;
+        b[e] = acc[dt][u * 8 + 4 + e] * s;
+      }
+      *reinterpret_cast<f32x4*>(row + dt * 32 + u * 16 + hf * 8) = a;
+      *reinterpret_cast<f32x4*>(row + dt * 32 + u * 16 + hf * 8 + 4) = b;
+    }
+}
+// acc = acc * s + the partial sums of the row (same layout)
+template <int D>
+__device__ __forceinline__ void add_part(const float* row, f32x16* acc, float s, int hf) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(row + dt * 32 + u * 16 + hf * 8);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(row + dt * 32 + u * 16 + hf * 8 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[dt][u * 8 + e] = fmaf(acc[dt][u * 8 + e], s, a[e]);
+        acc[dt][u * 8 + 4 + e] = fmaf(acc[dt][u * 8 + 4 + e], s, b[e]);
+      }
+    }
+}
+
 // ===========================================================================
 // dkdv, fp32 ("generic": written for any element type, instantiated for
 // fp32 only).  Also takes groups that are not whole tiles: key rows past
@@ -107,7 +168,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
     T* __restrict__ dk, T* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, int wrap,
-    float scale) {
+    float scale, int pass, float* __restrict__ part) {
   using S = DkdvShape<T, D>;
   constexpr int BKV = S::kBKV, BQ = S::kBQ, NQS = S::kNQS;
   constexpr int QCPR = S::kQCPR, TCPR = S::kTCPR, QRPT = S::kQRowsPerThread;
@@ -131,12 +192,14 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   const int c = (to.pair / groups) % Hkv, b = to.pair / (groups * Hkv);
   const int r = H / Hkv;
   const int h0 = c * r;
-  const int sig0 = (h0 >= H - shift_heads) ? G / 2 : 0;
+  int hb, he, mode;                             // the query heads this launch takes (dkdv_head_range)
+  if (!dkdv_head_range(pass, H, shift_heads, h0, r, hb, he, mode)) return;
+  const int sig0 = (h0 + hb >= H - shift_heads) ? G / 2 : 0;
   const bool swap = wrap == kWrapSwap;
   const WrapGroup wg = wrap_group(N, G);
   auto tok = [&](int j, int sig) { return swap ? token_of_row<true>(j, sig, N, wg) : orig_row(j, sig, N); };
   const int ge0 = min(grp * G + G, N);          // end of the group (a last group may be short)
-  const int j0 = grp * G + pos * BKV;           // first key row, rolled frame of head h0
+  const int j0 = grp * G + pos * BKV;           // first key row, rolled frame of head h0 + hb
   if (j0 >= ge0) return;                        // a tile past the end of a short group
 
   const size_t qstride = (size_t)H * D, kvstride = (size_t)Hkv * D;
@@ -164,7 +227,7 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   const float c2 = scale * kLog2e;
   const int q_dc = tid % (D / 8), q_qg = tid / (D / 8);
 
-  for (int hh = 0; hh < r; ++hh) {
+  for (int hh = hb; hh < he; ++hh) {
     const int h = h0 + hh;
     const int sig = (h >= H - shift_heads) ? G / 2 : 0;
     // same key rows in head h's rolled frame
@@ -260,13 +323,27 @@ __global__ __launch_bounds__(256) void s2attn_bwd_dkdv(
   }
 
   if (!k_ok) return;
+  float dk_scale = scale;
+  if (mode != 0) {
+    // two passes (dkdv_head_range): the first stores fp32 sums, the second adds them
+    const size_t dv_part = (size_t)(gridDim.x / tiles_per_group / groups) * N * D;   // B * Hkv * N * D
+    float* pk = part + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
+    if (mode == 1) {
+      store_part<D>(pk, dkacc, scale, hf);
+      store_part<D>(pk + dv_part, dvacc, 1.f, hf);
+      return;
+    }
+    add_part<D>(pk, dkacc, scale, hf);
+    add_part<D>(pk + dv_part, dvacc, 1.f, hf);
+    dk_scale = 1.f;
+  }
   T* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
   T* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
 #pragma unroll
   for (int dt = 0; dt < S::kDT; ++dt)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      *reinterpret_cast<v8<T>*>(dkrow + dt * 32 + u * 16 + hf * 8) = scale8<T>(dkacc[dt], u * 8, scale);
+      *reinterpret_cast<v8<T>*>(dkrow + dt * 32 + u * 16 + hf * 8) = scale8<T>(dkacc[dt], u * 8, dk_scale);
       *reinterpret_cast<v8<T>*>(dvrow + dt * 32 + u * 16 + hf * 8) = pack8<T>(dvacc[dt], u * 8);
     }
 }
@@ -531,12 +608,12 @@ __device__ __forceinline__ void store_turned_back(bf16* row, const f32x16* acc, 
 // ROPE (launched for rope.on): q and k arrive rotated by the rotary embedding; dk is turned back
 // (the transpose of the rotation) before it is stored, so it is the gradient
 // with respect to the unrotated k.
-template <int D, bool SPLIT, bool EDGE, bool SWAP, bool ROPE>
+template <int D, bool SPLIT, bool EDGE, bool SWAP, bool ROPE, bool PART>
 __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dvec,
     bf16* __restrict__ dk, bf16* __restrict__ dv, int N, int H, int Hkv, int G, int shift_heads, float scale,
-    RopeArgs rope) {
+    RopeArgs rope, int pass, float* __restrict__ part) {
   using S = DkdvB16Shape<D>;
   constexpr int BKV = S::kBKV, BQ = S::kBQ, CPR = S::kCPR, RB = S::kRowB;
   // static, so that tile addresses are compile-time constants and every LDS
@@ -557,9 +634,13 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   const int c = (to.pair / groups) % Hkv, b = to.pair / (groups * Hkv);
   const int r = H / Hkv;
   const int h0 = c * r;
-  const int sig0 = (h0 >= H - shift_heads) ? G / 2 : 0;
+  // the query heads [hb, he) of this KV head that this launch takes, and what
+  // the epilogue does (pass 0: all heads; passes 1, 2: unshifted, then shifted)
+  int hb, he, mode;
+  if (!dkdv_head_range(PART ? pass : 0, H, shift_heads, h0, r, hb, he, mode)) return;
+  const int sig0 = (h0 + hb >= H - shift_heads) ? G / 2 : 0;
   const WrapGroup wg = wrap_group(N, G);
-  const int j0 = grp * G + pos * BKV;                 // key rows, rolled frame of head h0
+  const int j0 = grp * G + pos * BKV;                 // key rows, rolled frame of head h0 + hb
   const int ge0 = EDGE ? min(grp * G + G, N) : grp * G + G;   // end of their group
   if (EDGE && j0 >= ge0) return;                      // a tile past the end of a short group
 
@@ -651,7 +732,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     wqe = fr_wqe[sh];
   };
   // EDGE: the group end; one frame only (a KV head shared by shifted and
-  // unshifted query heads needs whole tiles)
+  // unshifted query heads either has whole tiles in both frames or runs its
+  // two kinds of heads in two passes)
   const int qge = fr_qge[sig0 != 0];
   // EDGE with the split option: query rows from the cut on see no key row before it
   const int cut = (EDGE && SPLIT) ? split_cut(fr_jk0[sig0 != 0] - fr_jk0[sig0 != 0] % G, sig0 != 0, wg) : -1;
@@ -773,8 +855,8 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     }
   };
 
-  int hh = 0, sig, jk0, qt_b, qt_e, wqe;
-  head_frame(0, sig, jk0, qt_b, qt_e, wqe);
+  int hh = hb, sig, jk0, qt_b, qt_e, wqe;
+  head_frame(hb, sig, jk0, qt_b, qt_e, wqe);
   int qt = qt_b;
   issue_step(hh, qt, sig, 0);
   // advance the cursor to the next (head, query tile); returns false past the end
@@ -782,12 +864,12 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
     nhh = hh; nqt = qt + 1; nsig = sig; njk0 = jk0; nqb = qt_b; nqe = qt_e; nwqe = wqe;
     if (nqt == qt_e) {
       ++nhh;
-      if (nhh < r) {
+      if (nhh < he) {
         head_frame(nhh, nsig, njk0, nqb, nqe, nwqe);
         nqt = nqb;
       }
     }
-    return nhh < r;
+    return nhh < he;
   };
   auto one = [&](auto stg_c) {
     constexpr int STG = decltype(stg_c)::value;
@@ -826,6 +908,19 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
       }
     if (EDGE && j0 + key_row >= ge0) return;          // a key of the next group
     const int tk = token_of_row<SWAP>(j0 + key_row, sig0, N, wg);
+    if (mode != 0) {
+      // two passes: the first stores its fp32 sums (dK scaled), the second adds them
+      const size_t dv_part = (size_t)(gridDim.x / tiles_per_group / groups) * N * D;   // B * Hkv * N * D
+      float* pk = part + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
+      if (mode == 1) {
+        store_part<D>(pk, dkacc, scale, hf);
+        store_part<D>(pk + dv_part, dvacc, 1.f, hf);
+        return;
+      }
+      add_part<D>(pk, dkacc, scale, hf);
+      add_part<D>(pk + dv_part, dvacc, 1.f, hf);
+    }
+    const float dk_scale = mode == 2 ? 1.f : scale;   // pass 2's dK sums are scaled already
     bf16* dkrow = dk + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
     bf16* dvrow = dv + ((size_t)b * N + tk) * kvstride + (size_t)c * D;
 #pragma unroll
@@ -834,14 +929,14 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
       for (int u = 0; u < 2; ++u)
         *reinterpret_cast<bf16x8*>(dvrow + dt * 32 + u * 16 + hf * 8) = pack8<bf16>(dvacc[dt], u * 8);
     if (ROPE) {
-      store_turned_back<D>(dkrow, dkacc, scale, (double)tk * rope.pos_scale, rope.log2_base, hf);
+      store_turned_back<D>(dkrow, dkacc, dk_scale, (double)tk * rope.pos_scale, rope.log2_base, hf);
       return;
     }
 #pragma unroll
     for (int dt = 0; dt < S::kDT; ++dt)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<bf16x8*>(dkrow + dt * 32 + u * 16 + hf * 8) = scale8<bf16>(dkacc[dt], u * 8, scale);
+        *reinterpret_cast<bf16x8*>(dkrow + dt * 32 + u * 16 + hf * 8) = scale8<bf16>(dkacc[dt], u * 8, dk_scale);
   }
 }
 // ---------------------------------------------------------------------------
@@ -1115,22 +1210,27 @@ hipError_t launch_bwd_prep(const void* o, const void* dO, const float* lse, floa
 }
 
 template <int D>
-hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
-                            const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                            int shift_heads, int wrap, float scale, RopeArgs rope, hipStream_t stream) {
+hipError_t launch_dkdv_bf16_pass(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                                 const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
+                                 int shift_heads, int wrap, float scale, RopeArgs rope, hipStream_t stream, int pass,
+                                 float* part) {
   using S = DkdvB16Shape<D>;
   constexpr int BKV = S::kBKV;
   const bool whole = N % G == 0 && G % BKV == 0;
   const dim3 grid(whole ? B * Hkv * (N / BKV) : B * Hkv * ((N + G - 1) / G) * ((G + BKV - 1) / BKV));
   const dim3 block(S::kThreads);
-#define S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, ROPE)                                                             \
-  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, SPLIT, EDGE, SWAP, ROPE>), grid, block, 0, stream,              \
+#define S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, ROPE, PART)                                                       \
+  hipLaunchKernelGGL((s2attn_bwd_dkdv_bf16<D, SPLIT, EDGE, SWAP, ROPE, PART>), grid, block, 0, stream,        \
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, dvec, (bf16*)dk,   \
-                     (bf16*)dv, N, H, Hkv, G, shift_heads, scale, rope)
-#define S2A_DKDV_LAUNCH(SPLIT, EDGE, SWAP)                    \
-  do {                                                        \
-    if (rope.on) S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, true);  \
-    else S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, false);         \
+                     (bf16*)dv, N, H, Hkv, G, shift_heads, scale, rope, pass, part)
+  // PART (the two-pass epilogue) is its own instantiation, so that the one-pass
+  // kernels keep their register allocation
+#define S2A_DKDV_LAUNCH(SPLIT, EDGE, SWAP)                                       \
+  do {                                                                           \
+    if (pass != 0 && rope.on) S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, true, true);  \
+    else if (pass != 0) S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, false, true);       \
+    else if (rope.on) S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, true, false);         \
+    else S2A_DKDV_LAUNCH_R(SPLIT, EDGE, SWAP, false, false);                     \
   } while (0)
   if (wrap == kWrapSplit) {
     if (whole) S2A_DKDV_LAUNCH(true, false, false); else S2A_DKDV_LAUNCH(true, true, false);
@@ -1145,29 +1245,51 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
   return hipGetLastError();
 }
 
+// part == NULL: one launch over every query head; else the two passes of
+// dkdv_head_range, part holding the first pass's fp32 sums (2 B N Hkv D floats).
+template <int D>
+hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                            const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
+                            int shift_heads, int wrap, float scale, RopeArgs rope, hipStream_t stream,
+                            float* part = nullptr) {
+  if (part) {
+    const hipError_t e = launch_dkdv_bf16_pass<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads,
+                                                  wrap, scale, rope, stream, 1, part);
+    if (e != hipSuccess) return e;
+    return launch_dkdv_bf16_pass<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale,
+                                    rope, stream, 2, part);
+  }
+  return launch_dkdv_bf16_pass<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale, rope,
+                                  stream, 0, nullptr);
+}
+
 template <typename T, int D>
 hipError_t launch_dkdv_generic(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                                const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                               int shift_heads, int wrap, float scale, hipStream_t stream) {
+                               int shift_heads, int wrap, float scale, hipStream_t stream, float* part) {
   using S = DkdvShape<T, D>;
   const dim3 grid(B * Hkv * ((N + G - 1) / G) * ((G + S::kBKV - 1) / S::kBKV));
-  hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), grid, dim3(S::kThreads), 0,
-                     stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dk, (T*)dv, N,
-                     H, Hkv, G, shift_heads, wrap, scale);
-  return hipGetLastError();
+  for (int pass = part ? 1 : 0; pass <= (part ? 2 : 0); ++pass) {
+    hipLaunchKernelGGL((s2attn_bwd_dkdv<T, D>), grid, dim3(S::kThreads), 0,
+                       stream, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse2, dvec, (T*)dk, (T*)dv, N,
+                       H, Hkv, G, shift_heads, wrap, scale, pass, part);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename T, int D>
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
                            const float* dvec, void* dk, void* dv, int B, int H, int Hkv, int N, int G,
-                           int shift_heads, int wrap, hipStream_t stream) {
+                           int shift_heads, int wrap, hipStream_t stream, float* part) {
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (std::is_same_v<T, bf16>)
     return launch_dkdv_bf16<D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale,
-                               RopeArgs{nullptr, 0, 0, 0}, stream);
+                               RopeArgs{nullptr, 0, 0, 0}, stream, part);
   else
     return launch_dkdv_generic<T, D>(q, k, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale,
-                                     stream);
+                                     stream, part);
 }
 
 // Wave count of a dq launch: as the forward's (8 waves for whole 256-row
@@ -1271,28 +1393,28 @@ template <int D>
 hipError_t launch_bwd_rope(const void* q_rot, const void* k_rot, const void* v, const void* o, const float* lse,
                            const void* dO, float* lse2, float* dvec, void* dq, void* dk, void* dv, int B, int H,
                            int Hkv, int N, int G, int shift_heads, int wrap, double pos_scale, double log2_base,
-                           hipStream_t stream) {
+                           hipStream_t stream, float* part) {
   const float scale = 1.0f / sqrtf((float)D);
   const RopeArgs rope{nullptr, pos_scale, log2_base, 1};
   const hipError_t e = launch_dq_bf16<D>(q_rot, k_rot, v, dO, o, lse, lse2, dvec, dq, B, H, Hkv, N, G, shift_heads,
                                          wrap, scale, stream, rope);
   if (e != hipSuccess) return e;
   return launch_dkdv_bf16<D>(q_rot, k_rot, v, dO, lse2, dvec, dk, dv, B, H, Hkv, N, G, shift_heads, wrap, scale,
-                             rope, stream);
+                             rope, stream, part);
 }
 template hipError_t launch_bwd_rope<64>(const void*, const void*, const void*, const void*, const float*, const void*,
                                         float*, float*, void*, void*, void*, int, int, int, int, int, int, int, double,
-                                        double, hipStream_t);
+                                        double, hipStream_t, float*);
 template hipError_t launch_bwd_rope<128>(const void*, const void*, const void*, const void*, const float*,
                                          const void*, float*, float*, void*, void*, void*, int, int, int, int, int, int,
-                                         int, double, double, hipStream_t);
+                                         int, double, double, hipStream_t, float*);
 
 #define S2A_INST_BWD(T, D)                                                                                 \
   template hipError_t launch_bwd_prep<T, D>(const void*, const void*, const float*, float*, float*, int,  \
                                             int, int, hipStream_t);                                        \
   template hipError_t launch_bwd_dkdv<T, D>(const void*, const void*, const void*, const void*,           \
                                             const float*, const float*, void*, void*, int, int, int, int,  \
-                                            int, int, int, hipStream_t);                                   \
+                                            int, int, int, hipStream_t, float*);                           \
   template hipError_t launch_bwd_dq<T, D>(const void*, const void*, const void*, const void*, const float*, \
                                           const float*, void*, int, int, int, int, int, int, int, hipStream_t); \
   template hipError_t launch_bwd_prep_dq<T, D>(const void*, const void*, const void*, const void*,           \

@@ -44,6 +44,9 @@ CASES = [  # workload, wrap, pos_scale, base
     (small_workload("rope-split", B=1, H=4, Hkv=2, d=128, N=1024, G=256, shift_heads=2), "split", 0.25, 1e4),
     (small_workload("rope-swap", B=1, H=4, Hkv=4, d=128, N=1024, G=512, shift_heads=2), "swap", 1.0, 1e4),
     (small_workload("rope-unaligned", B=1, H=2, Hkv=2, d=128, N=1000, G=300, shift_heads=1), "roll", 0.125, 1e4),
+    # a key/value head shared by shifted and unshifted query heads, G/2 = 192
+    # not a multiple of 128: the two-pass dK/dV with the rotary epilogue
+    (small_workload("rope-mixed-two-pass", B=1, H=6, Hkv=2, d=128, N=768, G=384, shift_heads=2), "split", 0.25, 1e4),
 ]
 
 
