@@ -171,6 +171,8 @@ MIXED = [
     small_workload("bf16-mixed-g100-gqa4", B=1, H=4, Hkv=1, d=128, N=777, G=100, shift_heads=1),
     small_workload("f32-mixed-g103", B=1, H=6, Hkv=2, d=64, N=515, G=103, shift_heads=2, dtype="f32"),
     small_workload("f32-mixed-g128", B=1, H=4, Hkv=2, d=128, N=512, G=128, shift_heads=1, dtype="f32"),
+    # Table 7's 1/6 group at N = 8192: 6 groups (the last of 2 rows) per head, many key tiles each
+    small_workload("bf16-mixed-table7-8k", B=1, H=6, Hkv=2, d=128, N=8192, G=1365, shift_heads=2),
 ]
 
 
