@@ -630,10 +630,18 @@ __global__ __launch_bounds__(512) void s2attn_bwd_dkdv_bf16(
   const int groups = EDGE ? num_groups(N, G) : N / G;
   const int tiles_per_group = EDGE ? (G + BKV - 1) / BKV : G / BKV;
   const TileOrder to = tile_order(blockIdx.x, gridDim.x / tiles_per_group, tiles_per_group);
-  const int pos = to.rank, grp = to.pair % groups;       // key tiles early in a group first
+  const int grp = to.pair % groups;
   const int c = (to.pair / groups) % Hkv, b = to.pair / (groups * Hkv);
   const int r = H / Hkv;
   const int h0 = c * r;
+  // Key tiles early in a group first (they meet the most queries).  A key/value
+  // head read by unshifted and shifted query heads in one pass (whole tiles, G/2
+  // a whole number of them): its tile at position p in the first frame sits at
+  // p + T/2 (mod T) in the other, so the work of p and of p + T/2 is alike and
+  // falls with p within each half: the two halves go interleaved.
+  const int n_unsh = min(max(H - shift_heads - h0, 0), r);
+  const bool mixed = !EDGE && !PART && n_unsh != 0 && n_unsh != r && (tiles_per_group & 1) == 0;
+  const int pos = mixed ? (to.rank >> 1) + (to.rank & 1) * (tiles_per_group >> 1) : to.rank;
   // the query heads [hb, he) of this KV head that this launch takes, and what
   // the epilogue does (pass 0: all heads; passes 1, 2: unshifted, then shifted)
   int hb, he, mode;
