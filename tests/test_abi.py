@@ -194,7 +194,8 @@ def test_wrap_option_validation(lib):
 
 def test_mixed_shift_workspace(lib):
     """A key/value head read by shifted and unshifted query heads (H=6, Hkv=2,
-    two shifted heads: head pair 2..3 is mixed).  Where both frames cut the keys
+    the last two heads shifted: key/value head 1 serves query heads 3..5, of
+    which 3 is unshifted).  Where both frames cut the keys
     into the same 128-row tiles (whole groups, G a multiple of 256) one dK/dV
     pass serves; otherwise dK/dV takes two passes and the workspace also holds
     the first pass's fp32 dK and dV, 2 * B * N * Hkv * d floats."""
