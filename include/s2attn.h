@@ -210,19 +210,21 @@ int s2attn_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO
 /*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the backward
- * of s2attn_bwd_ex without a caller workspace.  Its scratch (the fp32 -Dvec
- * and lse * log2(e) rows, 8 bytes per query row) lives in a device array of
- * the library, S2ATTN_NOALLOC_MAX_ROWS rows (32 MiB) on every GPU the call runs
- * on, held until the process ends; its address is looked up once per device
- * (the device current at the call) and the call allocates nothing.  Same
- * arguments, checks and results as s2attn_bwd_ex, bit for bit; B * H * N above
- * S2ATTN_NOALLOC_MAX_ROWS, or a shape whose dk and dv take two passes (see
- * s2attn_bwd_workspace_bytes), returns S2ATTN_ERR_SCRATCH (after the size
- * checks, before the pointer checks and any HIP call).  The scratch needs no clearing:
- * the backward's first stage writes every row its second stage reads.  Every
- * call on one GPU shares that GPU's scratch: calls whose kernels can overlap
- * on one GPU (other streams, other host threads) race and must be serialised
- * by the caller.  S2ATTN_ERR_HIP also reports a failed lookup of the scratch.
+ * of s2attn_bwd_ex without a caller workspace.  Its scratch (the workspace
+ * of s2attn_bwd_ex: the fp32 -Dvec and lse * log2(e) rows, 8 bytes per query
+ * row, and where dk and dv take two passes the first pass's sums) lives in a
+ * device array of the library, 32 MiB (S2ATTN_NOALLOC_MAX_ROWS query rows) on
+ * every GPU the call runs on, held until the process ends; its address is
+ * looked up once per device (the device current at the call) and the call
+ * allocates nothing.  Same arguments, checks and results as s2attn_bwd_ex,
+ * bit for bit; B * H * N above S2ATTN_NOALLOC_MAX_ROWS, or a workspace
+ * (s2attn_bwd_workspace_bytes) larger than the array, returns
+ * S2ATTN_ERR_SCRATCH (after the size checks, before the pointer checks and
+ * any HIP call).  The scratch needs no clearing: each stage writes every
+ * value a later stage reads.  Every call on one GPU shares that GPU's
+ * scratch: calls whose kernels can overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller.  S2ATTN_ERR_HIP
+ * also reports a failed lookup of the scratch.
  */
 #define S2ATTN_NOALLOC_MAX_ROWS (1 << 22)
 int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,

@@ -398,16 +398,15 @@ int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* 
   if (st != S2ATTN_OK) return st;
   const size_t rows = (size_t)B * H * N;
   if (rows > (size_t)S2ATTN_NOALLOC_MAX_ROWS) return S2ATTN_ERR_SCRATCH;
-  // the scratch array holds the row sums only, not a two-pass dK/dV's partial sums
-  if (two_pass_dkdv(H, Hkv, N, G, shift_heads)) return S2ATTN_ERR_SCRATCH;
+  // the workspace layout of s2attn_bwd_ex, inside the scratch array (a two-pass
+  // dK/dV's partial sums included, where they fit)
+  const size_t need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype);
+  if (need > kScratchBytes) return S2ATTN_ERR_SCRATCH;
   if (empty_problem(B, N)) return S2ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return S2ATTN_ERR_NULL;
   if (misaligned16({q, k, v, o, dO, dq, dk, dv}) || misaligned4(lse)) return S2ATTN_ERR_ALIGN;
   void* base = scratch_address();
   if (!base) return S2ATTN_ERR_HIP;
-  // the workspace layout of s2attn_bwd_ex, inside the scratch array
-  const size_t need = s2attn_bwd_workspace_bytes(B, H, Hkv, N, d, G, shift_heads, dtype);
-  if (need > kScratchBytes) return S2ATTN_ERR_SCRATCH;
   Workspace ws;
   st = check_workspace(base, need, B, H, Hkv, N, d, G, shift_heads, dtype, &ws);
   if (st != S2ATTN_OK) return st;
@@ -446,7 +445,7 @@ const char* s2attn_status_str(int status) {  switch (status) {
     case S2ATTN_ERR_HIP: return "HIP kernel launch failed";
     case S2ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than s2attn_bwd_workspace_bytes()";
     case S2ATTN_ERR_ALIGN: return "a tensor pointer is misaligned (element tensors need 16 bytes, lse 4)";
-    case S2ATTN_ERR_SCRATCH: return "the problem does not fit the library's scratch array (B * H * N above S2ATTN_NOALLOC_MAX_ROWS, or a key/value head shared by shifted and unshifted query heads that needs the two-pass dK/dV)";
+    case S2ATTN_ERR_SCRATCH: return "the problem does not fit the library's scratch array (B * H * N above S2ATTN_NOALLOC_MAX_ROWS, or a two-pass dK/dV whose workspace exceeds the array)";
     default: return "unknown status";
   }
 }

@@ -208,9 +208,13 @@ def test_mixed_shift_workspace(lib):
     assert lib.s2attn_bwd_workspace_bytes(1, 6, 2, 1024, 64, 128, 3, 0) == rows(1, 6, 1024)
     assert lib.s2attn_bwd_workspace_bytes(1, 6, 6, 1024, 64, 128, 1, 0) == rows(1, 6, 1024)
     assert fwd_status(lib, ptrs=False, H=6, Hkv=2, S=2, G=128, N=512) == _lib.S2ATTN_ERR_NULL   # shape accepted
-    # the noalloc backward's scratch holds the row sums only
-    call = lambda G: lib.s2attn_bwd_noalloc(*([None] * 9), 1, 6, 2, 1024, 64, G, 2, 0, 0, None)
-    assert call(256) == _lib.S2ATTN_ERR_NULL and call(128) == _lib.S2ATTN_ERR_SCRATCH
+    # the noalloc backward holds the first pass's sums in its scratch array where
+    # they fit (32 MiB with the row sums; the sums take 2 * N * Hkv * d floats)
+    call = lambda N, G, d: lib.s2attn_bwd_noalloc(*([None] * 9), 1, 6, 2, N, d, G, 2, 0, 0, None)
+    assert call(1024, 256, 64) == _lib.S2ATTN_ERR_NULL and call(1024, 128, 64) == _lib.S2ATTN_ERR_NULL
+    assert call(8192, 128, 128) == _lib.S2ATTN_ERR_NULL                # 16.8 MB of sums
+    assert call(16384, 128, 128) == _lib.S2ATTN_ERR_SCRATCH            # 33.6 MB of sums
+    assert call(32768, 256, 128) == _lib.S2ATTN_ERR_NULL              # one pass: the row sums only
 
 
 def test_workspace_size(lib):

@@ -1,10 +1,12 @@
 """s2attn_bwd_noalloc (the backward with the library's own scratch array, for
 callers that cannot allocate) against s2attn_bwd_ex, through the C ABI.
 
-Three calls in a row share the GPU's scratch array, each smaller than the one
+Four calls in a row share the GPU's scratch array, each smaller than the one
 before, so the later ones run on scratch still holding the earlier rows: the
-7B 32k workload, a bf16 shape whose groups are not whole tiles, and an fp32
-shape with the split option.  Each must equal s2attn_bwd_ex on the same inputs
+7B 32k workload, a bf16 shape whose groups are not whole tiles, a bf16 shape
+whose dK/dV takes two passes (a key/value head shared by shifted and
+unshifted query heads, G = 100: the first pass's sums also sit in the
+scratch), and an fp32 shape with the split option.  Each must equal s2attn_bwd_ex on the same inputs
 bit for bit (the same kernels, no atomics), which is within the bf16 / fp32
 bars of the oracle parity tests; the smallest one is also checked against the
 oracle.
@@ -23,6 +25,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     (WORKLOADS["llama2-7b-32k"], "roll", "cuda"),
     (small_workload("edge", B=2, H=4, Hkv=2, d=128, N=1000, G=256, shift_heads=2), "roll", "cpu"),
+    (small_workload("mixed-two-pass", B=1, H=6, Hkv=2, d=64, N=500, G=100, shift_heads=2), "swap", "cpu"),
     (small_workload("f32-split", B=1, H=2, Hkv=2, d=64, N=512, G=128, shift_heads=1, dtype="f32"), "split", "cpu"),
 ]
 
