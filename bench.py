@@ -15,8 +15,9 @@ longest one is the roofline kernel.  Afterwards a vendor bf16 GEMM on
 standard-normal operands is timed as the practical matrix-core ceiling for
 data of this distribution, and the float64 CPU oracle is timed on a bounded
 sample of the same workload (rank 0, one GPU only).  The other workloads of
-the metric's N range (8k, 100k, and the 70B GQA shape at 32k) are then timed
-and reported under "range" (outside the timed region): each is warmed up for
+the metric's N range (8k, 100k, and the 70B GQA shape at 32k), Table 7's 1/6
+group at 8k and full causal attention at 100k (G = N) are then timed and
+reported under "range" (outside the timed region): each is warmed up for
 at least half a second, so the clock has left the idle state the CPU timing
 leaves it in, and timed over at least a quarter second of steps.
 
@@ -258,7 +259,8 @@ def main():
                          "on dq and dk), the step before the attention, and a whole step with the rotary passes "
                          "stand-alone against one with them fused into the attention kernels (k's pass kept); "
                          "reported apart from the step")
-    ap.add_argument("--range", default="llama2-7b-8k,llama2-7b-100k,llama2-70b-gqa-32k",
+    ap.add_argument("--range", default="llama2-7b-8k,llama2-7b-100k,llama2-70b-gqa-32k,llama2-7b-8k-g1365,"
+                                       "llama2-7b-100k-fullattn",
                     help="comma-separated workloads also timed (forward and backward only, a few steps each) and "
                          "reported under \"range\", so the metric's whole N range is measured in one run; empty = none")
     ap.add_argument("--range-steps", type=int, default=10)
